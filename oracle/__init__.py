@@ -1,0 +1,187 @@
+"""fp64 CPU oracle (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The HIP library never loads it and it never
+loads the HIP library; the two share no code.  ``oracle.c`` holds the
+arithmetic; this module only compiles it with gcc and marshals numpy arrays.
+
+Functions with a pin in ``tests/test_oracle_pins.py``: every function here.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, E4M3, F64 = 0, 1, 2, 3
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (-O2, no fast-math, OpenMP over rows)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P, I, D, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_int64
+        L.oracle_sdpa.argtypes = [P, I, P, I, P, I, P, I, I, I, I, I, I, D, P, P]
+        L.oracle_layernorm.argtypes = [P, I64, I, P, P, D, P, P, P]
+        L.oracle_encoder_block.argtypes = [P, P, P, I, P, I, I, I, I, D, P, P, P, D, P, P, P, P, P]
+        L.oracle_prefill_paged.argtypes = [P, I, P, P, D, D, P, I, I, I, I, D, I, I, I, I, P, I, P, P]
+        L.oracle_decode.argtypes = [P, I, I64, P]
+        L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f64.restype = D
+        L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_to_f64.restype = D
+        _lib = L
+    return _lib
+
+
+def _raw(x):
+    """Return (contiguous numpy array of the raw storage, dtype code)."""
+    import torch
+
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().contiguous()
+        if x.dtype == torch.bfloat16:
+            return x.view(torch.int16).numpy().view(np.uint16), BF16
+        if x.dtype == torch.float8_e4m3fn:
+            return x.view(torch.uint8).numpy(), E4M3
+        if x.dtype == torch.float32:
+            return x.numpy(), F32
+        if x.dtype == torch.float64:
+            return x.numpy(), F64
+        raise TypeError(f"oracle: unsupported dtype {x.dtype}")
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.float64:
+        return x, F64
+    raise TypeError(f"oracle: unsupported dtype {x.dtype}")
+
+
+def _f64(x):
+    if x is None:
+        return None
+    import torch
+
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().to(torch.float64).numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def decode(x) -> np.ndarray:
+    """Widen raw bf16 / e4m3fn / fp32 storage to fp64 with the oracle's own decoders."""
+    raw, dt = _raw(x)
+    out = np.empty(raw.size, dtype=np.float64)
+    lib().oracle_decode(_ptr(raw), dt, raw.size, _ptr(out))
+    return out.reshape(raw.shape)
+
+
+def sdpa(q, k, v, scale: float, mask=None, return_lse: bool = False):
+    """q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D]; mask additive [B,1,1,Skv] or [B,Skv] (nullable)."""
+    qr, qt = _raw(q)
+    kr, kt = _raw(k)
+    vr, vt = _raw(v)
+    B, Hq, Sq, D = qr.shape
+    _, Hkv, Skv, _ = kr.shape
+    m = None if mask is None else _f64(mask).reshape(B, Skv)
+    out = np.empty((B, Hq, Sq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, Sq), dtype=np.float64)
+    rc = lib().oracle_sdpa(_ptr(qr), qt, _ptr(kr), kt, _ptr(vr), vt, _ptr(m), B, Hq, Hkv, Sq, Skv, D,
+                           float(scale), _ptr(out), _ptr(lse))
+    if rc:
+        raise ValueError(f"oracle_sdpa rc={rc}")
+    return (out, lse) if return_lse else out
+
+
+def layernorm(x, gamma=None, beta=None, eps: float = 1e-6):
+    """LayerNorm over the last dim; returns (y, mean, rstd) in fp64."""
+    xs = _f64(x)
+    N = xs.shape[-1]
+    rows = xs.size // N
+    xs = xs.reshape(rows, N)
+    g, b = _f64(gamma), _f64(beta)
+    y = np.empty_like(xs)
+    mean = np.empty(rows)
+    rstd = np.empty(rows)
+    rc = lib().oracle_layernorm(_ptr(xs), rows, N, _ptr(g), _ptr(b), float(eps), _ptr(y), _ptr(mean),
+                                _ptr(rstd))
+    if rc:
+        raise ValueError(f"oracle_layernorm rc={rc}")
+    return y.reshape(np.shape(x)), mean, rstd
+
+
+def encoder_block(q, k, v, scale, residual, gamma=None, beta=None, eps=1e-6, mask=None):
+    """Attention -> token-major [B,S,H*D] -> + fp32 residual -> LayerNorm.
+
+    Returns dict with attn [B,H,S,D], res_out [B,S,H*D], ln_out, mean, rstd (fp64).
+    """
+    import torch
+
+    qr, qt = _raw(q)
+    kr, kt = _raw(k)
+    vr, vt = _raw(v)
+    if not (qt == kt == vt):
+        raise TypeError("encoder_block: q/k/v must share a dtype")
+    B, H, S, D = qr.shape
+    res = residual.detach().cpu().contiguous().to(torch.float32).numpy() \
+        if isinstance(residual, torch.Tensor) else np.ascontiguousarray(residual, dtype=np.float32)
+    m = None if mask is None else _f64(mask).reshape(B, S)
+    attn = np.empty((B, H, S, D))
+    res_out = np.empty((B, S, H * D))
+    ln = np.empty((B, S, H * D))
+    mean = np.empty(B * S)
+    rstd = np.empty(B * S)
+    rc = lib().oracle_encoder_block(_ptr(qr), _ptr(kr), _ptr(vr), qt, _ptr(m), B, H, S, D, float(scale),
+                                    _ptr(res), _ptr(_f64(gamma)), _ptr(_f64(beta)), float(eps), _ptr(attn),
+                                    _ptr(res_out), _ptr(ln), _ptr(mean), _ptr(rstd))
+    if rc:
+        raise ValueError(f"oracle_encoder_block rc={rc}")
+    return {"attn": attn, "res_out": res_out, "ln_out": ln, "mean": mean, "rstd": rstd}
+
+
+def prefill_paged(q, k_cache, v_cache, k_scale, v_scale, block_table, L_act, scale, rows,
+                  return_lse: bool = False):
+    """History-only paged prefill for token indices ``rows`` and all query heads.
+
+    q [Hq,Lq,D]; caches [num_blocks,Hkv,bs,D] e4m3fn; returns out [Hq,len(rows),D] fp64.
+    """
+    import torch
+
+    qr, qt = _raw(q)
+    kc = k_cache.detach().cpu().contiguous().view(torch.uint8).numpy()
+    vc = v_cache.detach().cpu().contiguous().view(torch.uint8).numpy()
+    bt = np.ascontiguousarray(np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table),
+                              dtype=np.int32)
+    r = np.ascontiguousarray(np.asarray(rows.cpu() if hasattr(rows, "cpu") else rows), dtype=np.int64)
+    Hq, Lq, D = qr.shape
+    nb, Hkv, bs, _ = kc.shape
+    out = np.empty((Hq, r.size, D))
+    lse = np.empty((Hq, r.size))
+    rc = lib().oracle_prefill_paged(_ptr(qr), qt, _ptr(kc), _ptr(vc), float(k_scale), float(v_scale), _ptr(bt),
+                                    bt.size, nb, bs, int(L_act), float(scale), Hq, Hkv, Lq, D, _ptr(r), r.size,
+                                    _ptr(out), _ptr(lse))
+    if rc:
+        raise ValueError(f"oracle_prefill_paged rc={rc}")
+    return (out, lse) if return_lse else out

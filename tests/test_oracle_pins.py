@@ -1,0 +1,288 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+Each test ties one oracle function to brute force on tiny inputs, to a library
+routine it reduces to in a special case, to a closed form, or to an invariant
+the definition implies.  The tolerances are fp64 round-off (1e-12 relative)
+unless the invariant is exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+
+torch.set_default_dtype(torch.float32)
+
+
+def _rand(g, *shape):
+    return torch.randn(*shape, generator=g, dtype=torch.float64)
+
+
+def _torch_sdpa64(q, k, v, scale, mask=None):
+    """torch CPU fp64 SDPA with GQA expanded by repeat_interleave (contiguous groups)."""
+    q, k, v = (t.to(torch.float64) for t in (q, k, v))
+    G = q.shape[1] // k.shape[1]
+    k = k.repeat_interleave(G, dim=1)
+    v = v.repeat_interleave(G, dim=1)
+    am = None if mask is None else mask.to(torch.float64)
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=am, scale=scale).numpy()
+
+
+def _relmax(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ----------------------------------------------------------------------------- decoders
+
+
+def test_bf16_decoder_all_patterns():
+    bits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16)
+    ref = bits.view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.decode(bits.view(torch.bfloat16))
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+
+
+def test_e4m3_decoder_all_patterns():
+    bits = torch.arange(0, 256, dtype=torch.int32).to(torch.uint8)
+    ref = bits.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.decode(bits.view(torch.float8_e4m3fn))
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    # closed-form points of the OCP e4m3fn definition
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x38] == 1.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.isnan(got).sum() == 2
+
+
+# ----------------------------------------------------------------------------- SDPA
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv,D,masked", [
+    (1, 1, 1, 3, 5, 4, False),
+    (2, 4, 2, 4, 7, 8, True),
+    (1, 6, 3, 1, 16, 8, True),
+    (2, 2, 1, 5, 1, 3, False),
+])
+def test_sdpa_matches_brute_force(B, Hq, Hkv, Sq, Skv, D, masked):
+    g = torch.Generator().manual_seed(7 + Skv)
+    q, k, v = _rand(g, B, Hq, Sq, D), _rand(g, B, Hkv, Skv, D), _rand(g, B, Hkv, Skv, D)
+    mask = None
+    if masked:
+        mask = torch.zeros(B, 1, 1, Skv, dtype=torch.float64)
+        mask[:, 0, 0, Skv // 2 + 1:] = -math.inf
+        mask[0, 0, 0, 0] = -0.75  # a finite additive entry as well
+    scale = 0.37
+    got = oracle.sdpa(q, k, v, scale, mask)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            ref = brute.softmax_attention(q[b, h].tolist(), k[b, h // G].tolist(), v[b, h // G].tolist(), scale,
+                                          None if mask is None else mask[b, 0, 0].tolist())
+            assert _relmax(got[b, h], ref) < 1e-12
+
+
+@pytest.mark.parametrize("in_dtype", [torch.float64, torch.float32, torch.bfloat16])
+def test_sdpa_matches_torch_fp64_gqa(in_dtype):
+    g = torch.Generator().manual_seed(11)
+    B, Hq, Hkv, Sq, Skv, D = 2, 8, 2, 33, 45, 16
+    q, k, v = (_rand(g, B, h, s, D).to(in_dtype) for h, s in ((Hq, Sq), (Hkv, Skv), (Hkv, Skv)))
+    lens = [45, 17]
+    mask = torch.zeros(B, 1, 1, Skv, dtype=torch.float64)
+    for b, n in enumerate(lens):
+        mask[b, 0, 0, n:] = -math.inf
+    got, lse = oracle.sdpa(q, k, v, 0.25, mask, return_lse=True)
+    ref = _torch_sdpa64(q, k, v, 0.25, mask)
+    assert _relmax(got, ref) < 1e-12
+    # lse against the log-sum-exp of the torch fp64 scores
+    kk = k.to(torch.float64).repeat_interleave(Hq // Hkv, 1)
+    s = 0.25 * q.to(torch.float64) @ kk.transpose(-1, -2) + mask
+    assert _relmax(lse, torch.logsumexp(s, -1).numpy()) < 1e-12
+
+
+# ----------------------------------------------------------------------------- invariants
+
+
+def _case(seed, B=1, H=2, Sq=9, Skv=13, D=8):
+    g = torch.Generator().manual_seed(seed)
+    return _rand(g, B, H, Sq, D), _rand(g, B, H, Skv, D), _rand(g, B, H, Skv, D)
+
+
+def test_probability_rows_sum_to_one():
+    # V = identity (Skv == D) makes o_i the probability row P_i itself.
+    q, k, _ = _case(1, Skv=8, D=8)
+    v = torch.eye(8, dtype=torch.float64).expand(1, 2, 8, 8).contiguous()
+    P = oracle.sdpa(q, k, v, 0.5)
+    assert np.all(P >= 0)
+    assert np.max(np.abs(P.sum(-1) - 1.0)) < 1e-14
+
+
+def test_constant_v_returns_constant():
+    q, k, _ = _case(2)
+    v = torch.full((1, 2, 13, 8), 3.25, dtype=torch.float64)
+    o = oracle.sdpa(q, k, v, 0.3)
+    assert np.max(np.abs(o - 3.25)) < 1e-13
+
+
+def test_kv_permutation_invariance():
+    q, k, v = _case(3)
+    mask = torch.zeros(1, 1, 1, 13, dtype=torch.float64)
+    mask[..., 4] = -math.inf
+    mask[..., 7] = 0.5
+    perm = torch.randperm(13, generator=torch.Generator().manual_seed(9))
+    o1 = oracle.sdpa(q, k, v, 0.4, mask)
+    o2 = oracle.sdpa(q, k[:, :, perm], v[:, :, perm], 0.4, mask[..., perm])
+    assert np.max(np.abs(o1 - o2)) < 1e-14
+
+
+def test_masked_keys_are_ignored_bitwise():
+    q, k, v = _case(4)
+    mask = torch.zeros(1, 1, 1, 13, dtype=torch.float64)
+    mask[..., 9:] = -math.inf
+    o1 = oracle.sdpa(q, k, v, 0.4, mask)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, 9:] = 1e30
+    v2[:, :, 9:] = -1e300
+    o2 = oracle.sdpa(q, k2, v2, 0.4, mask)
+    assert np.array_equal(o1, o2)
+
+
+def test_one_hot_score_selects_single_value_row():
+    # q = 8000 e_t, k_{j*} = e_t, other keys orthogonal to e_t, scale 1/8 -> s_{j*} = 1000.
+    D, Skv, t, jstar = 8, 11, 3, 6
+    g = torch.Generator().manual_seed(5)
+    k = _rand(g, 1, 1, Skv, D)
+    k[..., t] = 0.0
+    k[0, 0, jstar] = 0.0
+    k[0, 0, jstar, t] = 1.0
+    q = torch.zeros(1, 1, 1, D, dtype=torch.float64)
+    q[..., t] = 8000.0
+    v = _rand(g, 1, 1, Skv, D)
+    o = oracle.sdpa(q, k, v, 1.0 / 8.0)
+    assert np.array_equal(o[0, 0, 0], v[0, 0, jstar].numpy())
+
+
+def test_zero_scale_gives_mean_of_unmasked_values():
+    q, k, v = _case(6)
+    mask = torch.zeros(1, 1, 1, 13, dtype=torch.float64)
+    mask[..., 10:] = -math.inf
+    o = oracle.sdpa(q, k, v, 0.0, mask)
+    ref = v[:, :, :10].mean(2, keepdim=True).expand_as(torch.as_tensor(o)).numpy()
+    assert np.max(np.abs(o - ref)) < 1e-14
+
+
+def test_single_key_returns_its_value():
+    q, k, v = _case(7, Skv=1)
+    o = oracle.sdpa(q, k, v, 0.9)
+    assert np.array_equal(o, v.expand(1, 2, 9, 8).numpy())
+
+
+def test_fully_masked_row_is_zero_with_neg_inf_lse():
+    q, k, v = _case(8)
+    mask = torch.full((1, 1, 1, 13), -math.inf, dtype=torch.float64)
+    o, lse = oracle.sdpa(q, k, v, 0.5, mask, return_lse=True)
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+
+
+def test_lse_merge_of_two_key_halves():
+    # attention over S1 u S2 equals the LSE-weighted merge of the two halves
+    q, k, v = _case(10, Skv=20)
+    o, lse = oracle.sdpa(q, k, v, 0.35, return_lse=True)
+    o1, l1 = oracle.sdpa(q, k[:, :, :7], v[:, :, :7], 0.35, return_lse=True)
+    o2, l2 = oracle.sdpa(q, k[:, :, 7:], v[:, :, 7:], 0.35, return_lse=True)
+    M = np.maximum(l1, l2)
+    w1, w2 = np.exp(l1 - M), np.exp(l2 - M)
+    merged = (w1[..., None] * o1 + w2[..., None] * o2) / (w1 + w2)[..., None]
+    assert _relmax(merged, o) < 1e-13
+    assert np.max(np.abs(M + np.log(w1 + w2) - lse)) < 1e-13
+
+
+# ----------------------------------------------------------------------------- LayerNorm
+
+
+def test_layernorm_matches_torch_and_brute():
+    g = torch.Generator().manual_seed(12)
+    x = _rand(g, 7, 48) * 3 + 1.5
+    gamma, beta = _rand(g, 48), _rand(g, 48)
+    y, mean, rstd = oracle.layernorm(x, gamma, beta, 1e-6)
+    ref = torch.nn.functional.layer_norm(x, (48,), gamma, beta, 1e-6).numpy()
+    assert _relmax(y, ref) < 1e-12
+    for r in range(7):
+        by, bm, br = brute.layernorm_row(x[r].tolist(), gamma.tolist(), beta.tolist(), 1e-6)
+        assert _relmax(y[r], by) < 1e-12
+        assert abs(mean[r] - bm) <= 1e-12 * abs(bm) and abs(rstd[r] - br) <= 1e-12 * br
+
+
+def test_layernorm_closed_forms():
+    g = torch.Generator().manual_seed(13)
+    x = _rand(g, 5, 64)
+    eps = 1e-3
+    y, _, _ = oracle.layernorm(x, None, None, eps)
+    var = x.var(-1, unbiased=False).numpy()
+    assert np.max(np.abs(y.mean(-1))) < 1e-14
+    assert np.max(np.abs((y ** 2).mean(-1) - var / (var + eps))) < 1e-13
+    # shift invariance: LN(x + c) == LN(x)
+    y2, _, _ = oracle.layernorm(x + 17.0, None, None, eps)
+    assert np.max(np.abs(y2 - y)) < 1e-12
+    # constant row -> beta
+    beta = _rand(g, 64)
+    y3, m3, _ = oracle.layernorm(torch.full((2, 64), 4.0, dtype=torch.float64), None, beta, eps)
+    assert np.array_equal(y3, beta.expand(2, 64).numpy()) and np.all(m3 == 4.0)
+
+
+def test_encoder_block_matches_torch_chain():
+    g = torch.Generator().manual_seed(14)
+    B, H, S, D = 2, 3, 10, 8
+    q, k, v = (_rand(g, B, H, S, D).to(torch.bfloat16) for _ in range(3))
+    res = torch.randn(B, S, H * D, generator=g)
+    gamma, beta = torch.rand(H * D, generator=g) + 0.5, torch.randn(H * D, generator=g)
+    mask = torch.zeros(B, 1, 1, S)
+    mask[1, ..., 6:] = -math.inf
+    out = oracle.encoder_block(q, k, v, 0.3, res, gamma, beta, 1e-6, mask)
+    attn = _torch_sdpa64(q, k, v, 0.3, mask.to(torch.float64))
+    x = res.to(torch.float64) + torch.from_numpy(attn).permute(0, 2, 1, 3).reshape(B, S, H * D)
+    ln = torch.nn.functional.layer_norm(x, (H * D,), gamma.double(), beta.double(), 1e-6)
+    assert _relmax(out["attn"], attn) < 1e-12
+    assert np.max(np.abs(out["res_out"] - x.numpy())) < 1e-13
+    assert _relmax(out["ln_out"], ln.numpy()) < 1e-12
+
+
+# ----------------------------------------------------------------------------- paged prefill
+
+
+def test_paged_prefill_equals_dense_on_logical_kv():
+    """Scatter a logical KV sequence into physical blocks through a random
+    permutation; the paged oracle must equal dense fp64 SDPA over the first
+    L_act logical keys (GQA heads contiguous)."""
+    g = torch.Generator().manual_seed(15)
+    Hq, Hkv, Lq, D, bs, nb, L_act = 8, 2, 6, 16, 8, 7, 37
+    q = _rand(g, Hq, Lq, D).to(torch.bfloat16)
+    logical_k = (torch.randn(nb * bs, Hkv, D, generator=g) * 2).to(torch.float8_e4m3fn)
+    logical_v = (torch.randn(nb * bs, Hkv, D, generator=g) * 2).to(torch.float8_e4m3fn)
+    bt = torch.randperm(nb, generator=g).to(torch.int32)
+    kc = torch.empty(nb, Hkv, bs, D, dtype=torch.float8_e4m3fn)
+    vc = torch.empty_like(kc)
+    for i in range(nb):  # logical block i lives in physical block bt[i]
+        kc[bt[i]] = logical_k[i * bs:(i + 1) * bs].transpose(0, 1)
+        vc[bt[i]] = logical_v[i * bs:(i + 1) * bs].transpose(0, 1)
+    ks, vs = 0.5, 0.125
+    rows = torch.tensor([5, 0, 3])
+    out, lse = oracle.prefill_paged(q, kc, vc, ks, vs, bt, L_act, 0.2, rows, return_lse=True)
+    kd = (logical_k[:L_act].to(torch.float64) * ks).transpose(0, 1)[None]
+    vd = (logical_v[:L_act].to(torch.float64) * vs).transpose(0, 1)[None]
+    ref = _torch_sdpa64(q[None, :, rows].to(torch.float64), kd, vd, 0.2)[0]
+    assert _relmax(out, ref) < 1e-12
+    # physical rows past L_act are ignored bitwise
+    kc2, vc2 = kc.clone(), vc.clone()
+    last = int(bt[L_act // bs])
+    kc2[last, :, L_act % bs:] = torch.tensor(448.0).to(torch.float8_e4m3fn)
+    for i in range(L_act // bs + 1, nb):
+        vc2[int(bt[i])] = torch.tensor(-448.0).to(torch.float8_e4m3fn)
+    out2 = oracle.prefill_paged(q, kc2, vc2, ks, vs, bt, L_act, 0.2, rows)
+    assert np.array_equal(out, out2)

@@ -1,0 +1,54 @@
+"""Algorithmic work per call, the denominators of every roofline figure.
+
+Attention counts the two contractions only (QK^T and PV, 2 FLOPs per MAC);
+softmax and normalisation are excluded, which is the convention the prefill
+POC uses for its model-MFU column (Prefill Context-Parallel Attention POC,
+"Profiling-optimized 4-chip case": QK and PV model FLOPs only).  Decode counts
+bytes: the unmasked K/V rows it must read plus the mask, q and out.
+"""
+from __future__ import annotations
+
+# MI355X published dense peaks and bandwidth (AMD public specifications).
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2
+PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+
+
+def attn_flops(n_q_rows: int, n_keys: int, D: int) -> int:
+    """QK^T + PV FLOPs for n_q_rows query rows (all heads) each over n_keys keys."""
+    return 4 * n_q_rows * n_keys * D
+
+
+def encoder_flops(B: int, H: int, S_q: int, S_kv: int, D: int) -> int:
+    return attn_flops(B * H * S_q, S_kv, D)
+
+
+def prefill_flops(Lq: int, Hq: int, n_keys: int, D: int) -> int:
+    return attn_flops(Lq * Hq, n_keys, D)
+
+
+def decode_bytes(lens, Hkv: int, Hq: int, S_ctx: int, D: int, elem: int = 2, mask_elem: int = 4) -> int:
+    """K+V rows actually attended (sum_b len_b per KV head), the fp32 mask, q and out."""
+    B = len(lens)
+    kv = sum(int(n) for n in lens) * Hkv * D * elem * 2
+    return kv + B * S_ctx * mask_elem + 2 * B * Hq * D * elem
+
+
+def decode_dense_bytes(B: int, Hkv: int, Hq: int, S_ctx: int, D: int, elem: int = 2) -> int:
+    return B * Hkv * S_ctx * D * elem * 2 + B * S_ctx * 4 + 2 * B * Hq * D * elem
+
+
+def res_ln_bytes(rows: int, hidden: int, x_bytes: int = 0, y_bytes: int = 2, res_out: bool = True,
+                 stats: bool = True) -> int:
+    """Residual read + optional x read + optional residual_out write + y write + mean/rstd."""
+    per_row = hidden * (4 + x_bytes + (4 if res_out else 0) + y_bytes) + (8 if stats else 0)
+    return rows * per_row
+
+
+def vit_encoder_flops(layers: int, tokens: int, hidden: int, mlp: int, patch_in: int) -> int:
+    """Closed-form forward FLOPs of a ViT encoder: QKV + out-projection + MLP +
+    attention (QK + PV) per layer, plus the patch embedding."""
+    per_layer = (2 * tokens * hidden * 3 * hidden + 2 * tokens * hidden * hidden
+                 + 2 * 2 * tokens * hidden * mlp + 4 * tokens * tokens * hidden)
+    return layers * per_layer + 2 * tokens * patch_in * hidden
