@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the flash-attention hot path on one MI355X.
+
+One step = one pass over every kernel of the path, each on its workload:
+  * encoder block: V-JEPA2 ViT-L attention (B=1, 16 heads, 2048 tokens, D=64,
+    bf16) + residual add into the fp32 [2048,1024] stream + LayerNorm;
+  * GQA decode: B=8, 16 query / 8 KV heads, head_dim 256, S_ctx 4096,
+    ragged lengths len_b ~ U{1..4096};
+  * paged FP8 prefill: 4096 query tokens x 32 heads over 2 KV heads, D=256,
+    512-token blocks under a permuted block table, 120000 live history keys.
+All inputs are synthetic, seeded, and resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is the step's attention throughput (QK^T + PV
+FLOPs of the three attention calls over the step time); `parts` gives each
+kernel's own metric (TFLOP/s and % of the bf16 MFMA peak, or GB/s and % of
+HBM peak) from HIP events recorded on the stream the kernels run on;
+`roofline` is the dominant kernel's (the prefill).  `cpu_baseline` times the
+fp64 oracle on a bounded sample of the prefill workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+from workloads import accounting as acc  # noqa: E402
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Accumulates HIP-event durations for one kernel family on the current stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def ms(self):
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+def cpu_baseline(pre, n_rows: int):
+    """Time the fp64 oracle on n_rows query tokens x all heads of the prefill."""
+    import oracle
+
+    oracle.build()
+    rows = pre.rows[:n_rows]
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    t0 = time.perf_counter()
+    oracle.prefill_paged(pre.q, pre.k_cache, pre.v_cache, pre.k_scale, pre.v_scale, pre.block_table, pre.L_act,
+                         pre.scale, rows)
+    dt = time.perf_counter() - t0
+    flops = acc.prefill_flops(len(rows), pre.Hq, pre.L_act, pre.D)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, cores), "kind": "oracle",
+            "sample": f"paged FP8 prefill, {len(rows)} query tokens x {pre.Hq} heads x {pre.L_act} keys "
+                      f"(fp64 C oracle incl. KV decode), {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=4, help="query tokens in the CPU-baseline sample (0: skip)")
+    ap.add_argument("--only", choices=["all", "encoder", "decode", "prefill"], default="all",
+                    help="run a single kernel family (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import transformer_attention_attn_amd as taa
+
+    taa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    _log("[bench] generating inputs")
+    enc = W.encoder_vjepa2()
+    dec = W.decode_gemma()
+    pre = W.prefill_paged()
+
+    e_q, e_k, e_v = (t.to(dev) for t in (enc.q, enc.k, enc.v))
+    e_res, e_g, e_b = enc.residual.to(dev), enc.gamma.to(dev), enc.beta.to(dev)
+    e_out = torch.empty_like(e_q)
+    e_rout = torch.empty_like(e_res)
+    e_ln = torch.empty(enc.B, enc.S, enc.H * enc.D, dtype=torch.bfloat16, device=dev)
+    e_mean = torch.empty(enc.B * enc.S, device=dev)
+    e_rstd = torch.empty(enc.B * enc.S, device=dev)
+
+    d_q, d_k, d_v, d_m = (t.to(dev) for t in (dec.q, dec.k, dec.v, dec.mask))
+    d_out = torch.empty_like(d_q)
+    d_ws = torch.empty(taa.attn_decode_gqa_workspace_size(dec.B, dec.Hq, dec.S_ctx, dec.D), dtype=torch.uint8,
+                       device=dev)
+
+    p_q, p_k, p_v, p_bt = (t.to(dev) for t in (pre.q, pre.k_cache, pre.v_cache, pre.block_table))
+    p_out = torch.empty_like(p_q)
+    torch.cuda.synchronize()
+
+    t_enc, t_dec, t_pre = Timer(), Timer(), Timer()
+    run_enc = args.only in ("all", "encoder")
+    run_dec = args.only in ("all", "decode")
+    run_pre = args.only in ("all", "prefill")
+
+    def step(timed: bool):
+        if run_enc:
+            s = t_enc.start() if timed else None
+            taa.attn_encoder_fwd(e_q, e_k, e_v, enc.scale, None, out=e_out, residual=e_res, residual_out=e_rout,
+                                 gamma=e_g, beta=e_b, eps=enc.eps, ln_out=e_ln, ln_mean=e_mean, ln_rstd=e_rstd)
+            if timed:
+                t_enc.stop(s)
+        if run_dec:
+            s = t_dec.start() if timed else None
+            taa.attn_decode_gqa(d_q, d_k, d_v, d_m, dec.scale, dec.G, out=d_out, workspace=d_ws)
+            if timed:
+                t_dec.stop(s)
+        if run_pre:
+            s = t_pre.start() if timed else None
+            taa.attn_prefill_paged(p_q, p_k, p_v, pre.k_scale, pre.v_scale, p_bt, pre.L_act, pre.scale, pre.G,
+                                   out=p_out)
+            if timed:
+                t_pre.stop(s)
+
+    _log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    _log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    f_enc = acc.encoder_flops(enc.B, enc.H, enc.S, enc.S, enc.D)
+    lens = dec.lens.tolist()
+    f_dec = 4 * sum(lens) * dec.Hq * dec.D  # each query head attends len_b keys of its batch row
+    f_pre = acc.prefill_flops(pre.Lq, pre.Hq, pre.L_act, pre.D)
+    b_dec = acc.decode_bytes(lens, dec.Hkv, dec.Hq, dec.S_ctx, dec.D)
+    total_flops = (f_enc if run_enc else 0) + (f_dec if run_dec else 0) + (f_pre if run_pre else 0)
+
+    parts = {}
+
+    def summ(ms):
+        return {"mean_ms": statistics.fmean(ms), "median_ms": statistics.median(ms), "min_ms": min(ms),
+                "max_ms": max(ms)}
+
+    if run_enc:
+        ms = t_enc.ms()
+        tf = f_enc / (statistics.fmean(ms) * 1e-3) / 1e12
+        parts["encoder_block"] = {**summ(ms), "tflops": tf, "frac_bf16_peak": tf / acc.PEAK_BF16_TFLOPS,
+                                  "flops": f_enc, "kernels": "attention+residual, res_ln"}
+    if run_dec:
+        ms = t_dec.ms()
+        gbs = b_dec / (statistics.fmean(ms) * 1e-3) / 1e9
+        parts["decode"] = {**summ(ms), "gbps": gbs, "frac_hbm_peak": gbs / acc.PEAK_HBM_GBPS, "bytes": b_dec,
+                           "dense_equiv_gbps": acc.decode_dense_bytes(dec.B, dec.Hkv, dec.Hq, dec.S_ctx, dec.D)
+                           / (statistics.fmean(ms) * 1e-3) / 1e9, "kernels": "split-K, combine"}
+    if run_pre:
+        ms = t_pre.ms()
+        tf = f_pre / (statistics.fmean(ms) * 1e-3) / 1e12
+        parts["prefill"] = {**summ(ms), "tflops": tf, "frac_bf16_peak": tf / acc.PEAK_BF16_TFLOPS, "flops": f_pre,
+                            "tflops_at_131072_convention": acc.prefill_flops(pre.Lq, pre.Hq, 131072, pre.D)
+                            / (statistics.fmean(ms) * 1e-3) / 1e12}
+
+    roofline = None
+    if run_pre:
+        p = parts["prefill"]
+        roofline = {"bound": "mfma", "achieved": p["tflops"], "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": p["tflops"] / acc.PEAK_BF16_TFLOPS, "traffic": None, "kernel": "prefill_paged_kernel"}
+    elif run_enc:
+        p = parts["encoder_block"]
+        roofline = {"bound": "mfma", "achieved": p["tflops"], "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": p["frac_bf16_peak"], "traffic": None, "kernel": "encoder_fwd_kernel+res_ln_kernel"}
+    elif run_dec:
+        p = parts["decode"]
+        roofline = {"bound": "hbm", "achieved": p["gbps"], "peak": acc.PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": p["frac_hbm_peak"], "traffic": None, "kernel": "decode_split_kernel+decode_combine_kernel"}
+
+    cpu = None
+    if args.cpu_rows > 0 and run_pre:
+        _log(f"[bench] cpu baseline: oracle on {args.cpu_rows} prefill tokens")
+        cpu = cpu_baseline(pre, args.cpu_rows)
+
+    line = {
+        "metric": "attn TFLOP/s & % MFMA peak (encoder/prefill); decode GB/s & % HBM peak",
+        "value": total_flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the pages' workloads, no weights or datasets)",
+        "config": {
+            "workload": "vjepa2_encoder_block_s2048 + gemma_gqa_decode_d256_ctx4096 + paged_fp8_prefill_q4096_hist120000"
+            if args.only == "all" else args.only,
+            "encoder": {"B": enc.B, "H": enc.H, "S": enc.S, "D": enc.D, "residual_ln_hidden": enc.H * enc.D},
+            "decode": {"B": dec.B, "Hq": dec.Hq, "Hkv": dec.Hkv, "S_ctx": dec.S_ctx, "D": dec.D, "sum_len": sum(lens)},
+            "prefill": {"Lq": pre.Lq, "Hq": pre.Hq, "Hkv": pre.Hkv, "D": pre.D, "block_size": pre.block_size,
+                        "actual_history_len": pre.L_act, "kv": "fp8_e4m3fn"},
+            "parallelism": "single GPU",
+        },
+        "parts": parts,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

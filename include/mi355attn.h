@@ -1,0 +1,185 @@
+/*
+ * mi355attn: flash (tiled online-softmax) scaled-dot-product attention and a
+ * residual + LayerNorm for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer that the caller allocates, owns
+ *    and keeps alive until the enqueued work has finished.  The library never
+ *    allocates or frees memory, never synchronizes, and enqueues all of its work on `stream` (0 = the null
+ *    stream).  Calls are asynchronous: a return of ATTN_OK means the work was
+ *    enqueued.
+ *  - Arguments are validated on the host before anything is launched.  A
+ *    failed check returns an error code and leaves every output untouched.
+ *  - Device DATA is not inspected on the host: a block-table entry outside
+ *    [0, num_blocks) is undefined behaviour.
+ *  - Results are bitwise deterministic: the same inputs give the same bits,
+ *    and a query row's output does not depend on any other batch entry.
+ *  - Softmax runs in fp32 (row max and row sum in fp32 registers), the
+ *    contractions run on bf16 MFMA with fp32 accumulation.  Inference only:
+ *    there is no backward pass.
+ *  - Masks are additive fp32: 0 keeps a key, -inf removes it (any finite
+ *    value is added to the scaled score).  A query row whose keys are all
+ *    removed produces an all-zero output and lse = -inf.
+ */
+#ifndef MI355ATTN_H
+#define MI355ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null required pointer, bad size, misaligned or non-unit-stride tensor */
+  ATTN_ERR_UNSUPPORTED = 2, /* a head_dim, dtype or shape that is not compiled in */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returns */
+  ATTN_ERR_HIP = 4          /* the HIP runtime rejected a launch */
+} attn_status_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_FP8_E4M3FN = 2 } attn_dtype_t;
+
+/* Static, human-readable text for a status code (never NULL). */
+ATTN_API const char *attn_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+ATTN_API int attn_version(void);
+
+/*
+ * Non-causal encoder attention with an optional fused residual add and
+ * LayerNorm epilogue.
+ *
+ * Follows: vit-encoder-neuron-kernels, "Supported shapes and limits"
+ * (bidirectional self-attention, standard LayerNorm, residual stream in
+ * fp32) and "Repository layout" (attention followed by residual + LayerNorm);
+ * V-JEPA2 ViT-L Encoder NKI Kernels for AWS Trainium2, "Repository layout"
+ * (residual + LayerNorm kernels around the attention inner); gte-encoder-
+ * neuron-kernels, "Constraints" (right padding expressed as an additive key
+ * mask).
+ *
+ *   o[b,h,i,:] = softmax_j(softmax_scale * q[b,h,i,:].k[b,h,j,:] + mask[b,j]) v[b,h,j,:]
+ *
+ * Layout: q [B,H,S_q,D], k/v [B,H,S_kv,D] addressed by element strides
+ * {b,h,s,d}; the d stride must be 1, the others multiples of 8 elements, and
+ * the base pointers 16-byte aligned.  in_dtype is ATTN_BF16 or ATTN_F32 (fp32
+ * inputs are rounded to bf16, round-to-nearest-even, as they are loaded).
+ * D must be 64.
+ *
+ * Outputs (each optional, but at least one of out / residual_out required):
+ *   out          attention output, out_dtype BF16 or F32, [B,H,S_q,D] by
+ *                element strides (use strides {S*H*D, D, H*D, 1} for the
+ *                token-major [B,S_q,H*D] layout); same alignment rules.
+ *   lse          fp32 [B,H,S_q], natural-log log-sum-exp of the scaled scores.
+ *   residual_out fp32 [B,S_q,H*D] contiguous: residual + o (head h owns
+ *                columns h*D..h*D+D-1); requires residual.  May alias residual.
+ *   ln_out       LayerNorm(residual_out) over H*D, ln_dtype BF16 or F32,
+ *                contiguous [B,S_q,H*D]; requires residual_out.
+ *   ln_mean/ln_rstd  fp32 [B*S_q] statistics of that LayerNorm (nullable).
+ * gamma/beta are fp32 [H*D] and nullable (affine-free LayerNorm).
+ * mask is nullable fp32 [B,1,1,S_kv] with batch stride mask_stride_b.
+ */
+typedef struct {
+  const void *q, *k, *v;
+  attn_dtype_t in_dtype;
+  int B, H, S_q, S_kv, D;
+  int64_t q_stride[4], k_stride[4], v_stride[4];
+  const float *mask;
+  int64_t mask_stride_b;
+  float softmax_scale;
+  void *out;
+  attn_dtype_t out_dtype;
+  int64_t out_stride[4];
+  float *lse;
+  const float *residual;
+  float *residual_out;
+  const float *gamma, *beta;
+  float eps;
+  void *ln_out;
+  attn_dtype_t ln_dtype;
+  float *ln_mean, *ln_rstd;
+} attn_encoder_args_t;
+
+ATTN_API int attn_encoder_fwd(const attn_encoder_args_t *args, hipStream_t stream);
+
+/*
+ * GQA single-token decode (split-K "flash-decode" plus a combine pass).
+ *
+ * Follows: head_dim>128 (256/512) GQA Flash-Decode NKI Kernel for AWS
+ * Trainium, "Input contract" (shapes, additive 0/-inf mask, softmax_scale,
+ * num_kv_groups) and "Supported shapes (the eligibility gate)" (turned into
+ * argument checks here, never into a fallback); its "Future performance
+ * follow-on" (sharding the KV stream across many programs) is the split-K.
+ *
+ *   q [B,Hq,1,D] bf16, k/v [B,Hkv,S_ctx,D] bf16, attn_mask [B,1,1,S_ctx] fp32
+ *   (nullable = no mask), out [B,Hq,1,D] bf16, all contiguous and 16-byte
+ *   aligned.  Query head h reads KV head h / num_kv_groups; Hq must equal
+ *   Hkv * num_kv_groups, num_kv_groups in {1, 2, 4, 8}, D == 256.  Key chunks whose
+ *   mask entries are all -inf are skipped without reading K/V.
+ *   workspace: device scratch of at least attn_decode_gqa_workspace_size()
+ *   bytes, 256-byte aligned, owned by the caller; its contents on entry are
+ *   ignored.
+ */
+ATTN_API size_t attn_decode_gqa_workspace_size(int B, int Hq, int S_ctx, int D);
+ATTN_API int attn_decode_gqa(const void *q, const void *k, const void *v, const float *attn_mask,
+                    float softmax_scale, int num_kv_groups, int B, int Hq, int Hkv, int S_ctx, int D,
+                    void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * History-only GQA prefill over a paged FP8 KV cache.
+ *
+ * Follows: Prefill Context-Parallel Attention POC for Trainium2, "Layout"
+ * (Q [Hq,Lq,D], K/V [blocks,Hkv,block_size,D], O [Hq,Lq,D]; Q heads sharing
+ * a KV head packed together; online max/sum in fp32; runtime additive score
+ * bias derived from actual_history_len) and "Current POC constraints" (BF16
+ * Q, FP8 E4M3FN K/V, head_dim a multiple of 128, block_size <= 512).  Only
+ * history keys participate; query tokens do not attend to one another.
+ *
+ *   q [Hq,Lq,D] bf16; k_cache/v_cache [num_blocks,Hkv,block_size,D] e4m3fn
+ *   codes with one fp32 dequantisation scale each (k = code * k_scale);
+ *   block_table int32 [max_blocks] maps logical block i to a physical block;
+ *   logical key j lives at block_table[j / block_size], row j % block_size.
+ *   Keys j >= actual_history_len get an additive -inf (blocks wholly past
+ *   it are never read).  out [Hq,Lq,D] bf16, lse fp32 [Hq,Lq] (nullable).
+ *   Requirements: D == 256, block_size a multiple of 64, 1 <= actual_history_len
+ *   <= max_blocks*block_size, Hq == Hkv*num_kv_groups, all pointers 16-byte
+ *   aligned.
+ */
+ATTN_API int attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache, float k_scale,
+                       float v_scale, const int32_t *block_table, int max_blocks, int num_blocks,
+                       int block_size, int actual_history_len, float softmax_scale, int num_kv_groups,
+                       int Hq, int Hkv, int Lq, int D, void *out, float *lse, hipStream_t stream);
+
+/*
+ * (Residual +) LayerNorm over the last dimension.
+ *
+ * Follows: gte-encoder-neuron-kernels, "Repository layout" ((residual +)
+ * LayerNorm kernel) and vit-encoder-neuron-kernels, "Supported shapes and
+ * limits" (standard LayerNorm, fp32 residual stream and statistics).
+ *
+ *   residual_out = residual + x          (x nullable: then residual_out = residual)
+ *   y = (residual_out - mean) * rstd * gamma + beta,  rstd = 1/sqrt(var + eps),
+ *   var the biased variance; statistics in fp32.
+ *   residual fp32 [rows,hidden]; x [rows,hidden] in x_dtype (BF16 or F32);
+ *   residual_out fp32 (nullable, may alias residual); y in y_dtype (BF16 or
+ *   F32); gamma/beta fp32 [hidden] nullable; mean/rstd fp32 [rows] nullable.
+ *   hidden must be a multiple of 8 and at most 8192; pointers 16-byte aligned.
+ */
+ATTN_API int res_ln(const float *residual, const void *x, attn_dtype_t x_dtype, const float *gamma,
+           const float *beta, float eps, int rows, int hidden, float *residual_out, void *y,
+           attn_dtype_t y_dtype, float *mean, float *rstd, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355ATTN_H */

@@ -1,0 +1,54 @@
+"""Comparison helpers for the GPU parity tests.
+
+Tolerances for floating-point outputs of bf16/fp8 inputs: max-abs 2e-2 and
+rel_l2 1e-2 against the fp64 oracle fed the same quantised values; LayerNorm
+statistics within 1e-5 (rstd relative; mean relative to sqrt(var + eps)),
+evaluated by running the oracle LayerNorm on the GPU's own fp32 residual
+stream so that the attention error does not leak into the statistics check.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+MAX_ABS = 2e-2
+REL_L2 = 1e-2
+LN_STAT = 1e-5
+
+
+def to64(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        return x.detach().float().cpu().double().numpy() if x.dtype != torch.float64 else x.cpu().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def metrics(got, ref) -> dict:
+    g, r = to64(got).ravel(), to64(ref).ravel()
+    d = g - r
+    nr = np.linalg.norm(r)
+    return {
+        "max_abs": float(np.max(np.abs(d))) if d.size else 0.0,
+        "rel_l2": float(np.linalg.norm(d) / nr) if nr > 0 else float(np.linalg.norm(d)),
+        "cos": float(g @ r / (np.linalg.norm(g) * nr)) if nr > 0 and np.linalg.norm(g) > 0 else 1.0,
+        "finite": bool(np.all(np.isfinite(g))),
+    }
+
+
+def assert_close(got, ref, what: str, max_abs: float = MAX_ABS, rel_l2: float = REL_L2) -> dict:
+    m = metrics(got, ref)
+    assert m["finite"], f"{what}: non-finite values {m}"
+    assert m["max_abs"] <= max_abs and m["rel_l2"] <= rel_l2, f"{what}: {m}"
+    return m
+
+
+def assert_ln_stats(res_out_gpu, mean_gpu, rstd_gpu, gamma, beta, eps, what: str):
+    import oracle
+
+    x = to64(res_out_gpu)
+    _, mu, rs = oracle.layernorm(x, None, None, eps)
+    mg, rg = to64(mean_gpu).ravel(), to64(rstd_gpu).ravel()
+    sd = 1.0 / rs  # sqrt(var + eps)
+    e_mean = float(np.max(np.abs(mg - mu) / sd))
+    e_rstd = float(np.max(np.abs(rg - rs) / rs))
+    assert e_mean <= LN_STAT and e_rstd <= LN_STAT, f"{what}: mean err {e_mean:.3g}, rstd err {e_rstd:.3g}"
+    return e_mean, e_rstd

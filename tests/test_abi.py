@@ -1,0 +1,166 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, maps one HIP runtime, and rejects bad arguments on the host
+before any launch.  Every call below fails validation, so nothing is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import transformer_attention_attn_amd as taa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355attn.h")
+
+BAD = 0x1001          # misaligned fake device address (never dereferenced: validation rejects first)
+FAKE = 0x100000       # 16-byte-aligned fake address, only used where another argument is invalid
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = text.split("extern \"C\" {", 1)[1]
+    return sorted(set(re.findall(r"ATTN_API\s+[\w\s\*]*?\b(\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return taa.load()
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared_functions()
+    for n in ("attn_encoder_fwd", "attn_decode_gqa", "attn_prefill_paged", "res_ln",
+              "attn_decode_gqa_workspace_size", "attn_status_string", "attn_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_single_hip_runtime_mapped(lib):
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    real = {os.path.realpath(p) for p in paths}
+    assert len(real) == 1, real
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert taa.attn_status_string(s).startswith(("ATTN_OK", "ATTN_ERR"))
+    assert taa.attn_status_string(99) == "unknown attn status"
+    assert taa.attn_version() == 10000
+
+
+def _enc(**kw):
+    a = taa.EncoderArgs()
+    a.q, a.k, a.v = FAKE, FAKE, FAKE
+    a.in_dtype = taa.ATTN_BF16
+    a.B, a.H, a.S_q, a.S_kv, a.D = 1, 2, 128, 128, 64
+    for i, s in enumerate((2 * 128 * 64, 128 * 64, 64, 1)):
+        a.q_stride[i] = a.k_stride[i] = a.v_stride[i] = a.out_stride[i] = s
+    a.softmax_scale = 0.125
+    a.out = FAKE
+    a.out_dtype = taa.ATTN_BF16
+    for k, v in kw.items():
+        if k.endswith("_stride"):
+            for i, s in enumerate(v):
+                getattr(a, k)[i] = s
+        else:
+            setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), taa.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), taa.ATTN_ERR_INVALID_ARG),
+    (dict(S_kv=-1), taa.ATTN_ERR_INVALID_ARG),
+    (dict(D=128), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(in_dtype=taa.ATTN_FP8_E4M3FN), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(q=BAD), taa.ATTN_ERR_INVALID_ARG),
+    (dict(k_stride=(0, 0, 64, 2)), taa.ATTN_ERR_INVALID_ARG),
+    (dict(v_stride=(0, 0, 60, 1)), taa.ATTN_ERR_INVALID_ARG),
+    (dict(out=None), taa.ATTN_ERR_INVALID_ARG),
+    (dict(residual=FAKE), taa.ATTN_ERR_INVALID_ARG),           # residual without residual_out
+    (dict(ln_out=FAKE), taa.ATTN_ERR_INVALID_ARG),             # LayerNorm needs the residual stream
+    (dict(softmax_scale=float("nan")), taa.ATTN_ERR_INVALID_ARG),
+    (dict(out_dtype=taa.ATTN_FP8_E4M3FN), taa.ATTN_ERR_UNSUPPORTED),
+])
+def test_encoder_validation(lib, kw, expect):
+    a = _enc(**kw)
+    assert lib.attn_encoder_fwd(ctypes.byref(a), None) == expect
+    assert lib.attn_encoder_fwd(None, None) == taa.ATTN_ERR_INVALID_ARG
+
+
+def _dec(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, mask=None, scale=1.0, G=2, B=8, Hq=16, Hkv=8, S=4096, D=256,
+                out=FAKE, ws=None, wsb=0)
+    args.update(kw)
+    return (args["q"], args["k"], args["v"], args["mask"], args["scale"], args["G"], args["B"], args["Hq"],
+            args["Hkv"], args["S"], args["D"], args["out"], args["ws"], args["wsb"], None)
+
+
+def test_decode_workspace_size(lib):
+    n = taa.attn_decode_gqa_workspace_size(8, 16, 4096, 256)
+    chunks = 4096 // 128
+    assert n >= 8 * 16 * chunks * (256 + 2) * 4
+    assert taa.attn_decode_gqa_workspace_size(0, 16, 4096, 256) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), taa.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=15), taa.ATTN_ERR_INVALID_ARG),                   # Hq != Hkv * G
+    (dict(D=128), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(G=16, Hq=128), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(G=3, Hq=24), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(k=BAD), taa.ATTN_ERR_INVALID_ARG),
+    (dict(), taa.ATTN_ERR_WORKSPACE),                          # no workspace
+    (dict(ws=FAKE, wsb=100), taa.ATTN_ERR_WORKSPACE),          # too small
+    (dict(ws=FAKE + 16, wsb=1 << 30), taa.ATTN_ERR_INVALID_ARG),  # misaligned workspace
+    (dict(scale=float("inf")), taa.ATTN_ERR_INVALID_ARG),
+])
+def test_decode_validation(lib, kw, expect):
+    assert lib.attn_decode_gqa(*_dec(**kw)) == expect
+
+
+def _pre(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=1.0, vs=1.0, bt=FAKE, maxb=256, nb=256, bs=512, L=120000, scale=0.0625,
+             G=16, Hq=32, Hkv=2, Lq=4096, D=256, out=FAKE, lse=None)
+    a.update(kw)
+    return (a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["maxb"], a["nb"], a["bs"], a["L"], a["scale"],
+            a["G"], a["Hq"], a["Hkv"], a["Lq"], a["D"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(bt=None), taa.ATTN_ERR_INVALID_ARG),
+    (dict(L=0), taa.ATTN_ERR_INVALID_ARG),
+    (dict(L=256 * 512 + 1), taa.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=31), taa.ATTN_ERR_INVALID_ARG),
+    (dict(D=128), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(bs=100, L=1000), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(ks=0.0), taa.ATTN_ERR_INVALID_ARG),
+    (dict(out=BAD), taa.ATTN_ERR_INVALID_ARG),
+])
+def test_prefill_validation(lib, kw, expect):
+    assert lib.attn_prefill_paged(*_pre(**kw)) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, None, 0, None, None, 1e-6, 4, 64, None, FAKE, 1, None, None, None), taa.ATTN_ERR_INVALID_ARG),
+    ((FAKE, None, 0, None, None, 1e-6, 4, 60, None, FAKE, 1, None, None, None), taa.ATTN_ERR_INVALID_ARG),
+    ((FAKE, None, 0, None, None, 1e-6, 4, 16384, None, FAKE, 1, None, None, None), taa.ATTN_ERR_UNSUPPORTED),
+    ((FAKE, None, 0, None, None, 1e-6, 4, 64, None, FAKE, 2, None, None, None), taa.ATTN_ERR_UNSUPPORTED),
+    ((FAKE, None, 0, None, None, -1.0, 4, 64, None, FAKE, 1, None, None, None), taa.ATTN_ERR_INVALID_ARG),
+    ((FAKE, None, 0, None, None, 1e-6, 4, 64, None, BAD, 1, None, None, None), taa.ATTN_ERR_INVALID_ARG),
+])
+def test_res_ln_validation(lib, args, expect):
+    assert lib.res_ln(*args, None) == expect
+
+
+def test_binding_raises_instead_of_falling_back():
+    with pytest.raises(ValueError):
+        taa.attn_decode_gqa(torch.zeros(1, 2, 1, 256), torch.zeros(1, 1, 8, 256), torch.zeros(1, 1, 8, 256), None,
+                            1.0, 2)

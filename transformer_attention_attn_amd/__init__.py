@@ -1,0 +1,245 @@
+"""Python binding of libmi355attn.so (gfx950 flash attention + residual LayerNorm).
+
+Argument marshalling only: every step of every call runs in the HIP kernels of
+the shared library.  torch supplies device memory (outputs are allocated here
+when the caller passes none) and the current HIP stream.  There is no CPU or
+PyTorch fallback: if the library is missing or a call is rejected, an exception
+is raised.
+
+Entry points (same names as the C ABI in include/mi355attn.h):
+  attn_encoder_fwd, attn_decode_gqa, attn_decode_gqa_workspace_size,
+  attn_prefill_paged, res_ln, attn_status_string, attn_version.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmi355attn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3FN = 0, 1, 2
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {attn_status_string(status)}")
+
+
+class EncoderArgs(ctypes.Structure):
+    """Mirror of attn_encoder_args_t."""
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("in_dtype", ctypes.c_int),
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("S_q", ctypes.c_int), ("S_kv", ctypes.c_int),
+        ("D", ctypes.c_int),
+        ("q_stride", ctypes.c_int64 * 4), ("k_stride", ctypes.c_int64 * 4), ("v_stride", ctypes.c_int64 * 4),
+        ("mask", ctypes.c_void_p), ("mask_stride_b", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float),
+        ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int), ("out_stride", ctypes.c_int64 * 4),
+        ("lse", ctypes.c_void_p),
+        ("residual", ctypes.c_void_p), ("residual_out", ctypes.c_void_p),
+        ("gamma", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("eps", ctypes.c_float),
+        ("ln_out", ctypes.c_void_p), ("ln_dtype", ctypes.c_int),
+        ("ln_mean", ctypes.c_void_p), ("ln_rstd", ctypes.c_void_p),
+    ]
+
+
+def load(path: str | None = None):
+    """Load the HIP library (torch is imported first so that the process maps
+    a single HIP runtime: the library binds to the one torch loaded)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m transformer_attention_attn_amd.build`")
+    L = ctypes.CDLL(p)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_status_string.argtypes = [I]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_version.restype = I
+    L.attn_encoder_fwd.argtypes = [ctypes.POINTER(EncoderArgs), P]
+    L.attn_encoder_fwd.restype = I
+    L.attn_decode_gqa_workspace_size.argtypes = [I, I, I, I]
+    L.attn_decode_gqa_workspace_size.restype = Z
+    L.attn_decode_gqa.argtypes = [P, P, P, P, F, I, I, I, I, I, I, P, P, Z, P]
+    L.attn_decode_gqa.restype = I
+    L.attn_prefill_paged.argtypes = [P, P, P, F, F, P, I, I, I, I, F, I, I, I, I, I, P, P, P]
+    L.attn_prefill_paged.restype = I
+    L.res_ln.argtypes = [P, P, I, P, P, F, I, I, P, P, I, P, P, P]
+    L.res_ln.restype = I
+    _lib = L
+    return L
+
+
+def attn_status_string(status: int) -> str:
+    return load().attn_status_string(int(status)).decode()
+
+
+def attn_version() -> int:
+    return load().attn_version()
+
+
+# ----------------------------------------------------------------------------- helpers
+
+_DT = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float8_e4m3fn: ATTN_FP8_E4M3FN}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int, what: str):
+    if rc != ATTN_OK:
+        raise AttnError(rc, what)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+# ----------------------------------------------------------------------------- entry points
+
+
+def attn_encoder_fwd(q, k, v, softmax_scale: float, mask=None, *, out=None, out_dtype=torch.bfloat16,
+                     want_out: bool = True, lse=None, residual=None, residual_out=None, gamma=None, beta=None,
+                     eps: float = 1e-6, ln_out=None, ln_dtype=torch.bfloat16, want_ln: bool | None = None,
+                     ln_mean=None, ln_rstd=None, stream=None):
+    """Non-causal SDPA over q/k/v [B,H,S,D] (bf16 or fp32, any strides with a
+    unit d stride), optional additive key mask [B,1,1,S_kv] fp32, optional
+    fused residual add (+ LayerNorm) into the fp32 residual stream [B,S,H*D].
+
+    Returns a dict of the produced tensors (out, lse, residual_out, ln_out,
+    ln_mean, ln_rstd as requested).
+    """
+    _need_cuda(q, k, v, mask, residual, gamma, beta)
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    res = {}
+    if want_out and out is None:
+        out = torch.empty(B, H, Sq, D, dtype=out_dtype, device=q.device)
+    if residual is not None and residual_out is None:
+        residual_out = torch.empty_like(residual)
+    if want_ln is None:
+        want_ln = residual is not None
+    if want_ln and ln_out is None:
+        ln_out = torch.empty(B, Sq, H * D, dtype=ln_dtype, device=q.device)
+        ln_mean = torch.empty(B * Sq, dtype=torch.float32, device=q.device) if ln_mean is None else ln_mean
+        ln_rstd = torch.empty(B * Sq, dtype=torch.float32, device=q.device) if ln_rstd is None else ln_rstd
+    a = EncoderArgs()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.in_dtype = _DT.get(q.dtype, -1)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share a dtype")
+    a.B, a.H, a.S_q, a.S_kv, a.D = B, H, Sq, Skv, D
+    for i in range(4):
+        a.q_stride[i], a.k_stride[i], a.v_stride[i] = q.stride(i), k.stride(i), v.stride(i)
+    if mask is not None:
+        if mask.dtype != torch.float32 or mask.shape[-1] != Skv or mask.stride(-1) != 1:
+            raise ValueError("mask must be fp32 [B,1,1,S_kv] with a unit last stride")
+        a.mask = mask.data_ptr()
+        a.mask_stride_b = mask.stride(0) if mask.shape[0] > 1 else Skv
+    a.softmax_scale = float(softmax_scale)
+    if out is not None:
+        a.out = out.data_ptr()
+        a.out_dtype = _DT.get(out.dtype, -1)
+        for i in range(4):
+            a.out_stride[i] = out.stride(i)
+    a.lse = None if lse is None else lse.data_ptr()
+    a.residual = None if residual is None else residual.data_ptr()
+    a.residual_out = None if residual_out is None else residual_out.data_ptr()
+    a.gamma = None if gamma is None else gamma.data_ptr()
+    a.beta = None if beta is None else beta.data_ptr()
+    a.eps = float(eps)
+    if ln_out is not None:
+        a.ln_out = ln_out.data_ptr()
+        a.ln_dtype = _DT.get(ln_out.dtype, -1)
+    a.ln_mean = None if ln_mean is None else ln_mean.data_ptr()
+    a.ln_rstd = None if ln_rstd is None else ln_rstd.data_ptr()
+    _check(load().attn_encoder_fwd(ctypes.byref(a), _stream(stream)), "attn_encoder_fwd")
+    for name, t in (("out", out), ("lse", lse), ("residual_out", residual_out), ("ln_out", ln_out),
+                    ("ln_mean", ln_mean), ("ln_rstd", ln_rstd)):
+        if t is not None:
+            res[name] = t
+    return res
+
+
+def attn_decode_gqa_workspace_size(B: int, Hq: int, S_ctx: int, D: int) -> int:
+    return int(load().attn_decode_gqa_workspace_size(B, Hq, S_ctx, D))
+
+
+def attn_decode_gqa(q, k, v, attn_mask, softmax_scale: float, num_kv_groups: int, *, out=None, workspace=None,
+                    stream=None):
+    """GQA single-token decode: q [B,Hq,1,D], k/v [B,Hkv,S_ctx,D] bf16, additive
+    mask [B,1,1,S_ctx] fp32 (or None).  Returns out [B,Hq,1,D] bf16."""
+    _need_cuda(q, k, v, attn_mask)
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    if attn_mask is not None and not attn_mask.is_contiguous():
+        raise ValueError("attn_mask must be contiguous")
+    B, Hq, _, D = q.shape
+    Hkv, S_ctx = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty(B, Hq, 1, D, dtype=torch.bfloat16, device=q.device)
+    need = attn_decode_gqa_workspace_size(B, Hq, S_ctx, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = load().attn_decode_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(attn_mask), float(softmax_scale), int(num_kv_groups),
+                                B, Hq, Hkv, S_ctx, D, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "attn_decode_gqa")
+    return out
+
+
+def attn_prefill_paged(q, k_cache, v_cache, k_scale: float, v_scale: float, block_table, actual_history_len: int,
+                       softmax_scale: float, num_kv_groups: int, *, out=None, lse=None, want_lse: bool = False,
+                       stream=None):
+    """History-only GQA prefill: q [Hq,Lq,D] bf16, caches [num_blocks,Hkv,bs,D]
+    e4m3fn, block_table int32 [max_blocks].  Returns out [Hq,Lq,D] bf16 (and lse)."""
+    _need_cuda(q, k_cache, v_cache, block_table)
+    if block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32")
+    for t in (q, k_cache, v_cache, block_table):
+        if not t.is_contiguous():
+            raise ValueError("prefill tensors must be contiguous")
+    Hq, Lq, D = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    if out is None:
+        out = torch.empty(Hq, Lq, D, dtype=torch.bfloat16, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty(Hq, Lq, dtype=torch.float32, device=q.device)
+    rc = load().attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale),
+                                   _ptr(block_table), block_table.numel(), nb, bs, int(actual_history_len),
+                                   float(softmax_scale), int(num_kv_groups), Hq, Hkv, Lq, D, _ptr(out), _ptr(lse),
+                                   _stream(stream))
+    _check(rc, "attn_prefill_paged")
+    return (out, lse) if lse is not None else out
+
+
+def res_ln(residual, x=None, gamma=None, beta=None, eps: float = 1e-6, *, residual_out=None, y=None,
+           y_dtype=torch.bfloat16, mean=None, rstd=None, stream=None):
+    """(Residual +) LayerNorm over the last dim of the fp32 residual [rows, hidden]."""
+    _need_cuda(residual, x, gamma, beta)
+    hidden = residual.shape[-1]
+    rows = residual.numel() // hidden
+    if y is None:
+        y = torch.empty(residual.shape, dtype=y_dtype, device=residual.device)
+    rc = load().res_ln(_ptr(residual), _ptr(x), _DT.get(x.dtype, -1) if x is not None else ATTN_F32, _ptr(gamma),
+                       _ptr(beta), float(eps), rows, hidden, _ptr(residual_out), _ptr(y), _DT.get(y.dtype, -1),
+                       _ptr(mean), _ptr(rstd), _stream(stream))
+    _check(rc, "res_ln")
+    return y

@@ -1,0 +1,227 @@
+// C-ABI entry points: host-side validation, then kernel launches on the
+// caller's stream.  No allocation, no synchronisation.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/mi355attn.h"
+#include "launch.h"
+
+using namespace mi355;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK: success";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument (null pointer, size, stride or alignment)";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: head_dim, dtype or shape not compiled in";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace missing or too small";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: HIP runtime error at launch";
+    default: return "unknown attn status";
+  }
+}
+
+int attn_version(void) { return 10000; }
+
+int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
+  if (!a) return ATTN_ERR_INVALID_ARG;
+  if (!a->q || !a->k || !a->v) return ATTN_ERR_INVALID_ARG;
+  if (a->B <= 0 || a->H <= 0 || a->S_q <= 0 || a->S_kv <= 0 || a->D <= 0) return ATTN_ERR_INVALID_ARG;
+  if (a->in_dtype != ATTN_BF16 && a->in_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (a->D != 64) return ATTN_ERR_UNSUPPORTED;
+  if (!(a->softmax_scale == a->softmax_scale) || isinf(a->softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!a->out && !a->residual_out) return ATTN_ERR_INVALID_ARG;
+  if ((a->residual == nullptr) != (a->residual_out == nullptr)) return ATTN_ERR_INVALID_ARG;
+  if (a->ln_out && !a->residual_out) return ATTN_ERR_INVALID_ARG;
+  if ((a->ln_mean || a->ln_rstd) && !a->ln_out) return ATTN_ERR_INVALID_ARG;
+  if (a->ln_out && !(a->eps >= 0.0f)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v)) return ATTN_ERR_INVALID_ARG;
+  const int64_t *st[3] = {a->q_stride, a->k_stride, a->v_stride};
+  for (int t = 0; t < 3; ++t) {
+    if (st[t][3] != 1) return ATTN_ERR_INVALID_ARG;
+    for (int i = 0; i < 3; ++i)
+      if (st[t][i] < 0 || st[t][i] % 8) return ATTN_ERR_INVALID_ARG;
+  }
+  if (a->out) {
+    if (a->out_dtype != ATTN_BF16 && a->out_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(a->out) || a->out_stride[3] != 1) return ATTN_ERR_INVALID_ARG;
+    for (int i = 0; i < 3; ++i)
+      if (a->out_stride[i] < 0 || a->out_stride[i] % 8) return ATTN_ERR_INVALID_ARG;
+  }
+  if (a->residual && (!aligned16(a->residual) || !aligned16(a->residual_out))) return ATTN_ERR_INVALID_ARG;
+  if (a->mask && (a->mask_stride_b < a->S_kv && a->B > 1)) return ATTN_ERR_INVALID_ARG;
+  const int64_t hidden = (int64_t)a->H * a->D;
+  if (a->ln_out) {
+    if (a->ln_dtype != ATTN_BF16 && a->ln_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (hidden > res_ln_max_hidden()) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(a->ln_out) || (a->gamma && !aligned16(a->gamma)) || (a->beta && !aligned16(a->beta)))
+      return ATTN_ERR_INVALID_ARG;
+  }
+  if ((int64_t)a->B * a->H * ((a->S_q + encoder_rows_per_block() - 1) / encoder_rows_per_block()) > 0x7fffffffLL)
+    return ATTN_ERR_UNSUPPORTED;
+
+  EncoderLaunch L;
+  memset(&L, 0, sizeof L);
+  L.q = a->q;
+  L.k = a->k;
+  L.v = a->v;
+  for (int i = 0; i < 4; ++i) {
+    L.qs[i] = a->q_stride[i];
+    L.ks[i] = a->k_stride[i];
+    L.vs[i] = a->v_stride[i];
+    L.os[i] = a->out_stride[i];
+  }
+  L.mask = a->mask;
+  L.mask_sb = a->mask_stride_b;
+  L.B = a->B;
+  L.H = a->H;
+  L.Sq = a->S_q;
+  L.Skv = a->S_kv;
+  L.c = a->softmax_scale * 1.4426950408889634f;
+  L.out = a->out;
+  L.out_f32 = a->out_dtype == ATTN_F32;
+  L.lse = a->lse;
+  L.res = a->residual;
+  L.res_out = a->residual_out;
+  int rc = hip_status(launch_encoder(L, a->in_dtype == ATTN_F32, stream));
+  if (rc != ATTN_OK || !a->ln_out) return rc;
+
+  ResLnLaunch R;
+  memset(&R, 0, sizeof R);
+  R.res = a->residual_out;
+  R.x = nullptr;
+  R.gamma = a->gamma;
+  R.beta = a->beta;
+  R.eps = a->eps;
+  R.rows = a->B * a->S_q;
+  R.hidden = (int)hidden;
+  R.res_out = nullptr;
+  R.y = a->ln_out;
+  R.y_bf16 = a->ln_dtype == ATTN_BF16;
+  R.mean = a->ln_mean;
+  R.rstd = a->ln_rstd;
+  return hip_status(launch_res_ln(R, stream));
+}
+
+size_t attn_decode_gqa_workspace_size(int B, int Hq, int S_ctx, int D) {
+  if (B <= 0 || Hq <= 0 || S_ctx <= 0 || D <= 0) return 0;
+  const int64_t n_chunks = (S_ctx + decode_chunk_keys() - 1) / decode_chunk_keys();
+  const int64_t parts = (int64_t)B * Hq * n_chunks;
+  const int64_t o_bytes = ((parts * D * 4) + 255) / 256 * 256;
+  return (size_t)(o_bytes + parts * 2 * 4);
+}
+
+int attn_decode_gqa(const void *q, const void *k, const void *v, const float *attn_mask, float softmax_scale,
+                    int num_kv_groups, int B, int Hq, int Hkv, int S_ctx, int D, void *out, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_ctx <= 0 || D <= 0 || num_kv_groups <= 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)Hkv * num_kv_groups != Hq) return ATTN_ERR_INVALID_ARG;
+  if (D != 256) return ATTN_ERR_UNSUPPORTED;
+  if (num_kv_groups > decode_max_groups() || (num_kv_groups & (num_kv_groups - 1)))
+    return ATTN_ERR_UNSUPPORTED;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
+  if (attn_mask && !aligned16(attn_mask)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn_decode_gqa_workspace_size(B, Hq, S_ctx, D);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_INVALID_ARG;
+  const int n_chunks = (S_ctx + decode_chunk_keys() - 1) / decode_chunk_keys();
+  if (n_chunks > 65535 || Hkv > 65535 || B > 65535 || Hq > 65535) return ATTN_ERR_UNSUPPORTED;
+
+  DecodeLaunch L;
+  memset(&L, 0, sizeof L);
+  L.q = static_cast<const __bf16 *>(q);
+  L.k = static_cast<const __bf16 *>(k);
+  L.v = static_cast<const __bf16 *>(v);
+  L.mask = attn_mask;
+  L.B = B;
+  L.Hq = Hq;
+  L.Hkv = Hkv;
+  L.G = num_kv_groups;
+  L.S_ctx = S_ctx;
+  L.n_chunks = n_chunks;
+  L.c = softmax_scale * 1.4426950408889634f;
+  const int64_t parts = (int64_t)B * Hq * n_chunks;
+  L.ws_o = static_cast<float *>(workspace);
+  L.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + ((parts * D * 4) + 255) / 256 * 256);
+  L.out = static_cast<__bf16 *>(out);
+  return hip_status(launch_decode(L, stream));
+}
+
+int attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache, float k_scale, float v_scale,
+                       const int32_t *block_table, int max_blocks, int num_blocks, int block_size,
+                       int actual_history_len, float softmax_scale, int num_kv_groups, int Hq, int Hkv, int Lq,
+                       int D, void *out, float *lse, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !out) return ATTN_ERR_INVALID_ARG;
+  if (max_blocks <= 0 || num_blocks <= 0 || block_size <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || D <= 0 ||
+      num_kv_groups <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)Hkv * num_kv_groups != Hq) return ATTN_ERR_INVALID_ARG;
+  if (actual_history_len < 1 || (int64_t)actual_history_len > (int64_t)max_blocks * block_size)
+    return ATTN_ERR_INVALID_ARG;
+  if (D != 256) return ATTN_ERR_UNSUPPORTED;
+  if (block_size % 64 != 0 || block_size % prefill_key_tile() != 0) return ATTN_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
+  if (((int64_t)num_blocks * Hkv * block_size * D) > ((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)num_kv_groups * Lq > 0x7fffffffLL - 256) return ATTN_ERR_UNSUPPORTED;
+
+  PrefillLaunch L;
+  memset(&L, 0, sizeof L);
+  L.q = static_cast<const __bf16 *>(q);
+  L.kc = static_cast<const uint8_t *>(k_cache);
+  L.vc = static_cast<const uint8_t *>(v_cache);
+  L.bt = block_table;
+  L.bs = block_size;
+  L.L_act = actual_history_len;
+  L.Hkv = Hkv;
+  L.G = num_kv_groups;
+  L.Lq = Lq;
+  L.c = softmax_scale * k_scale * 1.4426950408889634f;
+  L.v_scale = v_scale;
+  L.out = static_cast<__bf16 *>(out);
+  L.lse = lse;
+  return hip_status(launch_prefill(L, stream));
+}
+
+int res_ln(const float *residual, const void *x, attn_dtype_t x_dtype, const float *gamma, const float *beta,
+           float eps, int rows, int hidden, float *residual_out, void *y, attn_dtype_t y_dtype, float *mean,
+           float *rstd, hipStream_t stream) {
+  if (!residual || !y) return ATTN_ERR_INVALID_ARG;
+  if (rows <= 0 || hidden <= 0 || hidden % 8) return ATTN_ERR_INVALID_ARG;
+  if (hidden > res_ln_max_hidden()) return ATTN_ERR_UNSUPPORTED;
+  if (x && x_dtype != ATTN_BF16 && x_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (y_dtype != ATTN_BF16 && y_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(residual) || !aligned16(y) || (x && !aligned16(x)) || (residual_out && !aligned16(residual_out)) ||
+      (gamma && !aligned16(gamma)) || (beta && !aligned16(beta)))
+    return ATTN_ERR_INVALID_ARG;
+  ResLnLaunch R;
+  memset(&R, 0, sizeof R);
+  R.res = residual;
+  R.x = x;
+  R.x_bf16 = x_dtype == ATTN_BF16;
+  R.gamma = gamma;
+  R.beta = beta;
+  R.eps = eps;
+  R.rows = rows;
+  R.hidden = hidden;
+  R.res_out = residual_out;
+  R.y = y;
+  R.y_bf16 = y_dtype == ATTN_BF16;
+  R.mean = mean;
+  R.rstd = rstd;
+  return hip_status(launch_res_ln(R, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,649 @@
+// Tiled online-softmax ("flash") attention forward for gfx950.
+//
+// One kernel template serves two callers:
+//   * the non-causal encoder (q/k/v [B,H,S,D] bf16 or fp32, optional additive
+//     key mask, fused residual-add epilogue);
+//   * the history-only GQA prefill over a paged FP8 (e4m3fn) KV cache, whose
+//     G query heads per KV head are packed into the M dimension (rows r of a KV
+//     head are (head g, token t) with r = g*Lq + t).
+//
+// Prefill Context-Parallel Attention POC for Trainium2, "Layout": Q heads that
+// share a KV head are packed together, online max/sum stay fp32 while the
+// probabilities are bf16 with fp32 accumulation, and keys past
+// actual_history_len receive an additive -inf bias.  Here the bias is
+// derived inside the kernel from the length and cache blocks wholly past it
+// are never read.
+//
+// Per workgroup: BM = 32*NT*RG query rows, RG row-group waves times NSPLIT
+// key-split waves.  Split s handles key tiles s, s+NSPLIT, ...; the splits
+// are merged through LDS at the end (log-sum-exp merge).  Each wave owns
+// 32*NT rows; its Q fragments stay in registers for the whole loop.
+//
+// Per key tile (BN keys), per wave:
+//   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys on M, query rows on N), so
+//   every lane owns one query row (lane % 32) and 16 keys per 32-key block;
+//   row max: in-lane max + one exchange with lane ^ 32;
+//   P = exp2(S*c - m) in fp32, packed to bf16 straight into the B operand of
+//   O^T += V^T P^T (d on M, rows on N): P never leaves registers.
+// K tiles sit in LDS as [key][d] (16-byte chunks XOR-swizzled by key), V tiles
+// as V^T [d][key] with keys permuted so each lane's 8 keys of a PV step are
+// one contiguous 16-byte read.  Global loads for tile i+1 are issued before
+// tile i is computed and written to the other LDS stage afterwards.
+#include "device_common.h"
+#include "launch.h"
+
+namespace mi355 {
+
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
+
+template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_>
+struct Geo {
+  static constexpr int D = D_, BN = BN_, NT = NT_, RG = RG_, NSPLIT = NSPLIT_;
+  static constexpr int GRP = GRP_;  // LDS fragments read per pipelined group
+  static constexpr int WAVES = RG * NSPLIT, THREADS = 64 * WAVES;
+  static constexpr int BM = 32 * NT * RG;
+  static constexpr int KT = BN * D * 2;  // bytes of one bf16 K tile
+  static constexpr int VT = D * BN * 2;  // bytes of one bf16 V^T tile
+  static constexpr int SPLIT_BYTES = KT + VT;
+  static constexpr int STAGE = NSPLIT * SPLIT_BYTES;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int KB = BN / 32;  // 32-key blocks per tile
+  static constexpr int SD = D / 16;   // k-steps of the QK^T contraction
+  static constexpr int MT = D / 32;   // d tiles of O^T
+  static constexpr int VROWS = (BN * 2 >= 128) ? 1 : 128 / (BN * 2);
+  static constexpr int VCH = BN / 8;  // 16-byte chunks per V^T row
+  static constexpr int VSW = VCH < 8 ? VCH : 8;
+  static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(LDS <= 65536, "LDS budget");
+
+  // byte offset of 16-byte chunk c of key row `key` in a K tile
+  static __device__ __forceinline__ int k_off(int key, int c) { return key * (D * 2) + ((c ^ (key & 7)) << 4); }
+  // byte offset of 16-byte chunk c of d-row `d` in a V^T tile
+  static __device__ __forceinline__ int v_off(int d, int c) {
+    return d * (BN * 2) + ((c ^ ((d / VROWS) % VSW)) << 4);
+  }
+  // storage position of key t of a tile: swap bits 2 and 3 so that the 8 keys
+  // lane-half h feeds to PV step kk of block kb are positions kb*32+16kk+8h+0..7
+  static __device__ __forceinline__ int vpos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+};
+
+// ------------------------------------------------------------------ sources
+
+// Encoder K/V: [B,H,S_kv,D] strided, bf16 or fp32 (fp32 rounded to bf16 here).
+template <class G, bool F32>
+struct EncSrc {
+  const char *kb, *vb;  // this (b,h)'s K and V base
+  int64_t ks, vs;       // element stride between keys
+  int n_keys;
+  static constexpr int ES = F32 ? 4 : 2;
+  static constexpr int KU = G::BN * (G::D / 8);            // K units (8 elements) per tile
+  static constexpr int VU = (G::BN / 2) * (G::D / 8);      // V units (2 keys x 8 elements)
+  static constexpr int UK = G::NSPLIT * KU / G::THREADS;
+  static constexpr int UV = G::NSPLIT * VU / G::THREADS;
+  static_assert(UK * G::THREADS == G::NSPLIT * KU && UV * G::THREADS == G::NSPLIT * VU, "units");
+  static_assert(VU % 64 == 0 && (G::D / 8) % 8 == 0, "V unit mapping");
+  static constexpr int W = F32 ? 2 : 1;  // 16-byte loads per 8 elements
+  struct Stage {
+    u32x4_t k[UK][W];
+    u32x4_t v[UV][2][W];
+  };
+
+  __device__ __forceinline__ void load(Stage &st, int it, int tid) const {
+#pragma unroll
+    for (int j = 0; j < UK; ++j) {
+      const int u = tid + j * G::THREADS;
+      const int sp = u / KU, w = u % KU;
+      const int t = w / (G::D / 8), c = w % (G::D / 8);
+      const int key = (it * G::NSPLIT + sp) * G::BN + t;
+      const char *p = kb + ((int64_t)key * ks + 8 * c) * ES;
+#pragma unroll
+      for (int x = 0; x < W; ++x) st.k[j][x] = key < n_keys ? ldg<u32x4_t>(p + 16 * x) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < UV; ++j) {
+      const int u = tid + j * G::THREADS;
+      const int sp = u / VU, w = u % VU;
+      const int p2 = (w % 8) + 8 * ((w / 64) % (G::BN / 16));
+      const int c8 = ((w / 8) % 8) + 8 * (w / (64 * (G::BN / 16)));
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int key = (it * G::NSPLIT + sp) * G::BN + 2 * p2 + r;
+        const char *p = vb + ((int64_t)key * vs + 8 * c8) * ES;
+#pragma unroll
+        for (int x = 0; x < W; ++x) st.v[j][r][x] = key < n_keys ? ldg<u32x4_t>(p + 16 * x) : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  }
+
+  // 8 elements of a raw unit -> 4 packed bf16 pairs (element order kept)
+  static __device__ __forceinline__ u32x4_t to_bf16(const u32x4_t (&x)[W]) {
+    if constexpr (F32) {
+      return u32x4_t{pack_bf16(__uint_as_float(x[0][0]), __uint_as_float(x[0][1])),
+                     pack_bf16(__uint_as_float(x[0][2]), __uint_as_float(x[0][3])),
+                     pack_bf16(__uint_as_float(x[1][0]), __uint_as_float(x[1][1])),
+                     pack_bf16(__uint_as_float(x[1][2]), __uint_as_float(x[1][3]))};
+    } else {
+      return x[0];
+    }
+  }
+
+  __device__ __forceinline__ void store(const Stage &st, char *stage, int tid) const {
+    asm volatile("" : "+v"(tid));  // recompute the per-thread addresses here instead of keeping them live
+#pragma unroll
+    for (int j = 0; j < UK; ++j) {
+      const int u = tid + j * G::THREADS;
+      const int sp = u / KU, w = u % KU;
+      const int t = w / (G::D / 8), c = w % (G::D / 8);
+      *reinterpret_cast<u32x4_t *>(stage + sp * G::SPLIT_BYTES + G::k_off(t, c)) = to_bf16(st.k[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < UV; ++j) {
+      const int u = tid + j * G::THREADS;
+      const int sp = u / VU, w = u % VU;
+      const int p2 = (w % 8) + 8 * ((w / 64) % (G::BN / 16));
+      const int c8 = ((w / 8) % 8) + 8 * (w / (64 * (G::BN / 16)));
+      const u32x4_t a = to_bf16(st.v[j][0]), b = to_bf16(st.v[j][1]);
+      const int pos = G::vpos(2 * p2);
+      char *vt = stage + sp * G::SPLIT_BYTES + G::KT;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = (i & 1) ? (a[i >> 1] >> 16) : (a[i >> 1] & 0xffffu);
+        const uint32_t hi = (i & 1) ? (b[i >> 1] & 0xffff0000u) : (b[i >> 1] << 16);
+        const int d = 8 * c8 + i;
+        *reinterpret_cast<uint32_t *>(vt + G::v_off(d, pos >> 3) + (pos & 7) * 2) = lo | hi;
+      }
+    }
+  }
+};
+
+// Paged FP8 K/V: cache [num_blocks, Hkv, bs, D] e4m3fn; the K tile of 16 fp8
+// per unit, V 2 keys x 8 fp8 per unit.  Converted to bf16 exactly on store.
+template <class G>
+struct PagedSrc {
+  const uint8_t *kc, *vc;
+  const int32_t *bt;
+  int64_t head_off;  // kvh * bs * D
+  int64_t blk_stride;  // Hkv * bs * D
+  int bs, n_keys;
+  static constexpr int KU = G::BN * (G::D / 16);
+  static constexpr int VU = (G::BN / 2) * (G::D / 8);
+  static constexpr int UK = KU / G::THREADS;
+  static constexpr int UV = VU / G::THREADS;
+  static_assert(G::NSPLIT == 1, "paged source is single-split");
+  static_assert(UK * G::THREADS == KU && UV * G::THREADS == VU, "units");
+  struct Stage {
+    u32x4_t k[UK];
+    u32x2_t v[UV][2];
+  };
+
+  __device__ __forceinline__ void load(Stage &st, int it, int tid) const {
+    asm volatile("" : "+v"(tid));  // recompute the per-thread offsets here instead of keeping them live
+    const int key0 = it * G::BN;
+    const int64_t base = (int64_t)bt[key0 / bs] * blk_stride + head_off + (int64_t)(key0 % bs) * G::D;
+#pragma unroll
+    for (int j = 0; j < UK; ++j) {
+      const int u = tid + j * G::THREADS;
+      const int t = u / (G::D / 16), c = u % (G::D / 16);
+      st.k[j] = key0 + t < n_keys ? ldg<u32x4_t>(kc + base + t * G::D + 16 * c) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < UV; ++j) {
+      const int w = tid + j * G::THREADS;
+      const int p2 = (w % 8) + 8 * ((w / 64) % (G::BN / 16));
+      const int c8 = ((w / 8) % 8) + 8 * (w / (64 * (G::BN / 16)));
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int t = 2 * p2 + r;
+        st.v[j][r] = key0 + t < n_keys ? ldg<u32x2_t>(vc + base + t * G::D + 8 * c8) : u32x2_t{0, 0};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(const Stage &st, char *stage, int tid) const {
+    asm volatile("" : "+v"(tid));  // recompute the per-thread addresses here instead of keeping them live
+#pragma unroll
+    for (int j = 0; j < UK; ++j) {
+      const int u = tid + j * G::THREADS;
+      const int t = u / (G::D / 16), c = u % (G::D / 16);
+      const u32x4_t x = st.k[j];
+      const u32x4_t lo = {e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]),
+                          e4m3x2_to_bf16x2<false>(x[1]), e4m3x2_to_bf16x2<true>(x[1])};
+      const u32x4_t hi = {e4m3x2_to_bf16x2<false>(x[2]), e4m3x2_to_bf16x2<true>(x[2]),
+                          e4m3x2_to_bf16x2<false>(x[3]), e4m3x2_to_bf16x2<true>(x[3])};
+      *reinterpret_cast<u32x4_t *>(stage + G::k_off(t, 2 * c)) = lo;
+      *reinterpret_cast<u32x4_t *>(stage + G::k_off(t, 2 * c + 1)) = hi;
+    }
+#pragma unroll
+    for (int j = 0; j < UV; ++j) {
+      const int w = tid + j * G::THREADS;
+      const int p2 = (w % 8) + 8 * ((w / 64) % (G::BN / 16));
+      const int c8 = ((w / 8) % 8) + 8 * (w / (64 * (G::BN / 16)));
+      const u32x2_t xa = st.v[j][0], xb = st.v[j][1];
+      const uint32_t a[4] = {e4m3x2_to_bf16x2<false>(xa[0]), e4m3x2_to_bf16x2<true>(xa[0]),
+                             e4m3x2_to_bf16x2<false>(xa[1]), e4m3x2_to_bf16x2<true>(xa[1])};
+      const uint32_t b[4] = {e4m3x2_to_bf16x2<false>(xb[0]), e4m3x2_to_bf16x2<true>(xb[0]),
+                             e4m3x2_to_bf16x2<false>(xb[1]), e4m3x2_to_bf16x2<true>(xb[1])};
+      const int pos = G::vpos(2 * p2);
+      char *vt = stage + G::KT;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = (i & 1) ? (a[i >> 1] >> 16) : (a[i >> 1] & 0xffffu);
+        const uint32_t hi = (i & 1) ? (b[i >> 1] & 0xffff0000u) : (b[i >> 1] << 16);
+        *reinterpret_cast<uint32_t *>(vt + G::v_off(8 * c8 + i, pos >> 3) + (pos & 7) * 2) = lo | hi;
+      }
+    }
+  }
+};
+
+// ------------------------------------------------------------------ core loop
+
+template <class G>
+struct WaveState {
+  f32x16_t o[G::NT][G::MT];
+  float m[G::NT], l[G::NT];
+};
+
+// One key tile for one wave.  `mask` (nullable) is the additive key mask of
+// this batch row in natural-log units.
+template <class G>
+__device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&qf)[G::NT][G::SD],
+                                             const char *kt, const char *vt, int key0, int n_keys,
+                                             float c, const float *mask, int lane) {
+  const int l32 = lane & 31, h = lane >> 5;
+  f32x16_t s[G::NT][G::KB];
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt)
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb) s[nt][kb] = f32x16_t{};
+
+  // QK^T: fragments f = sd*KB + kb, read from LDS GRP at a time one group
+  // ahead of the MFMAs that consume them (bounded register footprint).
+  {
+    constexpr int NF = G::SD * G::KB, GRP = G::GRP, NG = NF / GRP;
+    static_assert(NF % GRP == 0, "QK fragment groups");
+    // K fragment (kb, sd): row kb*32 + l32, chunk 2*sd + h.  The XOR swizzle
+    // only touches the low 3 chunk bits, so the address is one of 4 per-lane
+    // bases plus a compile-time offset.
+    int kbase[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kbase[j] = l32 * (G::D * 2) + (((2 * j + h) ^ (l32 & 7)) << 4);
+    auto kfrag = [&](int f) {
+      const int kb = f % G::KB, sd = f / G::KB;
+      return *reinterpret_cast<const u32x4_t *>(kt + kbase[sd & 3] + kb * 32 * G::D * 2 + (sd >> 2) * 128);
+    };
+    u32x4_t fb[2][GRP];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) fb[0][j] = kfrag(j);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) {
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) fb[(g + 1) & 1][j] = kfrag((g + 1) * GRP + j);
+      }
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const int f = g * GRP + j;
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt)
+          s[nt][f % G::KB] = mfma32(as_bf16x8(fb[g & 1][j]), as_bf16x8(qf[nt][f / G::KB]), s[nt][f % G::KB]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  const bool tail = key0 + G::BN > n_keys;
+  float mx[G::NT];
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = key0 + kb * 32 + (v >> 2) * 8 + 4 * h + (v & 3);
+        float x = s[nt][kb][v] * c;
+        if (mask) x += (key < n_keys ? mask[key] : 0.0f) * kLog2e;
+        if (tail && key >= n_keys) x = -INFINITY;
+        s[nt][kb][v] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    mx[nt] = fmaxf(mloc, xor32(mloc));
+  }
+
+  // Lazy rescale: the reference max m of a row only moves when the tile max
+  // exceeds it by more than kTau (log2 units), so p = 2^(s - m) <= 2^kTau and
+  // the O/l rescale (a VALU pass over every accumulator) is rare.  Exact: the
+  // final O/l uses one consistent reference per row.
+  bool grow = false;
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) grow |= mx[nt] > ws.m[nt] + kTau;
+  if (__ballot(grow) != 0) {
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) {
+      const float m_new = fmaxf(ws.m[nt], mx[nt]);
+      const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(ws.m[nt] - m_new);
+      ws.m[nt] = m_new;
+      ws.l[nt] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] *= alpha;
+    }
+  }
+
+  u32x4_t pb[G::NT][G::KB][2];
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const float m_use = ws.m[nt] == -INFINITY ? 0.0f : ws.m[nt];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = fast_exp2(s[nt][kb][v] - m_use);
+        s[nt][kb][v] = p;
+        lsum += p;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        pb[nt][kb][kk] = u32x4_t{pack_bf16(s[nt][kb][8 * kk + 0], s[nt][kb][8 * kk + 1]),
+                                 pack_bf16(s[nt][kb][8 * kk + 2], s[nt][kb][8 * kk + 3]),
+                                 pack_bf16(s[nt][kb][8 * kk + 4], s[nt][kb][8 * kk + 5]),
+                                 pack_bf16(s[nt][kb][8 * kk + 6], s[nt][kb][8 * kk + 7])};
+    }
+    ws.l[nt] += lsum;
+  }
+
+  // PV: fragments f = (kb*2 + kk)*MT + mt of V^T, same group pipelining.
+  {
+    constexpr int NF = G::KB * 2 * G::MT, GRP = G::GRP, NG = NF / GRP;
+    static_assert(NF % GRP == 0, "PV fragment groups");
+    // V^T fragment (mt, kb, kk): row mt*32 + l32, chunk kb*4 + kk*2 + h; the
+    // swizzle depends on the lane only, so KB*2 per-lane bases + offsets.
+    const int vsw = (l32 / G::VROWS) % G::VSW;
+    int vbase[G::KB * 2];
+#pragma unroll
+    for (int j = 0; j < G::KB * 2; ++j) vbase[j] = l32 * (G::BN * 2) + (((2 * j + h) ^ vsw) << 4);
+    auto vfrag = [&](int f) {
+      const int mt = f % G::MT, j = f / G::MT;
+      return *reinterpret_cast<const u32x4_t *>(vt + vbase[j] + mt * 32 * G::BN * 2);
+    };
+    u32x4_t fb[2][GRP];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) fb[0][j] = vfrag(j);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g + 1 < NG) {
+#pragma unroll
+        for (int j = 0; j < GRP; ++j) fb[(g + 1) & 1][j] = vfrag((g + 1) * GRP + j);
+      }
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const int f = g * GRP + j;
+        const int mt = f % G::MT, kk = (f / G::MT) % 2, kb = f / (2 * G::MT);
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt)
+          ws.o[nt][mt] = mfma32(as_bf16x8(fb[g & 1][j]), as_bf16x8(pb[nt][kb][kk]), ws.o[nt][mt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// The pipelined key loop shared by both kernels.  Returns with every wave's
+// state complete and the LDS free (a barrier has been passed).
+template <class G, class Src>
+__device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, const u32x4_t (&qf)[G::NT][G::SD],
+                                           char *smem, float c, const float *mask) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sp = wave / G::RG;
+  const int n_tiles = (src.n_keys + G::BN - 1) / G::BN;
+  const int n_iter = (n_tiles + G::NSPLIT - 1) / G::NSPLIT;
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    ws.m[nt] = -INFINITY;
+    ws.l[nt] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] = f32x16_t{};
+  }
+  if (n_iter <= 0) return;
+
+  typename Src::Stage st;
+  src.load(st, 0, tid);
+  src.store(st, smem, tid);
+  __syncthreads();
+  for (int it = 0; it < n_iter; ++it) {
+    const bool more = it + 1 < n_iter;
+    if (more) src.load(st, it + 1, tid);
+    // A split whose tile index runs past the last tile computes on an
+    // all-zero, fully masked tile (p = 0): no branch, so the accumulators
+    // never meet a control-flow merge.
+    const int ti = it * G::NSPLIT + sp;
+    const char *base = smem + (it & 1) * G::STAGE + sp * G::SPLIT_BYTES;
+    compute_tile<G>(ws, qf, base, base + G::KT, ti * G::BN, src.n_keys, c, mask, lane);
+    if (more) src.store(st, smem + ((it + 1) & 1) * G::STAGE, tid);
+    __syncthreads();
+  }
+}
+
+// Merge the NSPLIT key-split partial states into the split-0 waves (LDS).
+template <class G>
+__device__ __forceinline__ void merge_splits(WaveState<G> &ws, char *smem) {
+  if constexpr (G::NSPLIT > 1) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rg = wave % G::RG, sp = wave / G::RG;
+    constexpr int NREG = G::NT * (G::MT * 16 + 2);
+    float *red = reinterpret_cast<float *>(smem);
+    static_assert((G::NSPLIT - 1) * G::RG * NREG * 64 * 4 <= G::LDS, "merge space");
+    if (sp > 0) {
+      float *dst = red + ((sp - 1) * G::RG + rg) * NREG * 64 + lane;
+      int r = 0;
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt) {
+        dst[(r++) * 64] = ws.m[nt];
+        dst[(r++) * 64] = ws.l[nt];
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) dst[(r++) * 64] = ws.o[nt][mt][v];
+      }
+    }
+    __syncthreads();
+    if (sp == 0) {
+#pragma unroll
+      for (int s = 1; s < G::NSPLIT; ++s) {
+        const float *src = red + ((s - 1) * G::RG + rg) * NREG * 64 + lane;
+        int r = 0;
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt) {
+          const float m2 = src[(r++) * 64], l2 = src[(r++) * 64];
+          const float M = fmaxf(ws.m[nt], m2);
+          const float Mu = M == -INFINITY ? 0.0f : M;
+          const float a1 = fast_exp2(ws.m[nt] - Mu), a2 = fast_exp2(m2 - Mu);
+          ws.m[nt] = M;
+          ws.l[nt] = ws.l[nt] * a1 + l2 * a2;
+#pragma unroll
+          for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) ws.o[nt][mt][v] = ws.o[nt][mt][v] * a1 + src[(r++) * 64] * a2;
+        }
+      }
+    }
+  }
+}
+
+// Linear workgroup id -> logical tile id, so that consecutive logical tiles
+// (which share K/V) run on the same XCD: the hardware deals workgroups to the
+// 8 XCDs round-robin.
+__device__ __forceinline__ int xcd_remap(int lin, int total) {
+  if (total % 8) return lin;
+  return (lin % 8) * (total / 8) + lin / 8;
+}
+
+// ------------------------------------------------------------------ encoder kernel
+
+template <class G, bool F32IN>
+__global__ __launch_bounds__(G::THREADS) void encoder_fwd_kernel(EncoderLaunch a) {
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
+  const int n_qt = (a.Sq + G::BM - 1) / G::BM;
+  const int total = n_qt * a.H * a.B;
+  const int lid = xcd_remap(blockIdx.x, total);
+  const int qt = lid % n_qt, h = (lid / n_qt) % a.H, b = lid / (n_qt * a.H);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave % G::RG, sp = wave / G::RG;
+  const int l32 = lane & 31, hh = lane >> 5;
+  constexpr int ES = F32IN ? 4 : 2;
+
+  // Q fragments (B operand of S^T = K Q^T): row = lane%32, 8 d per lane-half
+  u32x4_t qf[G::NT][G::SD];
+  const char *qb = reinterpret_cast<const char *>(a.q) + (b * a.qs[0] + h * a.qs[1]) * ES;
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const int row = qt * G::BM + (rg * G::NT + nt) * 32 + l32;
+#pragma unroll
+    for (int sd = 0; sd < G::SD; ++sd) {
+      const char *p = qb + (row * a.qs[2] + 16 * sd + 8 * hh) * ES;
+      if (row < a.Sq) {
+        if constexpr (F32IN) {
+          const u32x4_t x0 = ldg<u32x4_t>(p), x1 = ldg<u32x4_t>(p + 16);
+          qf[nt][sd] = u32x4_t{pack_bf16(__uint_as_float(x0[0]), __uint_as_float(x0[1])),
+                               pack_bf16(__uint_as_float(x0[2]), __uint_as_float(x0[3])),
+                               pack_bf16(__uint_as_float(x1[0]), __uint_as_float(x1[1])),
+                               pack_bf16(__uint_as_float(x1[2]), __uint_as_float(x1[3]))};
+        } else {
+          qf[nt][sd] = ldg<u32x4_t>(p);
+        }
+      } else {
+        qf[nt][sd] = u32x4_t{0, 0, 0, 0};
+      }
+    }
+  }
+
+  EncSrc<G, F32IN> src;
+  src.kb = reinterpret_cast<const char *>(a.k) + (b * a.ks[0] + h * a.ks[1]) * ES;
+  src.vb = reinterpret_cast<const char *>(a.v) + (b * a.vs[0] + h * a.vs[1]) * ES;
+  src.ks = a.ks[2];
+  src.vs = a.vs[2];
+  src.n_keys = a.Skv;
+  const float *mask = a.mask ? a.mask + b * a.mask_sb : nullptr;
+
+  WaveState<G> ws;
+  flash_loop<G>(ws, src, qf, smem, a.c, mask);
+  merge_splits<G>(ws, smem);
+  if (sp != 0) return;
+
+  const int HD = a.H * G::D;
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const int row = qt * G::BM + (rg * G::NT + nt) * 32 + l32;
+    const float lt = ws.l[nt] + xor32(ws.l[nt]);
+    if (row >= a.Sq) continue;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (a.lse && hh == 0)
+      a.lse[((int64_t)b * a.H + h) * a.Sq + row] = lt > 0.0f ? (ws.m[nt] + __log2f(lt)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = mt * 32 + r4 * 8 + 4 * hh;
+        const f32x4_t val = {ws.o[nt][mt][4 * r4 + 0] * inv, ws.o[nt][mt][4 * r4 + 1] * inv,
+                             ws.o[nt][mt][4 * r4 + 2] * inv, ws.o[nt][mt][4 * r4 + 3] * inv};
+        if (a.out) {
+          const int64_t off = b * a.os[0] + h * a.os[1] + row * a.os[2] + d0;
+          if (a.out_f32) {
+            *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(a.out) + off) = val;
+          } else {
+            *reinterpret_cast<u32x2_t *>(reinterpret_cast<__bf16 *>(a.out) + off) =
+                u32x2_t{pack_bf16(val[0], val[1]), pack_bf16(val[2], val[3])};
+          }
+        }
+        if (a.res_out) {
+          const int64_t off = ((int64_t)b * a.Sq + row) * HD + h * G::D + d0;
+          const f32x4_t r = ldg<f32x4_t>(a.res + off);
+          *reinterpret_cast<f32x4_t *>(a.res_out + off) = r + val;
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------ prefill kernel
+
+template <class G>
+__global__ __launch_bounds__(G::THREADS)
+void prefill_paged_kernel(PrefillLaunch a) {
+  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
+  const int rows = a.G * a.Lq;  // packed (head, token) rows per KV head
+  const int n_rt = (rows + G::BM - 1) / G::BM;
+  const int lid = xcd_remap(blockIdx.x, n_rt * a.Hkv);
+  const int rt = lid % n_rt, kvh = lid / n_rt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave % G::RG;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int64_t row_base = (int64_t)kvh * rows;  // first packed row of this KV head in [Hq*Lq]
+
+  u32x4_t qf[G::NT][G::SD];
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
+#pragma unroll
+    for (int sd = 0; sd < G::SD; ++sd)
+      qf[nt][sd] = r < rows ? ldg<u32x4_t>(a.q + (row_base + r) * G::D + 16 * sd + 8 * hh) : u32x4_t{0, 0, 0, 0};
+  }
+
+  PagedSrc<G> src;
+  src.kc = a.kc;
+  src.vc = a.vc;
+  src.bt = a.bt;
+  src.head_off = (int64_t)kvh * a.bs * G::D;
+  src.blk_stride = (int64_t)a.Hkv * a.bs * G::D;
+  src.bs = a.bs;
+  src.n_keys = a.L_act;
+
+  WaveState<G> ws;
+  flash_loop<G>(ws, src, qf, smem, a.c, nullptr);
+
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
+    const float lt = ws.l[nt] + xor32(ws.l[nt]);
+    if (r >= rows) continue;
+    const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
+    if (a.lse && hh == 0) a.lse[row_base + r] = lt > 0.0f ? (ws.m[nt] + __log2f(lt)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = mt * 32 + r4 * 8 + 4 * hh;
+        *reinterpret_cast<u32x2_t *>(a.out + (row_base + r) * G::D + d0) =
+            u32x2_t{pack_bf16(ws.o[nt][mt][4 * r4 + 0] * inv, ws.o[nt][mt][4 * r4 + 1] * inv),
+                    pack_bf16(ws.o[nt][mt][4 * r4 + 2] * inv, ws.o[nt][mt][4 * r4 + 3] * inv)};
+      }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+using EncGeo = Geo<64, 64, 1, 4, 2, 4>;     // BM 128, 8 waves, 2 key splits
+using PrefGeo = Geo<256, 32, 1, 8, 1, 1>;   // BM 256, 8 waves of 32 rows, 2 waves per SIMD
+
+hipError_t launch_encoder(const EncoderLaunch &a, bool f32_in, hipStream_t stream) {
+  const int n_qt = (a.Sq + EncGeo::BM - 1) / EncGeo::BM;
+  const dim3 grid(n_qt * a.H * a.B), block(EncGeo::THREADS);
+  if (f32_in)
+    hipLaunchKernelGGL((encoder_fwd_kernel<EncGeo, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((encoder_fwd_kernel<EncGeo, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+int encoder_rows_per_block() { return EncGeo::BM; }
+
+hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream) {
+  const int rows = a.G * a.Lq;
+  const int n_rt = (rows + PrefGeo::BM - 1) / PrefGeo::BM;
+  const dim3 grid(n_rt * a.Hkv), block(PrefGeo::THREADS);
+  hipLaunchKernelGGL((prefill_paged_kernel<PrefGeo>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+int prefill_key_tile() { return PrefGeo::BN; }
+
+}  // namespace mi355

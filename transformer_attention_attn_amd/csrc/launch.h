@@ -1,0 +1,69 @@
+// Kernel launch records passed by value from the C-ABI layer to the kernels.
+// Host-validated; the kernels trust these fields.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355 {
+
+struct EncoderLaunch {
+  const void *q, *k, *v;
+  int64_t qs[4], ks[4], vs[4];  // element strides {b,h,s,d}, d stride 1
+  const float *mask;            // nullable, natural-log additive [B, S_kv] rows
+  int64_t mask_sb;
+  int B, H, Sq, Skv;
+  float c;                      // softmax_scale * log2(e)
+  void *out;                    // nullable
+  int64_t os[4];
+  int out_f32;
+  float *lse;                   // nullable [B,H,Sq]
+  const float *res;             // nullable [B,Sq,H*D]
+  float *res_out;               // nullable (non-null iff res non-null)
+};
+
+struct PrefillLaunch {
+  const __bf16 *q;
+  const uint8_t *kc, *vc;
+  const int32_t *bt;
+  int bs, L_act, Hkv, G, Lq;
+  float c;        // softmax_scale * k_scale * log2(e)
+  float v_scale;
+  __bf16 *out;
+  float *lse;     // nullable
+};
+
+struct DecodeLaunch {
+  const __bf16 *q, *k, *v;
+  const float *mask;  // nullable [B, S_ctx]
+  int B, Hq, Hkv, G, S_ctx, n_chunks;
+  float c;            // softmax_scale * log2(e)
+  float *ws_o;        // [B*Hq*n_chunks, D]
+  float *ws_ml;       // [B*Hq*n_chunks, 2]
+  __bf16 *out;
+};
+
+struct ResLnLaunch {
+  const float *res;
+  const void *x;      // nullable
+  int x_bf16;
+  const float *gamma, *beta;
+  float eps;
+  int rows, hidden;
+  float *res_out;     // nullable
+  void *y;
+  int y_bf16;
+  float *mean, *rstd; // nullable
+};
+
+hipError_t launch_encoder(const EncoderLaunch &a, bool f32_in, hipStream_t stream);
+int encoder_rows_per_block();
+hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream);
+int prefill_key_tile();
+hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
+int decode_chunk_keys();
+int decode_max_groups();
+hipError_t launch_res_ln(const ResLnLaunch &a, hipStream_t stream);
+int res_ln_max_hidden();
+
+}  // namespace mi355
