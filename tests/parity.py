@@ -14,6 +14,10 @@ import torch
 MAX_ABS = 2e-2
 REL_L2 = 1e-2
 LN_STAT = 1e-5
+# log-sum-exp outputs: the kernels normalise by the sum of the bf16-rounded
+# probabilities they multiply into V (each within 2^-9 relative of the exact
+# one), so |delta lse| <= ln(1 + 2^-9) + fp32 rounding; allow 2^-8.
+LSE_ABS = 2.0 ** -8
 
 
 def to64(x) -> np.ndarray:

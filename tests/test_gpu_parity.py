@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import assert_close, assert_ln_stats, metrics, to64
+from parity import LSE_ABS, assert_close, assert_ln_stats, metrics, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -92,7 +92,7 @@ def test_encoder_token_major_output_and_lse(gpu_lib):
     assert_close(r["out"], ref, "token-major out")
     assert r["out"].permute(0, 2, 1, 3).is_contiguous()
     m = metrics(r["lse"], lse)
-    assert m["max_abs"] < 1e-3, m
+    assert m["max_abs"] < LSE_ABS, m
 
 
 def test_encoder_fully_masked_rows(gpu_lib):
@@ -125,10 +125,23 @@ def test_encoder_masked_keys_poisoned(gpu_lib):
     case = W.encoder_custom(9, 1, 2, 190, masked_lens=[150])
     _say("[encoder] masked-key poisoning")
     r1 = _enc_run(gpu_lib, case, with_ln=False)
-    case.k[:, :, 150:] = 1e4
-    case.v[:, :, 150:] = -3e4
+    case.k[:, :, 150:] = float("nan")
+    case.v[:, :, 150:] = float("inf")
     r2 = _enc_run(gpu_lib, case, with_ln=False)
     assert torch.equal(r1["out"], r2["out"])
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1e-3, 2.5])
+def test_encoder_scale_sign_and_magnitude(gpu_lib, scale):
+    case = W.encoder_custom(10, 2, 2, 160, masked_lens=[160, 97], scale=scale)
+    _say(f"[encoder] softmax_scale={scale}")
+    r = _enc_run(gpu_lib, case, with_ln=False, lse=True)
+    ref, lse = oracle.sdpa(case.q, case.k, case.v, case.scale, case.mask, return_lse=True)
+    assert_close(r["out"], ref, f"scale {scale}")
+    assert metrics(r["lse"], lse)["max_abs"] < LSE_ABS
+    nomask = W.encoder_custom(10, 2, 2, 160, scale=scale)
+    r = _enc_run(gpu_lib, nomask, with_ln=False)
+    assert_close(r["out"], oracle.sdpa(nomask.q, nomask.k, nomask.v, nomask.scale), f"scale {scale}, no mask")
 
 
 def test_encoder_one_hot_selects_value_row(gpu_lib):
@@ -259,7 +272,7 @@ def test_prefill_small_full_check(gpu_lib, Hq, Hkv, Lq, nb, bs, L):
     ref, rlse = oracle.prefill_paged(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale,
                                      case.block_table, case.L_act, case.scale, rows, return_lse=True)
     assert_close(out, ref, "prefill out")
-    assert metrics(lse, rlse)["max_abs"] < 2e-3
+    assert metrics(lse, rlse)["max_abs"] < LSE_ABS
 
 
 def test_prefill_full_config_sampled_rows(gpu_lib):
@@ -273,6 +286,15 @@ def test_prefill_full_config_sampled_rows(gpu_lib):
     assert_close(got, ref, "prefill full (sampled rows)")
     o2 = _pre_run(gpu_lib, case)
     assert torch.equal(out, o2)
+
+
+@pytest.mark.parametrize("scale", [-0.05, 0.0])
+def test_prefill_scale_sign(gpu_lib, scale):
+    case = W.prefill_paged(61, 4, 2, 50, 256, 4, 64, 210, n_rows=50, scale=scale)
+    out = _pre_run(gpu_lib, case)
+    ref = oracle.prefill_paged(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale, case.block_table,
+                               case.L_act, case.scale, torch.arange(case.Lq))
+    assert_close(out, ref, f"prefill scale {scale}")
 
 
 def test_prefill_poisoned_tail_ignored(gpu_lib):

@@ -12,6 +12,17 @@ namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Kernels take the exp2 scale c > 0: a negative scale becomes a positive one on
+// -q (exact), and a zero scale a positive one so small that every exponent
+// rounds to 2^0 exactly (|c * s| < 2^-40 for any finite bf16 score), which is
+// what a zero scale gives.
+void exp2_scale(float scale, float *c, int *q_neg) {
+  float x = scale * 1.4426950408889634f;
+  *q_neg = x < 0.0f;
+  x = fabsf(x);
+  *c = x > 0.0f ? x : 1e-30f;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
 }  // namespace
@@ -49,6 +60,7 @@ int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
     if (st[t][3] != 1) return ATTN_ERR_INVALID_ARG;
     for (int i = 0; i < 3; ++i)
       if (st[t][i] < 0 || st[t][i] % 8) return ATTN_ERR_INVALID_ARG;
+    if (st[t][2] >= ((int64_t)1 << 22)) return ATTN_ERR_UNSUPPORTED;  // per-tile offsets are 32-bit
   }
   if (a->out) {
     if (a->out_dtype != ATTN_BF16 && a->out_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
@@ -85,7 +97,7 @@ int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
   L.H = a->H;
   L.Sq = a->S_q;
   L.Skv = a->S_kv;
-  L.c = a->softmax_scale * 1.4426950408889634f;
+  exp2_scale(a->softmax_scale, &L.c, &L.q_neg);
   L.out = a->out;
   L.out_f32 = a->out_dtype == ATTN_F32;
   L.lse = a->lse;
@@ -187,7 +199,7 @@ int attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache, 
   L.Hkv = Hkv;
   L.G = num_kv_groups;
   L.Lq = Lq;
-  L.c = softmax_scale * k_scale * 1.4426950408889634f;
+  exp2_scale(softmax_scale * k_scale, &L.c, &L.q_neg);
   L.v_scale = v_scale;
   L.out = static_cast<__bf16 *>(out);
   L.lse = lse;

@@ -28,46 +28,28 @@ namespace mi355 {
 
 constexpr int kDecD = 256;
 constexpr int kDecChunk = 128;  // keys per workgroup
-constexpr int kDecRound = 16;   // keys per wave round
 constexpr int kDecGmax = 8;     // query heads per KV head supported
 
 template <int G>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeLaunch a) {
-  __shared__ __attribute__((aligned(16))) float sc[4][G][kDecRound];
+  constexpr int KW = kDecChunk / 4;  // keys per wave (two MFMA groups of 16)
+  __shared__ __attribute__((aligned(16))) float sc[4][G][KW];
   __shared__ __attribute__((aligned(16))) float red_o[4][G][kDecD];
   __shared__ float red_ml[4][G][2];
 
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int key_base = chunk * kDecChunk;
   const float *mrow = a.mask ? a.mask + (int64_t)b * a.S_ctx : nullptr;
   const int64_t part0 = ((int64_t)b * a.Hq + (int64_t)kvh * G) * a.n_chunks + chunk;  // head g adds g*n_chunks
+  const int key0 = chunk * kDecChunk + wave * KW;
 
-  // Whole-chunk early exit when no key is live.
-  bool live = false;
-  if (tid < kDecChunk) {
-    const int key = key_base + tid;
-    live = key < a.S_ctx && (mrow == nullptr || mrow[key] != -INFINITY);
+  // Liveness of this wave's 32 keys (one mask read per lane, then a vote).
+  bool kl = false;
+  if (lane < KW) {
+    const int key = key0 + lane;
+    kl = key < a.S_ctx && (mrow == nullptr || mrow[key] != -INFINITY);
   }
-  if (!__syncthreads_or(live)) {
-    if (tid < G) {
-      a.ws_ml[(part0 + (int64_t)tid * a.n_chunks) * 2 + 0] = -INFINITY;
-      a.ws_ml[(part0 + (int64_t)tid * a.n_chunks) * 2 + 1] = 0.0f;
-    }
-    return;
-  }
-
-  // q^T as the B operand: lane l holds q[g = l%16][32s + 8(l/16) .. +7], zero for g >= G.
-  const int gq = lane & 15, quad = lane >> 4;
-  u32x4_t qf[kDecD / 32];
-  const __bf16 *qrow = a.q + ((int64_t)b * a.Hq + (int64_t)kvh * G + gq) * kDecD;
-#pragma unroll
-  for (int s = 0; s < kDecD / 32; ++s)
-    qf[s] = gq < G ? ldg<u32x4_t>(qrow + 32 * s + 8 * quad) : u32x4_t{0, 0, 0, 0};
-
-  const int64_t kv_off = ((int64_t)b * a.Hkv + kvh) * a.S_ctx * kDecD;
-  const __bf16 *kbase = a.k + kv_off;
-  const __bf16 *vbase = a.v + kv_off;
+  const uint64_t live = __ballot(kl);
 
   float m[G], l[G];
   f32x4_t o[G];
@@ -78,86 +60,83 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeLaunch a) {
     o[g] = f32x4_t{0, 0, 0, 0};
   }
 
-  for (int rd = 0; rd < kDecChunk / 4 / kDecRound; ++rd) {
-    const int key0 = key_base + wave * (kDecChunk / 4) + rd * kDecRound;
-    // Liveness of this round's 16 keys: lanes 0..15 look, the wave votes.
-    bool kl = false;
-    if (lane < kDecRound) {
-      const int key = key0 + lane;
-      kl = key < a.S_ctx && (mrow == nullptr || mrow[key] != -INFINITY);
+  if (live != 0) {
+    const int gq = lane & 15, quad = lane >> 4;
+    const int64_t kv_off = ((int64_t)b * a.Hkv + kvh) * a.S_ctx * kDecD;
+    const __bf16 *kbase = a.k + kv_off;
+    const __bf16 *vbase = a.v + kv_off;
+    // All K/V loads of the wave go out together; dead keys are not loaded.
+    u32x4_t kf[2][kDecD / 32];
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      const bool kin = (live >> (grp * 16 + gq)) & 1;
+#pragma unroll
+      for (int s = 0; s < kDecD / 32; ++s)
+        kf[grp][s] = kin ? ldg<u32x4_t>(kbase + (int64_t)(key0 + grp * 16 + gq) * kDecD + 32 * s + 8 * quad)
+                         : u32x4_t{0, 0, 0, 0};
     }
-    const uint64_t live_bits = __ballot(kl);
-    if (live_bits == 0) continue;
-
-    // K: A operand rows key0 + lane%16; V: lane owns columns 4*lane .. +3.
-    // Dead keys are not loaded (zeros), so masked K/V bytes never enter the math.
-    const bool kin = (live_bits >> gq) & 1;
-    u32x4_t kf[kDecD / 32];
+    u32x2_t vf[KW];
+#pragma unroll
+    for (int j = 0; j < KW; ++j)
+      vf[j] = ((live >> j) & 1) ? ldg<u32x2_t>(vbase + (int64_t)(key0 + j) * kDecD + 4 * lane) : u32x2_t{0, 0};
+    // q^T as the B operand: lane l holds q[g = l%16][32s + 8(l/16) .. +7], zero for g >= G.
+    u32x4_t qf[kDecD / 32];
+    const __bf16 *qrow = a.q + ((int64_t)b * a.Hq + (int64_t)kvh * G + gq) * kDecD;
 #pragma unroll
     for (int s = 0; s < kDecD / 32; ++s)
-      kf[s] = kin ? ldg<u32x4_t>(kbase + (int64_t)(key0 + gq) * kDecD + 32 * s + 8 * quad) : u32x4_t{0, 0, 0, 0};
-    u32x2_t vf[kDecRound];
-#pragma unroll
-    for (int j = 0; j < kDecRound; ++j)
-      vf[j] = ((live_bits >> j) & 1) ? ldg<u32x2_t>(vbase + (int64_t)(key0 + j) * kDecD + 4 * lane) : u32x2_t{0, 0};
+      qf[s] = gq < G ? ldg<u32x4_t>(qrow + 32 * s + 8 * quad) : u32x4_t{0, 0, 0, 0};
 
-    f32x4_t s4 = {0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < kDecD / 32; ++s) s4 = mfma16(as_bf16x8(kf[s]), as_bf16x8(qf[s]), s4);
-    // lane l now holds S^T[key = 4*(l/16) + i][head g = l%16]
-    if (gq < G) {
-      f32x4_t x;
+    for (int grp = 0; grp < 2; ++grp) {
+      f32x4_t s4 = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kj = 4 * quad + i;
-        const float mk = ((live_bits >> kj) & 1) ? (mrow ? mrow[key0 + kj] : 0.0f) : -INFINITY;
-        x[i] = mk == -INFINITY ? -INFINITY : s4[i] * a.c + mk * kLog2e;
+      for (int s = 0; s < kDecD / 32; ++s) s4 = mfma16(as_bf16x8(kf[grp][s]), as_bf16x8(qf[s]), s4);
+      // lane l holds S^T[key = grp*16 + 4*(l/16) + i][head g = l%16]
+      if (gq < G) {
+        f32x4_t x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kj = grp * 16 + 4 * quad + i;
+          const float mk = ((live >> kj) & 1) ? (mrow ? mrow[key0 + kj] : 0.0f) : -INFINITY;
+          x[i] = mk == -INFINITY ? -INFINITY : s4[i] * a.c + mk * kLog2e;
+        }
+        *reinterpret_cast<f32x4_t *>(&sc[wave][gq][grp * 16 + 4 * quad]) = x;
       }
-      *reinterpret_cast<f32x4_t *>(&sc[wave][gq][4 * quad]) = x;
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
 
-    float p[G][kDecRound];
+    // Softmax over the wave's 32 keys for each head, then PV on the VALU.
 #pragma unroll
     for (int g = 0; g < G; ++g) {
+      float p[KW];
 #pragma unroll
-      for (int q4 = 0; q4 < kDecRound / 4; ++q4) {
+      for (int q4 = 0; q4 < KW / 4; ++q4) {
         const f32x4_t t = *reinterpret_cast<const f32x4_t *>(&sc[wave][g][4 * q4]);
-        p[g][4 * q4 + 0] = t[0];
-        p[g][4 * q4 + 1] = t[1];
-        p[g][4 * q4 + 2] = t[2];
-        p[g][4 * q4 + 3] = t[3];
+        p[4 * q4 + 0] = t[0];
+        p[4 * q4 + 1] = t[1];
+        p[4 * q4 + 2] = t[2];
+        p[4 * q4 + 3] = t[3];
       }
-      float mr = p[g][0];
+      float mr = p[0];
 #pragma unroll
-      for (int j = 1; j < kDecRound; ++j) mr = fmaxf(mr, p[g][j]);
-      const float m_new = fmaxf(m[g], mr);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float alpha = fast_exp2(m[g] - m_use);
-      m[g] = m_new;
+      for (int j = 1; j < KW; ++j) mr = fmaxf(mr, p[j]);
+      m[g] = mr;
+      const float m_use = mr == -INFINITY ? 0.0f : mr;
       float ls = 0.0f;
+      f32x4_t acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int j = 0; j < kDecRound; ++j) {
-        p[g][j] = fast_exp2(p[g][j] - m_use);
-        ls += p[g][j];
+      for (int j = 0; j < KW; ++j) {
+        const float pj = fast_exp2(p[j] - m_use);
+        ls += pj;
+        acc[0] += pj * bf16_lo(vf[j][0]);
+        acc[1] += pj * bf16_hi(vf[j][0]);
+        acc[2] += pj * bf16_lo(vf[j][1]);
+        acc[3] += pj * bf16_hi(vf[j][1]);
       }
-      l[g] = l[g] * alpha + ls;
-      o[g] *= alpha;
+      l[g] = ls;
+      o[g] = acc;
     }
-#pragma unroll
-    for (int j = 0; j < kDecRound; ++j) {
-      const float v0 = bf16_lo(vf[j][0]), v1 = bf16_hi(vf[j][0]);
-      const float v2 = bf16_lo(vf[j][1]), v3 = bf16_hi(vf[j][1]);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        o[g][0] += p[g][j] * v0;
-        o[g][1] += p[g][j] * v1;
-        o[g][2] += p[g][j] * v2;
-        o[g][3] += p[g][j] * v3;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
   }
 
   // Merge the 4 waves' partials (fixed order) and write the chunk partial.
@@ -185,7 +164,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeLaunch a) {
       acc += red_o[w][g][tid] * sw;
     }
     const int64_t part = part0 + (int64_t)g * a.n_chunks;
-    a.ws_o[part * kDecD + tid] = acc;
+    if (M != -INFINITY) a.ws_o[part * kDecD + tid] = acc;
     if (tid == 0) {
       a.ws_ml[part * 2 + 0] = M;
       a.ws_ml[part * 2 + 1] = L;
@@ -193,6 +172,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeLaunch a) {
   }
 }
 
+// One workgroup per (batch, query head); thread d owns output column d.  The
+// chunk statistics are loaded first (independent loads), then every live
+// chunk's partial column, weighted by 2^(m_c - M); dead chunks (m_c = -inf,
+// whose partial was never written) are selected away, not branched around.
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeLaunch a) {
   const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int64_t p0 = ((int64_t)b * a.Hq + hq) * a.n_chunks;
@@ -200,12 +183,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeLaunch a) {
   for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, a.ws_ml[(p0 + c) * 2]);
   const float Mu = M == -INFINITY ? 0.0f : M;
   float L = 0.0f, acc = 0.0f;
+#pragma unroll 8
   for (int c = 0; c < a.n_chunks; ++c) {
     const float mc = a.ws_ml[(p0 + c) * 2];
-    if (mc == -INFINITY) continue;
-    const float w = fast_exp2(mc - Mu);
-    L += a.ws_ml[(p0 + c) * 2 + 1] * w;
-    acc += a.ws_o[(p0 + c) * kDecD + d] * w;
+    const float lc = a.ws_ml[(p0 + c) * 2 + 1];
+    const float oc = a.ws_o[(p0 + c) * kDecD + d];
+    const bool dead = mc == -INFINITY;
+    const float w = dead ? 0.0f : fast_exp2(mc - Mu);
+    L += dead ? 0.0f : lc * w;
+    acc += dead ? 0.0f : oc * w;
   }
   const float r = L > 0.0f ? acc / L : 0.0f;
   a.out[((int64_t)b * a.Hq + hq) * kDecD + d] = (__bf16)r;

@@ -22,13 +22,17 @@
 // Per key tile (BN keys), per wave:
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys on M, query rows on N), so
 //   every lane owns one query row (lane % 32) and 16 keys per 32-key block;
-//   row max: in-lane max + one exchange with lane ^ 32;
-//   P = exp2(S*c - m) in fp32, packed to bf16 straight into the B operand of
-//   O^T += V^T P^T (d on M, rows on N): P never leaves registers.
+//   row max: in-lane max + one v_permlane32_swap with the partner lane;
+//   P = exp2(S*c - m) with the scale folded into one FMA (c > 0, log2 units),
+//   packed to bf16 straight into the B operand of O^T += V^T P^T (d on M,
+//   rows on N): P never leaves registers; the row sum is taken on the packed
+//   bf16 P with v_dot2_f32_bf16, so it normalises exactly the values that were
+//   multiplied into V.
 // K tiles sit in LDS as [key][d] (16-byte chunks XOR-swizzled by key), V tiles
 // as V^T [d][key] with keys permuted so each lane's 8 keys of a PV step are
-// one contiguous 16-byte read.  Global loads for tile i+1 are issued before
-// tile i is computed and written to the other LDS stage afterwards.
+// one contiguous 16-byte read.  Global loads for the next PF tiles stay in
+// flight in registers (uniform 64-bit base + 32-bit per-thread offset) while a
+// tile is computed from one LDS stage and the next is written to the other.
 #include "device_common.h"
 #include "launch.h"
 
@@ -36,10 +40,11 @@ namespace mi355 {
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
-template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_>
+template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int PF_>
 struct Geo {
   static constexpr int D = D_, BN = BN_, NT = NT_, RG = RG_, NSPLIT = NSPLIT_;
   static constexpr int GRP = GRP_;  // LDS fragments read per pipelined group
+  static constexpr int PF = PF_;    // key tiles in flight in registers (global-load prefetch depth)
   static constexpr int WAVES = RG * NSPLIT, THREADS = 64 * WAVES;
   static constexpr int BM = 32 * NT * RG;
   static constexpr int KT = BN * D * 2;  // bytes of one bf16 K tile
@@ -65,19 +70,39 @@ struct Geo {
   // storage position of key t of a tile: swap bits 2 and 3 so that the 8 keys
   // lane-half h feeds to PV step kk of block kb are positions kb*32+16kk+8h+0..7
   static __device__ __forceinline__ int vpos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+  // V unit w (2 keys x 8 d) -> key pair p2, d-chunk c8: 8 key pairs x 8 chunks
+  // per wave, so that the transposed LDS writes of a wave spread over banks.
+  static __device__ __forceinline__ int v_pair(int w) { return (w % 8) + 8 * ((w / 64) % (BN / 16)); }
+  static __device__ __forceinline__ int v_chunk(int w) { return ((w / 8) % 8) + 8 * (w / (64 * (BN / 16))); }
 };
+
+// Write the 8 (key 2p, key 2p+1) bf16 pairs of d-rows d0..d0+7 into a V^T tile.
+template <class G>
+__device__ __forceinline__ void store_vt_pairs(char *vt, int p2, int c8, const u32x4_t &a, const u32x4_t &b) {
+  const int pos = G::vpos(2 * p2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo = (i & 1) ? (a[i >> 1] >> 16) : (a[i >> 1] & 0xffffu);
+    const uint32_t hi = (i & 1) ? (b[i >> 1] & 0xffff0000u) : (b[i >> 1] << 16);
+    *reinterpret_cast<uint32_t *>(vt + G::v_off(8 * c8 + i, pos >> 3) + (pos & 7) * 2) = lo | hi;
+  }
+}
 
 // ------------------------------------------------------------------ sources
 
 // Encoder K/V: [B,H,S_kv,D] strided, bf16 or fp32 (fp32 rounded to bf16 here).
+// Unit u of an iteration belongs to split u / KU; its key row is fixed per
+// thread, so the address is base(iteration) + a 32-bit per-thread offset.
 template <class G, bool F32>
 struct EncSrc {
-  const char *kb, *vb;  // this (b,h)'s K and V base
-  int64_t ks, vs;       // element stride between keys
+  const char *kb, *vb;       // this (b,h)'s K and V base
+  int64_t kstep, vstep;      // bytes between consecutive iterations (NSPLIT*BN keys)
+  int64_t ks, vs;            // element stride between keys
   int n_keys;
+  const float *mask;         // nullable: V rows of -inf-masked keys are not loaded (zeros)
   static constexpr int ES = F32 ? 4 : 2;
-  static constexpr int KU = G::BN * (G::D / 8);            // K units (8 elements) per tile
-  static constexpr int VU = (G::BN / 2) * (G::D / 8);      // V units (2 keys x 8 elements)
+  static constexpr int KU = G::BN * (G::D / 8);        // K units (8 elements) per tile
+  static constexpr int VU = (G::BN / 2) * (G::D / 8);  // V units (2 keys x 8 elements)
   static constexpr int UK = G::NSPLIT * KU / G::THREADS;
   static constexpr int UV = G::NSPLIT * VU / G::THREADS;
   static_assert(UK * G::THREADS == G::NSPLIT * KU && UV * G::THREADS == G::NSPLIT * VU, "units");
@@ -89,28 +114,32 @@ struct EncSrc {
   };
 
   __device__ __forceinline__ void load(Stage &st, int it, int tid) const {
+    asm volatile("" : "+v"(tid));  // per-thread offsets are cheap 32-bit math: recompute, don't keep live
+    const char *kbase = kb + it * kstep;
+    const char *vbase = vb + it * vstep;
+    const int key_it = it * G::NSPLIT * G::BN;
 #pragma unroll
     for (int j = 0; j < UK; ++j) {
       const int u = tid + j * G::THREADS;
       const int sp = u / KU, w = u % KU;
-      const int t = w / (G::D / 8), c = w % (G::D / 8);
-      const int key = (it * G::NSPLIT + sp) * G::BN + t;
-      const char *p = kb + ((int64_t)key * ks + 8 * c) * ES;
+      const int t = sp * G::BN + w / (G::D / 8), c = w % (G::D / 8);
+      const uint32_t off = (uint32_t)(t * ks + 8 * c) * ES;
 #pragma unroll
-      for (int x = 0; x < W; ++x) st.k[j][x] = key < n_keys ? ldg<u32x4_t>(p + 16 * x) : u32x4_t{0, 0, 0, 0};
+      for (int x = 0; x < W; ++x)
+        st.k[j][x] = key_it + t < n_keys ? ldg<u32x4_t>(kbase + off + 16 * x) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < UV; ++j) {
       const int u = tid + j * G::THREADS;
       const int sp = u / VU, w = u % VU;
-      const int p2 = (w % 8) + 8 * ((w / 64) % (G::BN / 16));
-      const int c8 = ((w / 8) % 8) + 8 * (w / (64 * (G::BN / 16)));
+      const int t0 = sp * G::BN + 2 * G::v_pair(w), c8 = G::v_chunk(w);
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const int key = (it * G::NSPLIT + sp) * G::BN + 2 * p2 + r;
-        const char *p = vb + ((int64_t)key * vs + 8 * c8) * ES;
+        const uint32_t off = (uint32_t)((t0 + r) * vs + 8 * c8) * ES;
+        const int key = key_it + t0 + r;
+        const bool live = key < n_keys && (mask == nullptr || mask[key] != -INFINITY);
 #pragma unroll
-        for (int x = 0; x < W; ++x) st.v[j][r][x] = key < n_keys ? ldg<u32x4_t>(p + 16 * x) : u32x4_t{0, 0, 0, 0};
+        for (int x = 0; x < W; ++x) st.v[j][r][x] = live ? ldg<u32x4_t>(vbase + off + 16 * x) : u32x4_t{0, 0, 0, 0};
       }
     }
   }
@@ -128,7 +157,7 @@ struct EncSrc {
   }
 
   __device__ __forceinline__ void store(const Stage &st, char *stage, int tid) const {
-    asm volatile("" : "+v"(tid));  // recompute the per-thread addresses here instead of keeping them live
+    asm volatile("" : "+v"(tid));
 #pragma unroll
     for (int j = 0; j < UK; ++j) {
       const int u = tid + j * G::THREADS;
@@ -140,29 +169,19 @@ struct EncSrc {
     for (int j = 0; j < UV; ++j) {
       const int u = tid + j * G::THREADS;
       const int sp = u / VU, w = u % VU;
-      const int p2 = (w % 8) + 8 * ((w / 64) % (G::BN / 16));
-      const int c8 = ((w / 8) % 8) + 8 * (w / (64 * (G::BN / 16)));
-      const u32x4_t a = to_bf16(st.v[j][0]), b = to_bf16(st.v[j][1]);
-      const int pos = G::vpos(2 * p2);
-      char *vt = stage + sp * G::SPLIT_BYTES + G::KT;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lo = (i & 1) ? (a[i >> 1] >> 16) : (a[i >> 1] & 0xffffu);
-        const uint32_t hi = (i & 1) ? (b[i >> 1] & 0xffff0000u) : (b[i >> 1] << 16);
-        const int d = 8 * c8 + i;
-        *reinterpret_cast<uint32_t *>(vt + G::v_off(d, pos >> 3) + (pos & 7) * 2) = lo | hi;
-      }
+      store_vt_pairs<G>(stage + sp * G::SPLIT_BYTES + G::KT, G::v_pair(w), G::v_chunk(w), to_bf16(st.v[j][0]),
+                        to_bf16(st.v[j][1]));
     }
   }
 };
 
-// Paged FP8 K/V: cache [num_blocks, Hkv, bs, D] e4m3fn; the K tile of 16 fp8
-// per unit, V 2 keys x 8 fp8 per unit.  Converted to bf16 exactly on store.
+// Paged FP8 K/V: cache [num_blocks, Hkv, bs, D] e4m3fn; a K unit is 16 fp8 of
+// one key, a V unit 2 keys x 8 fp8.  Converted to bf16 exactly on store.
 template <class G>
 struct PagedSrc {
   const uint8_t *kc, *vc;
   const int32_t *bt;
-  int64_t head_off;  // kvh * bs * D
+  int64_t head_off;    // kvh * bs * D
   int64_t blk_stride;  // Hkv * bs * D
   int bs, n_keys;
   static constexpr int KU = G::BN * (G::D / 16);
@@ -177,30 +196,30 @@ struct PagedSrc {
   };
 
   __device__ __forceinline__ void load(Stage &st, int it, int tid) const {
-    asm volatile("" : "+v"(tid));  // recompute the per-thread offsets here instead of keeping them live
+    asm volatile("" : "+v"(tid));
     const int key0 = it * G::BN;
+    // the tile lies inside one cache block (bs % BN == 0): one table lookup
     const int64_t base = (int64_t)bt[key0 / bs] * blk_stride + head_off + (int64_t)(key0 % bs) * G::D;
+    const uint8_t *kbase = kc + base, *vbase = vc + base;
 #pragma unroll
     for (int j = 0; j < UK; ++j) {
       const int u = tid + j * G::THREADS;
       const int t = u / (G::D / 16), c = u % (G::D / 16);
-      st.k[j] = key0 + t < n_keys ? ldg<u32x4_t>(kc + base + t * G::D + 16 * c) : u32x4_t{0, 0, 0, 0};
+      st.k[j] = key0 + t < n_keys ? ldg<u32x4_t>(kbase + (uint32_t)(t * G::D + 16 * c)) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < UV; ++j) {
       const int w = tid + j * G::THREADS;
-      const int p2 = (w % 8) + 8 * ((w / 64) % (G::BN / 16));
-      const int c8 = ((w / 8) % 8) + 8 * (w / (64 * (G::BN / 16)));
+      const int t0 = 2 * G::v_pair(w), c8 = G::v_chunk(w);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int t = 2 * p2 + r;
-        st.v[j][r] = key0 + t < n_keys ? ldg<u32x2_t>(vc + base + t * G::D + 8 * c8) : u32x2_t{0, 0};
-      }
+      for (int r = 0; r < 2; ++r)
+        st.v[j][r] = key0 + t0 + r < n_keys ? ldg<u32x2_t>(vbase + (uint32_t)((t0 + r) * G::D + 8 * c8))
+                                            : u32x2_t{0, 0};
     }
   }
 
   __device__ __forceinline__ void store(const Stage &st, char *stage, int tid) const {
-    asm volatile("" : "+v"(tid));  // recompute the per-thread addresses here instead of keeping them live
+    asm volatile("" : "+v"(tid));
 #pragma unroll
     for (int j = 0; j < UK; ++j) {
       const int u = tid + j * G::THREADS;
@@ -216,21 +235,12 @@ struct PagedSrc {
 #pragma unroll
     for (int j = 0; j < UV; ++j) {
       const int w = tid + j * G::THREADS;
-      const int p2 = (w % 8) + 8 * ((w / 64) % (G::BN / 16));
-      const int c8 = ((w / 8) % 8) + 8 * (w / (64 * (G::BN / 16)));
       const u32x2_t xa = st.v[j][0], xb = st.v[j][1];
-      const uint32_t a[4] = {e4m3x2_to_bf16x2<false>(xa[0]), e4m3x2_to_bf16x2<true>(xa[0]),
-                             e4m3x2_to_bf16x2<false>(xa[1]), e4m3x2_to_bf16x2<true>(xa[1])};
-      const uint32_t b[4] = {e4m3x2_to_bf16x2<false>(xb[0]), e4m3x2_to_bf16x2<true>(xb[0]),
-                             e4m3x2_to_bf16x2<false>(xb[1]), e4m3x2_to_bf16x2<true>(xb[1])};
-      const int pos = G::vpos(2 * p2);
-      char *vt = stage + G::KT;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lo = (i & 1) ? (a[i >> 1] >> 16) : (a[i >> 1] & 0xffffu);
-        const uint32_t hi = (i & 1) ? (b[i >> 1] & 0xffff0000u) : (b[i >> 1] << 16);
-        *reinterpret_cast<uint32_t *>(vt + G::v_off(8 * c8 + i, pos >> 3) + (pos & 7) * 2) = lo | hi;
-      }
+      const u32x4_t a = {e4m3x2_to_bf16x2<false>(xa[0]), e4m3x2_to_bf16x2<true>(xa[0]),
+                         e4m3x2_to_bf16x2<false>(xa[1]), e4m3x2_to_bf16x2<true>(xa[1])};
+      const u32x4_t b = {e4m3x2_to_bf16x2<false>(xb[0]), e4m3x2_to_bf16x2<true>(xb[0]),
+                         e4m3x2_to_bf16x2<false>(xb[1]), e4m3x2_to_bf16x2<true>(xb[1])};
+      store_vt_pairs<G>(stage + G::KT, G::v_pair(w), G::v_chunk(w), a, b);
     }
   }
 };
@@ -240,15 +250,27 @@ struct PagedSrc {
 template <class G>
 struct WaveState {
   f32x16_t o[G::NT][G::MT];
-  float m[G::NT], l[G::NT];
+  float m[G::NT], l[G::NT];  // m: running reference max, log2 units
 };
 
-// One key tile for one wave.  `mask` (nullable) is the additive key mask of
-// this batch row in natural-log units.
-template <class G>
+// max / sum of a value with its partner lane (lane ^ 32) in one VALU op
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One key tile for one wave.  c = softmax_scale*log2(e) > 0.  `mask` (only
+// read when HAS_MASK) is the additive key mask of this batch row, natural-log
+// units; keys >= n_keys are removed.
+template <class G, bool HAS_MASK>
 __device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&qf)[G::NT][G::SD],
                                              const char *kt, const char *vt, int key0, int n_keys,
                                              float c, const float *mask, int lane) {
+  asm volatile("" : "+v"(lane));  // lane-derived LDS offsets are recomputed per tile, not kept live
   const int l32 = lane & 31, h = lane >> 5;
   f32x16_t s[G::NT][G::KB];
 #pragma unroll
@@ -291,7 +313,36 @@ __device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&q
     }
   }
 
-  const bool tail = key0 + G::BN > n_keys;
+  // Scores into log2 units.  Without a mask the row max is taken on the raw
+  // scores and the scale is folded into the exp2 argument (one FMA per score);
+  // with a mask the scaled, masked score is formed first.
+  if constexpr (HAS_MASK) {
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int key = key0 + kb * 32 + r4 * 8 + 4 * h;
+        float mk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mk[i] = key + i < n_keys ? mask[key + i] * kLog2e : -INFINITY;
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)  // removed keys stay -inf whatever their K holds
+            s[nt][kb][4 * r4 + i] = mk[i] == -INFINITY ? -INFINITY : __builtin_fmaf(s[nt][kb][4 * r4 + i], c, mk[i]);
+      }
+  } else if (key0 + G::BN > n_keys) {  // ragged last tile (uniform branch)
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = key0 + kb * 32 + (v >> 2) * 8 + 4 * h + (v & 3);
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt)
+          if (key >= n_keys) s[nt][kb][v] = -INFINITY;
+      }
+  }
+
   float mx[G::NT];
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
@@ -299,15 +350,9 @@ __device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&q
 #pragma unroll
     for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = key0 + kb * 32 + (v >> 2) * 8 + 4 * h + (v & 3);
-        float x = s[nt][kb][v] * c;
-        if (mask) x += (key < n_keys ? mask[key] : 0.0f) * kLog2e;
-        if (tail && key >= n_keys) x = -INFINITY;
-        s[nt][kb][v] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    mx[nt] = fmaxf(mloc, xor32(mloc));
+      for (int v = 0; v < 16; v += 2) mloc = __builtin_fmaxf(mloc, __builtin_fmaxf(s[nt][kb][v], s[nt][kb][v + 1]));
+    mloc = pair_max(mloc);
+    mx[nt] = HAS_MASK ? mloc : mloc * c;  // -inf * c = -inf (c > 0)
   }
 
   // Lazy rescale: the reference max m of a row only moves when the tile max
@@ -329,27 +374,31 @@ __device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&q
     }
   }
 
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
   u32x4_t pb[G::NT][G::KB][2];
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
     const float m_use = ws.m[nt] == -INFINITY ? 0.0f : ws.m[nt];
-    float lsum = 0.0f;
+    float lsum = ws.l[nt];
 #pragma unroll
     for (int kb = 0; kb < G::KB; ++kb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(s[nt][kb][v] - m_use);
-        s[nt][kb][v] = p;
-        lsum += p;
-      }
+      for (int v = 0; v < 16; ++v)
+        s[nt][kb][v] = HAS_MASK ? fast_exp2(s[nt][kb][v] - m_use) : fast_exp2(__builtin_fmaf(s[nt][kb][v], c, -m_use));
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        pb[nt][kb][kk] = u32x4_t{pack_bf16(s[nt][kb][8 * kk + 0], s[nt][kb][8 * kk + 1]),
-                                 pack_bf16(s[nt][kb][8 * kk + 2], s[nt][kb][8 * kk + 3]),
-                                 pack_bf16(s[nt][kb][8 * kk + 4], s[nt][kb][8 * kk + 5]),
-                                 pack_bf16(s[nt][kb][8 * kk + 6], s[nt][kb][8 * kk + 7])};
+      for (int kk = 0; kk < 2; ++kk) {
+        // bit-cast plain scalars, never ext-vector elements: hipcc folded a
+        // bit_cast of pb[..][i] to element 0 for every i
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w[i] = pack_bf16(s[nt][kb][8 * kk + 2 * i], s[nt][kb][8 * kk + 2 * i + 1]);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), ones, lsum, false);
+        }
+        pb[nt][kb][kk] = u32x4_t{w[0], w[1], w[2], w[3]};
+      }
     }
-    ws.l[nt] += lsum;
+    ws.l[nt] = lsum;
   }
 
   // PV: fragments f = (kb*2 + kk)*MT + mt of V^T, same group pipelining.
@@ -388,15 +437,21 @@ __device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&q
   }
 }
 
-// The pipelined key loop shared by both kernels.  Returns with every wave's
-// state complete and the LDS free (a barrier has been passed).
-template <class G, class Src>
+// The pipelined key loop shared by both kernels.  PF register stages keep
+// the global loads of the next PF tiles in flight while a tile is computed
+// from one LDS stage and the next is written to the other.  The iteration
+// count is padded to a multiple of PF (padding tiles are all-masked zeros),
+// so the body unrolls over the register stages with static indices and the
+// accumulators never meet a branch.  Returns with the LDS free (barrier
+// passed).
+template <class G, bool HAS_MASK, class Src>
 __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, const u32x4_t (&qf)[G::NT][G::SD],
                                            char *smem, float c, const float *mask) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sp = wave / G::RG;
   const int n_tiles = (src.n_keys + G::BN - 1) / G::BN;
   const int n_iter = (n_tiles + G::NSPLIT - 1) / G::NSPLIT;
+  const int n_pad = (n_iter + G::PF - 1) / G::PF * G::PF;
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
     ws.m[nt] = -INFINITY;
@@ -406,21 +461,25 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
   }
   if (n_iter <= 0) return;
 
-  typename Src::Stage st;
-  src.load(st, 0, tid);
-  src.store(st, smem, tid);
+  typename Src::Stage st[G::PF];
+#pragma unroll
+  for (int u = 0; u < G::PF; ++u) src.load(st[u], u, tid);
+  src.store(st[0], smem, tid);
   __syncthreads();
-  for (int it = 0; it < n_iter; ++it) {
-    const bool more = it + 1 < n_iter;
-    if (more) src.load(st, it + 1, tid);
-    // A split whose tile index runs past the last tile computes on an
-    // all-zero, fully masked tile (p = 0): no branch, so the accumulators
-    // never meet a control-flow merge.
-    const int ti = it * G::NSPLIT + sp;
-    const char *base = smem + (it & 1) * G::STAGE + sp * G::SPLIT_BYTES;
-    compute_tile<G>(ws, qf, base, base + G::KT, ti * G::BN, src.n_keys, c, mask, lane);
-    if (more) src.store(st, smem + ((it + 1) & 1) * G::STAGE, tid);
-    __syncthreads();
+  for (int it0 = 0; it0 < n_pad; it0 += G::PF) {
+#pragma unroll
+    for (int u = 0; u < G::PF; ++u) {
+      const int it = it0 + u;
+      // register stage u held tile `it`, already written to LDS: refill it
+      if (it + G::PF < n_pad) src.load(st[u], it + G::PF, tid);
+      // A split whose tile index runs past the last tile computes on an
+      // all-zero, fully masked tile (p = 0).
+      const int ti = it * G::NSPLIT + sp;
+      const char *base = smem + (it & 1) * G::STAGE + sp * G::SPLIT_BYTES;
+      compute_tile<G, HAS_MASK>(ws, qf, base, base + G::KT, ti * G::BN, src.n_keys, c, mask, lane);
+      if (it + 1 < n_pad) src.store(st[(u + 1) % G::PF], smem + ((it + 1) & 1) * G::STAGE, tid);
+      __syncthreads();
+    }
   }
 }
 
@@ -478,9 +537,15 @@ __device__ __forceinline__ int xcd_remap(int lin, int total) {
   return (lin % 8) * (total / 8) + lin / 8;
 }
 
+// A negative softmax scale is applied as a positive one on -q (exact), so the
+// kernels only ever see c > 0.
+__device__ __forceinline__ u32x4_t neg_bf16x8(u32x4_t x, uint32_t sign) {
+  return u32x4_t{x[0] ^ sign, x[1] ^ sign, x[2] ^ sign, x[3] ^ sign};
+}
+
 // ------------------------------------------------------------------ encoder kernel
 
-template <class G, bool F32IN>
+template <class G, bool F32IN, bool HAS_MASK>
 __global__ __launch_bounds__(G::THREADS) void encoder_fwd_kernel(EncoderLaunch a) {
   __shared__ __attribute__((aligned(16))) char smem[G::LDS];
   const int n_qt = (a.Sq + G::BM - 1) / G::BM;
@@ -491,6 +556,7 @@ __global__ __launch_bounds__(G::THREADS) void encoder_fwd_kernel(EncoderLaunch a
   const int rg = wave % G::RG, sp = wave / G::RG;
   const int l32 = lane & 31, hh = lane >> 5;
   constexpr int ES = F32IN ? 4 : 2;
+  const uint32_t qsign = a.q_neg ? 0x80008000u : 0u;
 
   // Q fragments (B operand of S^T = K Q^T): row = lane%32, 8 d per lane-half
   u32x4_t qf[G::NT][G::SD];
@@ -501,19 +567,19 @@ __global__ __launch_bounds__(G::THREADS) void encoder_fwd_kernel(EncoderLaunch a
 #pragma unroll
     for (int sd = 0; sd < G::SD; ++sd) {
       const char *p = qb + (row * a.qs[2] + 16 * sd + 8 * hh) * ES;
+      u32x4_t x = {0, 0, 0, 0};
       if (row < a.Sq) {
         if constexpr (F32IN) {
           const u32x4_t x0 = ldg<u32x4_t>(p), x1 = ldg<u32x4_t>(p + 16);
-          qf[nt][sd] = u32x4_t{pack_bf16(__uint_as_float(x0[0]), __uint_as_float(x0[1])),
-                               pack_bf16(__uint_as_float(x0[2]), __uint_as_float(x0[3])),
-                               pack_bf16(__uint_as_float(x1[0]), __uint_as_float(x1[1])),
-                               pack_bf16(__uint_as_float(x1[2]), __uint_as_float(x1[3]))};
+          x = u32x4_t{pack_bf16(__uint_as_float(x0[0]), __uint_as_float(x0[1])),
+                      pack_bf16(__uint_as_float(x0[2]), __uint_as_float(x0[3])),
+                      pack_bf16(__uint_as_float(x1[0]), __uint_as_float(x1[1])),
+                      pack_bf16(__uint_as_float(x1[2]), __uint_as_float(x1[3]))};
         } else {
-          qf[nt][sd] = ldg<u32x4_t>(p);
+          x = ldg<u32x4_t>(p);
         }
-      } else {
-        qf[nt][sd] = u32x4_t{0, 0, 0, 0};
       }
+      qf[nt][sd] = neg_bf16x8(x, qsign);
     }
   }
 
@@ -522,11 +588,14 @@ __global__ __launch_bounds__(G::THREADS) void encoder_fwd_kernel(EncoderLaunch a
   src.vb = reinterpret_cast<const char *>(a.v) + (b * a.vs[0] + h * a.vs[1]) * ES;
   src.ks = a.ks[2];
   src.vs = a.vs[2];
+  src.kstep = (int64_t)G::NSPLIT * G::BN * a.ks[2] * ES;
+  src.vstep = (int64_t)G::NSPLIT * G::BN * a.vs[2] * ES;
   src.n_keys = a.Skv;
-  const float *mask = a.mask ? a.mask + b * a.mask_sb : nullptr;
+  const float *mask = HAS_MASK ? a.mask + b * a.mask_sb : nullptr;
+  src.mask = mask;
 
   WaveState<G> ws;
-  flash_loop<G>(ws, src, qf, smem, a.c, mask);
+  flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c, mask);
   merge_splits<G>(ws, smem);
   if (sp != 0) return;
 
@@ -534,7 +603,7 @@ __global__ __launch_bounds__(G::THREADS) void encoder_fwd_kernel(EncoderLaunch a
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
     const int row = qt * G::BM + (rg * G::NT + nt) * 32 + l32;
-    const float lt = ws.l[nt] + xor32(ws.l[nt]);
+    const float lt = pair_sum(ws.l[nt]);
     if (row >= a.Sq) continue;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     if (a.lse && hh == 0)
@@ -567,8 +636,7 @@ __global__ __launch_bounds__(G::THREADS) void encoder_fwd_kernel(EncoderLaunch a
 // ------------------------------------------------------------------ prefill kernel
 
 template <class G>
-__global__ __launch_bounds__(G::THREADS)
-void prefill_paged_kernel(PrefillLaunch a) {
+__global__ __launch_bounds__(G::THREADS) void prefill_paged_kernel(PrefillLaunch a) {
   __shared__ __attribute__((aligned(16))) char smem[G::LDS];
   const int rows = a.G * a.Lq;  // packed (head, token) rows per KV head
   const int n_rt = (rows + G::BM - 1) / G::BM;
@@ -578,6 +646,7 @@ void prefill_paged_kernel(PrefillLaunch a) {
   const int rg = wave % G::RG;
   const int l32 = lane & 31, hh = lane >> 5;
   const int64_t row_base = (int64_t)kvh * rows;  // first packed row of this KV head in [Hq*Lq]
+  const uint32_t qsign = a.q_neg ? 0x80008000u : 0u;
 
   u32x4_t qf[G::NT][G::SD];
 #pragma unroll
@@ -585,7 +654,8 @@ void prefill_paged_kernel(PrefillLaunch a) {
     const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
 #pragma unroll
     for (int sd = 0; sd < G::SD; ++sd)
-      qf[nt][sd] = r < rows ? ldg<u32x4_t>(a.q + (row_base + r) * G::D + 16 * sd + 8 * hh) : u32x4_t{0, 0, 0, 0};
+      qf[nt][sd] = neg_bf16x8(
+          r < rows ? ldg<u32x4_t>(a.q + (row_base + r) * G::D + 16 * sd + 8 * hh) : u32x4_t{0, 0, 0, 0}, qsign);
   }
 
   PagedSrc<G> src;
@@ -598,12 +668,12 @@ void prefill_paged_kernel(PrefillLaunch a) {
   src.n_keys = a.L_act;
 
   WaveState<G> ws;
-  flash_loop<G>(ws, src, qf, smem, a.c, nullptr);
+  flash_loop<G, false>(ws, src, qf, smem, a.c, nullptr);
 
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
     const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
-    const float lt = ws.l[nt] + xor32(ws.l[nt]);
+    const float lt = pair_sum(ws.l[nt]);
     if (r >= rows) continue;
     const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
     if (a.lse && hh == 0) a.lse[row_base + r] = lt > 0.0f ? (ws.m[nt] + __log2f(lt)) * kLn2 : -INFINITY;
@@ -621,16 +691,25 @@ void prefill_paged_kernel(PrefillLaunch a) {
 
 // ------------------------------------------------------------------ launchers
 
-using EncGeo = Geo<64, 64, 1, 4, 2, 4>;     // BM 128, 8 waves, 2 key splits
-using PrefGeo = Geo<256, 32, 1, 8, 1, 1>;   // BM 256, 8 waves of 32 rows, 2 waves per SIMD
+using EncGeo = Geo<64, 64, 1, 4, 2, 4, 2>;     // BM 128, 8 waves, 2 key splits, 2 tiles in flight
+using EncGeoF32 = Geo<64, 64, 1, 4, 2, 4, 1>;  // fp32 inputs: twice the staging registers per tile
+using PrefGeo = Geo<256, 32, 1, 8, 1, 1, 1>;   // BM 256, 8 waves of 32 rows, 2 waves per SIMD
 
 hipError_t launch_encoder(const EncoderLaunch &a, bool f32_in, hipStream_t stream) {
   const int n_qt = (a.Sq + EncGeo::BM - 1) / EncGeo::BM;
   const dim3 grid(n_qt * a.H * a.B), block(EncGeo::THREADS);
-  if (f32_in)
-    hipLaunchKernelGGL((encoder_fwd_kernel<EncGeo, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((encoder_fwd_kernel<EncGeo, false>), grid, block, 0, stream, a);
+  static_assert(EncGeo::BM == EncGeoF32::BM && EncGeo::THREADS == EncGeoF32::THREADS, "same launch shape");
+  if (f32_in) {
+    if (a.mask)
+      hipLaunchKernelGGL((encoder_fwd_kernel<EncGeoF32, true, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((encoder_fwd_kernel<EncGeoF32, true, false>), grid, block, 0, stream, a);
+  } else {
+    if (a.mask)
+      hipLaunchKernelGGL((encoder_fwd_kernel<EncGeo, false, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((encoder_fwd_kernel<EncGeo, false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

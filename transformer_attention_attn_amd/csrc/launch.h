@@ -13,7 +13,8 @@ struct EncoderLaunch {
   const float *mask;            // nullable, natural-log additive [B, S_kv] rows
   int64_t mask_sb;
   int B, H, Sq, Skv;
-  float c;                      // softmax_scale * log2(e)
+  float c;                      // |softmax_scale| * log2(e), > 0
+  int q_neg;                    // 1: the scale was negative, q is negated on load
   void *out;                    // nullable
   int64_t os[4];
   int out_f32;
@@ -27,7 +28,8 @@ struct PrefillLaunch {
   const uint8_t *kc, *vc;
   const int32_t *bt;
   int bs, L_act, Hkv, G, Lq;
-  float c;        // softmax_scale * k_scale * log2(e)
+  float c;        // |softmax_scale| * k_scale * log2(e), > 0
+  int q_neg;      // 1: the scale was negative, q is negated on load
   float v_scale;
   __bf16 *out;
   float *lse;     // nullable
