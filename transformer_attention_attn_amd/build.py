@@ -21,7 +21,7 @@ ARCH = "gfx950"
 
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Wno-unused-command-line-argument", "-fvisibility=hidden"]
+          "-Wno-unused-command-line-argument", "-fvisibility=hidden", "-fno-honor-nans"]
 
 
 def _compile(src: str) -> str:

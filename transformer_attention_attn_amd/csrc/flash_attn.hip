@@ -40,12 +40,13 @@ namespace mi355 {
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
-template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int PF_>
+template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int PF_, int OCC_ = 2>
 struct Geo {
   static constexpr int D = D_, BN = BN_, NT = NT_, RG = RG_, NSPLIT = NSPLIT_;
   static constexpr int GRP = GRP_;  // LDS fragments read per pipelined group
   static constexpr int PF = PF_;    // key tiles in flight in registers (global-load prefetch depth)
   static constexpr int WAVES = RG * NSPLIT, THREADS = 64 * WAVES;
+  static constexpr int WPE = OCC_;  // waves per SIMD the kernel is compiled for (register budget 512 / WPE)
   static constexpr int BM = 32 * NT * RG;
   static constexpr int KT = BN * D * 2;  // bytes of one bf16 K tile
   static constexpr int VT = D * BN * 2;  // bytes of one bf16 V^T tile
@@ -59,7 +60,7 @@ struct Geo {
   static constexpr int VCH = BN / 8;  // 16-byte chunks per V^T row
   static constexpr int VSW = VCH < 8 ? VCH : 8;
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
-  static_assert(LDS <= 65536, "LDS budget");
+  static_assert(LDS <= 160 * 1024, "LDS budget (gfx950: 160 KiB per workgroup)");
 
   // byte offset of 16-byte chunk c of key row `key` in a K tile
   static __device__ __forceinline__ int k_off(int key, int c) { return key * (D * 2) + ((c ^ (key & 7)) << 4); }
@@ -72,8 +73,8 @@ struct Geo {
   static __device__ __forceinline__ int vpos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
   // V unit w (2 keys x 8 d) -> key pair p2, d-chunk c8: 8 key pairs x 8 chunks
   // per wave, so that the transposed LDS writes of a wave spread over banks.
-  static __device__ __forceinline__ int v_pair(int w) { return (w % 8) + 8 * ((w / 64) % (BN / 16)); }
-  static __device__ __forceinline__ int v_chunk(int w) { return ((w / 8) % 8) + 8 * (w / (64 * (BN / 16))); }
+  static __device__ __forceinline__ unsigned v_pair(unsigned w) { return (w % 8) + 8 * ((w / 64) % (BN / 16)); }
+  static __device__ __forceinline__ unsigned v_chunk(unsigned w) { return ((w / 8) % 8) + 8 * (w / (64 * (BN / 16))); }
 };
 
 // Write the 8 (key 2p, key 2p+1) bf16 pairs of d-rows d0..d0+7 into a V^T tile.
@@ -113,7 +114,9 @@ struct EncSrc {
     u32x4_t v[UV][2][W];
   };
 
-  __device__ __forceinline__ void load(Stage &st, int it, int tid) const {
+  __device__ __forceinline__ int64_t tile_base(int) const { return 0; }
+
+  __device__ __forceinline__ void load(Stage &st, int it, int64_t, int tid) const {
     asm volatile("" : "+v"(tid));  // per-thread offsets are cheap 32-bit math: recompute, don't keep live
     const char *kbase = kb + it * kstep;
     const char *vbase = vb + it * vstep;
@@ -180,7 +183,7 @@ struct EncSrc {
 template <class G>
 struct PagedSrc {
   const uint8_t *kc, *vc;
-  const int32_t *bt;
+  const __attribute__((address_space(4))) int32_t *bt;  // constant address space: scalar loads
   int64_t head_off;    // kvh * bs * D
   int64_t blk_stride;  // Hkv * bs * D
   int bs, n_keys;
@@ -195,26 +198,34 @@ struct PagedSrc {
     u32x2_t v[UV][2];
   };
 
-  __device__ __forceinline__ void load(Stage &st, int it, int tid) const {
+  // Physical block of the tile `it` (uniform): a scalar load from the block
+  // table (read-only for the whole launch, so it may use the constant path).
+  __device__ __forceinline__ int64_t tile_base(int it) const {
+    const int last = (n_keys - 1) / G::BN;  // padding tiles reuse the last live block: always inside the table
+    const unsigned key0 = (unsigned)(it < last ? it : last) * G::BN;
+    const int32_t phys = bt[key0 / (unsigned)bs];
+    return (int64_t)phys * blk_stride + head_off + (int64_t)(key0 % (unsigned)bs) * G::D;
+  }
+
+  // `base` is tile_base(it), computed one tile ahead by the caller.
+  __device__ __forceinline__ void load(Stage &st, int it, int64_t base, unsigned tid) const {
     asm volatile("" : "+v"(tid));
-    const int key0 = it * G::BN;
-    // the tile lies inside one cache block (bs % BN == 0): one table lookup
-    const int64_t base = (int64_t)bt[key0 / bs] * blk_stride + head_off + (int64_t)(key0 % bs) * G::D;
+    const unsigned key0 = (unsigned)it * G::BN;
     const uint8_t *kbase = kc + base, *vbase = vc + base;
 #pragma unroll
     for (int j = 0; j < UK; ++j) {
-      const int u = tid + j * G::THREADS;
-      const int t = u / (G::D / 16), c = u % (G::D / 16);
-      st.k[j] = key0 + t < n_keys ? ldg<u32x4_t>(kbase + (uint32_t)(t * G::D + 16 * c)) : u32x4_t{0, 0, 0, 0};
+      const unsigned u = tid + j * G::THREADS;
+      const unsigned t = u / (G::D / 16), c = u % (G::D / 16);
+      st.k[j] = key0 + t < (unsigned)n_keys ? ldg<u32x4_t>(kbase + (t * G::D + 16 * c)) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < UV; ++j) {
-      const int w = tid + j * G::THREADS;
-      const int t0 = 2 * G::v_pair(w), c8 = G::v_chunk(w);
+      const unsigned w = tid + j * G::THREADS;
+      const unsigned t0 = 2 * G::v_pair(w), c8 = G::v_chunk(w);
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        st.v[j][r] = key0 + t0 + r < n_keys ? ldg<u32x2_t>(vbase + (uint32_t)((t0 + r) * G::D + 8 * c8))
-                                            : u32x2_t{0, 0};
+        st.v[j][r] = key0 + t0 + r < (unsigned)n_keys ? ldg<u32x2_t>(vbase + ((t0 + r) * G::D + 8 * c8))
+                                                       : u32x2_t{0, 0};
     }
   }
 
@@ -278,39 +289,37 @@ __device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&q
 #pragma unroll
     for (int kb = 0; kb < G::KB; ++kb) s[nt][kb] = f32x16_t{};
 
-  // QK^T: fragments f = sd*KB + kb, read from LDS GRP at a time one group
-  // ahead of the MFMAs that consume them (bounded register footprint).
+  // QK^T: fragment f = sd*KB + kb feeds NT MFMAs.  All fragments are
+  // written as loads up front; the scheduling groups below order them as
+  // RA reads ahead, then (MFMA x NT, next read) pairs, so RA LDS reads stay in
+  // flight behind the MFMAs while only RA+1 fragments are live.
   {
-    constexpr int NF = G::SD * G::KB, GRP = G::GRP, NG = NF / GRP;
-    static_assert(NF % GRP == 0, "QK fragment groups");
+    constexpr int NF = G::SD * G::KB, RA = G::GRP < NF ? G::GRP : NF;
     // K fragment (kb, sd): row kb*32 + l32, chunk 2*sd + h.  The XOR swizzle
     // only touches the low 3 chunk bits, so the address is one of 4 per-lane
     // bases plus a compile-time offset.
     int kbase[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kbase[j] = l32 * (G::D * 2) + (((2 * j + h) ^ (l32 & 7)) << 4);
-    auto kfrag = [&](int f) {
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4_t fb[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
       const int kb = f % G::KB, sd = f / G::KB;
-      return *reinterpret_cast<const u32x4_t *>(kt + kbase[sd & 3] + kb * 32 * G::D * 2 + (sd >> 2) * 128);
-    };
-    u32x4_t fb[2][GRP];
-#pragma unroll
-    for (int j = 0; j < GRP; ++j) fb[0][j] = kfrag(j);
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (g + 1 < NG) {
-#pragma unroll
-        for (int j = 0; j < GRP; ++j) fb[(g + 1) & 1][j] = kfrag((g + 1) * GRP + j);
-      }
-#pragma unroll
-      for (int j = 0; j < GRP; ++j) {
-        const int f = g * GRP + j;
-#pragma unroll
-        for (int nt = 0; nt < G::NT; ++nt)
-          s[nt][f % G::KB] = mfma32(as_bf16x8(fb[g & 1][j]), as_bf16x8(qf[nt][f / G::KB]), s[nt][f % G::KB]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      fb[f] = *reinterpret_cast<const u32x4_t *>(kt + kbase[sd & 3] + kb * 32 * G::D * 2 + (sd >> 2) * 128);
     }
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt)
+        s[nt][f % G::KB] = mfma32(as_bf16x8(fb[f]), as_bf16x8(qf[nt][f / G::KB]), s[nt][f % G::KB]);
+    __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, G::NT, 0);
+      if (f + RA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Scores into log2 units.  Without a mask the row max is taken on the raw
@@ -401,39 +410,34 @@ __device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&q
     ws.l[nt] = lsum;
   }
 
-  // PV: fragments f = (kb*2 + kk)*MT + mt of V^T, same group pipelining.
+  // PV: fragment f = (kb*2 + kk)*MT + mt of V^T, same read-ahead ordering.
   {
-    constexpr int NF = G::KB * 2 * G::MT, GRP = G::GRP, NG = NF / GRP;
-    static_assert(NF % GRP == 0, "PV fragment groups");
+    constexpr int NF = G::KB * 2 * G::MT, RA = G::GRP < NF ? G::GRP : NF;
     // V^T fragment (mt, kb, kk): row mt*32 + l32, chunk kb*4 + kk*2 + h; the
     // swizzle depends on the lane only, so KB*2 per-lane bases + offsets.
     const int vsw = (l32 / G::VROWS) % G::VSW;
     int vbase[G::KB * 2];
 #pragma unroll
     for (int j = 0; j < G::KB * 2; ++j) vbase[j] = l32 * (G::BN * 2) + (((2 * j + h) ^ vsw) << 4);
-    auto vfrag = [&](int f) {
-      const int mt = f % G::MT, j = f / G::MT;
-      return *reinterpret_cast<const u32x4_t *>(vt + vbase[j] + mt * 32 * G::BN * 2);
-    };
-    u32x4_t fb[2][GRP];
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4_t fb[NF];
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) fb[0][j] = vfrag(j);
+    for (int f = 0; f < NF; ++f)
+      fb[f] = *reinterpret_cast<const u32x4_t *>(vt + vbase[f / G::MT] + (f % G::MT) * 32 * G::BN * 2);
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (g + 1 < NG) {
+    for (int f = 0; f < NF; ++f) {
+      const int mt = f % G::MT, kk = (f / G::MT) % 2, kb = f / (2 * G::MT);
 #pragma unroll
-        for (int j = 0; j < GRP; ++j) fb[(g + 1) & 1][j] = vfrag((g + 1) * GRP + j);
-      }
-#pragma unroll
-      for (int j = 0; j < GRP; ++j) {
-        const int f = g * GRP + j;
-        const int mt = f % G::MT, kk = (f / G::MT) % 2, kb = f / (2 * G::MT);
-#pragma unroll
-        for (int nt = 0; nt < G::NT; ++nt)
-          ws.o[nt][mt] = mfma32(as_bf16x8(fb[g & 1][j]), as_bf16x8(pb[nt][kb][kk]), ws.o[nt][mt]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int nt = 0; nt < G::NT; ++nt)
+        ws.o[nt][mt] = mfma32(as_bf16x8(fb[f]), as_bf16x8(pb[nt][kb][kk]), ws.o[nt][mt]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, G::NT, 0);
+      if (f + RA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -463,7 +467,8 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
 
   typename Src::Stage st[G::PF];
 #pragma unroll
-  for (int u = 0; u < G::PF; ++u) src.load(st[u], u, tid);
+  for (int u = 0; u < G::PF; ++u) src.load(st[u], u, src.tile_base(u), tid);
+  int64_t next_base = src.tile_base(G::PF);  // address base of the next tile to load, looked up one tile early
   src.store(st[0], smem, tid);
   __syncthreads();
   for (int it0 = 0; it0 < n_pad; it0 += G::PF) {
@@ -471,7 +476,10 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
     for (int u = 0; u < G::PF; ++u) {
       const int it = it0 + u;
       // register stage u held tile `it`, already written to LDS: refill it
-      if (it + G::PF < n_pad) src.load(st[u], it + G::PF, tid);
+      if (it + G::PF < n_pad) {
+        src.load(st[u], it + G::PF, next_base, tid);
+        next_base = src.tile_base(it + G::PF + 1);
+      }
       // A split whose tile index runs past the last tile computes on an
       // all-zero, fully masked tile (p = 0).
       const int ti = it * G::NSPLIT + sp;
@@ -546,8 +554,9 @@ __device__ __forceinline__ u32x4_t neg_bf16x8(u32x4_t x, uint32_t sign) {
 // ------------------------------------------------------------------ encoder kernel
 
 template <class G, bool F32IN, bool HAS_MASK>
-__global__ __launch_bounds__(G::THREADS) void encoder_fwd_kernel(EncoderLaunch a) {
-  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
+__global__ __launch_bounds__(G::THREADS) __attribute__((amdgpu_waves_per_eu(G::WPE, G::WPE)))
+void encoder_fwd_kernel(EncoderLaunch a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // G::LDS bytes
   const int n_qt = (a.Sq + G::BM - 1) / G::BM;
   const int total = n_qt * a.H * a.B;
   const int lid = xcd_remap(blockIdx.x, total);
@@ -636,8 +645,9 @@ __global__ __launch_bounds__(G::THREADS) void encoder_fwd_kernel(EncoderLaunch a
 // ------------------------------------------------------------------ prefill kernel
 
 template <class G>
-__global__ __launch_bounds__(G::THREADS) void prefill_paged_kernel(PrefillLaunch a) {
-  __shared__ __attribute__((aligned(16))) char smem[G::LDS];
+__global__ __launch_bounds__(G::THREADS) __attribute__((amdgpu_waves_per_eu(G::WPE, G::WPE)))
+void prefill_paged_kernel(PrefillLaunch a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // G::LDS bytes
   const int rows = a.G * a.Lq;  // packed (head, token) rows per KV head
   const int n_rt = (rows + G::BM - 1) / G::BM;
   const int lid = xcd_remap(blockIdx.x, n_rt * a.Hkv);
@@ -661,7 +671,7 @@ __global__ __launch_bounds__(G::THREADS) void prefill_paged_kernel(PrefillLaunch
   PagedSrc<G> src;
   src.kc = a.kc;
   src.vc = a.vc;
-  src.bt = a.bt;
+  src.bt = (const __attribute__((address_space(4))) int32_t *)(a.bt);
   src.head_off = (int64_t)kvh * a.bs * G::D;
   src.blk_stride = (int64_t)a.Hkv * a.bs * G::D;
   src.bs = a.bs;
@@ -693,24 +703,30 @@ __global__ __launch_bounds__(G::THREADS) void prefill_paged_kernel(PrefillLaunch
 
 using EncGeo = Geo<64, 64, 1, 4, 2, 4, 2>;     // BM 128, 8 waves, 2 key splits, 2 tiles in flight
 using EncGeoF32 = Geo<64, 64, 1, 4, 2, 4, 1>;  // fp32 inputs: twice the staging registers per tile
-using PrefGeo = Geo<256, 32, 1, 8, 1, 1, 1>;   // BM 256, 8 waves of 32 rows, 2 waves per SIMD
+using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 1>;   // BM 256, 8 waves of 32 rows, 2 waves per SIMD
+
+// Launch with G::LDS bytes of dynamic LDS; kernels above 64 KiB are opted in
+// once per process (hipFuncSetAttribute is per function, not per device).
+template <class G, class K, class A>
+hipError_t launch_lds(K kernel, dim3 grid, const A &a, hipStream_t stream) {
+  if constexpr (G::LDS > 65536) {
+    static const hipError_t opt =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+    if (opt != hipSuccess) return opt;
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(G::THREADS), G::LDS, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_encoder(const EncoderLaunch &a, bool f32_in, hipStream_t stream) {
   const int n_qt = (a.Sq + EncGeo::BM - 1) / EncGeo::BM;
-  const dim3 grid(n_qt * a.H * a.B), block(EncGeo::THREADS);
+  const dim3 grid(n_qt * a.H * a.B);
   static_assert(EncGeo::BM == EncGeoF32::BM && EncGeo::THREADS == EncGeoF32::THREADS, "same launch shape");
-  if (f32_in) {
-    if (a.mask)
-      hipLaunchKernelGGL((encoder_fwd_kernel<EncGeoF32, true, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((encoder_fwd_kernel<EncGeoF32, true, false>), grid, block, 0, stream, a);
-  } else {
-    if (a.mask)
-      hipLaunchKernelGGL((encoder_fwd_kernel<EncGeo, false, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((encoder_fwd_kernel<EncGeo, false, false>), grid, block, 0, stream, a);
-  }
-  return hipGetLastError();
+  if (f32_in)
+    return a.mask ? launch_lds<EncGeoF32>(encoder_fwd_kernel<EncGeoF32, true, true>, grid, a, stream)
+                  : launch_lds<EncGeoF32>(encoder_fwd_kernel<EncGeoF32, true, false>, grid, a, stream);
+  return a.mask ? launch_lds<EncGeo>(encoder_fwd_kernel<EncGeo, false, true>, grid, a, stream)
+                : launch_lds<EncGeo>(encoder_fwd_kernel<EncGeo, false, false>, grid, a, stream);
 }
 
 int encoder_rows_per_block() { return EncGeo::BM; }
@@ -718,9 +734,7 @@ int encoder_rows_per_block() { return EncGeo::BM; }
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream) {
   const int rows = a.G * a.Lq;
   const int n_rt = (rows + PrefGeo::BM - 1) / PrefGeo::BM;
-  const dim3 grid(n_rt * a.Hkv), block(PrefGeo::THREADS);
-  hipLaunchKernelGGL((prefill_paged_kernel<PrefGeo>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  return launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo>, dim3(n_rt * a.Hkv), a, stream);
 }
 
 int prefill_key_tile() { return PrefGeo::BN; }
