@@ -36,8 +36,39 @@ import workloads as W  # noqa: E402
 from workloads import accounting as acc  # noqa: E402
 
 
+COPY_BYTES = 1 << 30
+
+
 def _log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: measured HBM traffic is only reported for the
+    exact kernels it was counted on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "transformer_attention_attn_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json (rocprofv3
+    FETCH_SIZE + WRITE_SIZE scaled by a plain copy), or None when the file is
+    missing or was measured on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        t = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
 
 
 class Timer:
@@ -86,7 +117,18 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4, help="query tokens in the CPU-baseline sample (0: skip)")
     ap.add_argument("--only", choices=["all", "encoder", "decode", "prefill"], default="all",
                     help="run a single kernel family (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 4 times (scales the rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 4}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -190,7 +232,8 @@ def main():
     if run_pre:
         p = parts["prefill"]
         roofline = {"bound": "mfma", "achieved": p["tflops"], "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": p["tflops"] / acc.PEAK_BF16_TFLOPS, "traffic": None, "kernel": "prefill_paged_kernel"}
+                    "frac": p["tflops"] / acc.PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill_paged_kernel"),
+                    "kernel": "prefill_paged_kernel", "kernel_source_hash": kernel_source_hash()}
     elif run_enc:
         p = parts["encoder_block"]
         roofline = {"bound": "mfma", "achieved": p["tflops"], "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
