@@ -121,6 +121,7 @@ def test_decode_workspace_size(lib):
     (dict(ws=FAKE, wsb=100), taa.ATTN_ERR_WORKSPACE),          # too small
     (dict(ws=FAKE + 16, wsb=1 << 30), taa.ATTN_ERR_INVALID_ARG),  # misaligned workspace
     (dict(scale=float("inf")), taa.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), taa.ATTN_ERR_INVALID_ARG),
 ])
 def test_decode_validation(lib, kw, expect):
     assert lib.attn_decode_gqa(*_dec(**kw)) == expect
@@ -142,6 +143,8 @@ def _pre(**kw):
     (dict(D=128), taa.ATTN_ERR_UNSUPPORTED),
     (dict(bs=100, L=1000), taa.ATTN_ERR_UNSUPPORTED),
     (dict(ks=0.0), taa.ATTN_ERR_INVALID_ARG),
+    (dict(ks=float("nan")), taa.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), taa.ATTN_ERR_INVALID_ARG),
     (dict(out=BAD), taa.ATTN_ERR_INVALID_ARG),
 ])
 def test_prefill_validation(lib, kw, expect):
@@ -154,6 +157,7 @@ def test_prefill_validation(lib, kw, expect):
     ((FAKE, None, 0, None, None, 1e-6, 4, 16384, None, FAKE, 1, None, None, None), taa.ATTN_ERR_UNSUPPORTED),
     ((FAKE, None, 0, None, None, 1e-6, 4, 64, None, FAKE, 2, None, None, None), taa.ATTN_ERR_UNSUPPORTED),
     ((FAKE, None, 0, None, None, -1.0, 4, 64, None, FAKE, 1, None, None, None), taa.ATTN_ERR_INVALID_ARG),
+    ((FAKE, None, 0, None, None, float("nan"), 4, 64, None, FAKE, 1, None, None, None), taa.ATTN_ERR_INVALID_ARG),
     ((FAKE, None, 0, None, None, 1e-6, 4, 64, None, BAD, 1, None, None, None), taa.ATTN_ERR_INVALID_ARG),
 ])
 def test_res_ln_validation(lib, args, expect):

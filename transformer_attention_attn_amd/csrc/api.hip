@@ -12,6 +12,13 @@ namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// finite by bit pattern (exponent field not all ones), immune to fast-math folding
+bool finite(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  return (u & 0x7f800000u) != 0x7f800000u;
+}
+
 // Kernels take the exp2 scale c > 0: a negative scale becomes a positive one on
 // -q (exact), and a zero scale a positive one so small that every exponent
 // rounds to 2^0 exactly (|c * s| < 2^-40 for any finite bf16 score), which is
@@ -48,12 +55,12 @@ int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
   if (a->B <= 0 || a->H <= 0 || a->S_q <= 0 || a->S_kv <= 0 || a->D <= 0) return ATTN_ERR_INVALID_ARG;
   if (a->in_dtype != ATTN_BF16 && a->in_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (a->D != 64) return ATTN_ERR_UNSUPPORTED;
-  if (!(a->softmax_scale == a->softmax_scale) || isinf(a->softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!finite(a->softmax_scale)) return ATTN_ERR_INVALID_ARG;
   if (!a->out && !a->residual_out) return ATTN_ERR_INVALID_ARG;
   if ((a->residual == nullptr) != (a->residual_out == nullptr)) return ATTN_ERR_INVALID_ARG;
   if (a->ln_out && !a->residual_out) return ATTN_ERR_INVALID_ARG;
   if ((a->ln_mean || a->ln_rstd) && !a->ln_out) return ATTN_ERR_INVALID_ARG;
-  if (a->ln_out && !(a->eps >= 0.0f)) return ATTN_ERR_INVALID_ARG;
+  if (a->ln_out && !(finite(a->eps) && a->eps >= 0.0f)) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v)) return ATTN_ERR_INVALID_ARG;
   const int64_t *st[3] = {a->q_stride, a->k_stride, a->v_stride};
   for (int t = 0; t < 3; ++t) {
@@ -140,7 +147,7 @@ int attn_decode_gqa(const void *q, const void *k, const void *v, const float *at
   if (D != 256) return ATTN_ERR_UNSUPPORTED;
   if (num_kv_groups > decode_max_groups() || (num_kv_groups & (num_kv_groups - 1)))
     return ATTN_ERR_UNSUPPORTED;
-  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!finite(softmax_scale)) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
   if (attn_mask && !aligned16(attn_mask)) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn_decode_gqa_workspace_size(B, Hq, S_ctx, D);
@@ -182,8 +189,8 @@ int attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache, 
     return ATTN_ERR_INVALID_ARG;
   if (D != 256) return ATTN_ERR_UNSUPPORTED;
   if (block_size % 64 != 0 || block_size % prefill_key_tile() != 0) return ATTN_ERR_UNSUPPORTED;
-  if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || isinf(k_scale) || isinf(v_scale)) return ATTN_ERR_INVALID_ARG;
-  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!finite(k_scale) || !finite(v_scale) || !(k_scale > 0.0f) || !(v_scale > 0.0f)) return ATTN_ERR_INVALID_ARG;
+  if (!finite(softmax_scale)) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
   if (((int64_t)num_blocks * Hkv * block_size * D) > ((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)num_kv_groups * Lq > 0x7fffffffLL - 256) return ATTN_ERR_UNSUPPORTED;
@@ -214,7 +221,7 @@ int res_ln(const float *residual, const void *x, attn_dtype_t x_dtype, const flo
   if (hidden > res_ln_max_hidden()) return ATTN_ERR_UNSUPPORTED;
   if (x && x_dtype != ATTN_BF16 && x_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (y_dtype != ATTN_BF16 && y_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
-  if (!(eps >= 0.0f)) return ATTN_ERR_INVALID_ARG;
+  if (!finite(eps) || !(eps >= 0.0f)) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(residual) || !aligned16(y) || (x && !aligned16(x)) || (residual_out && !aligned16(residual_out)) ||
       (gamma && !aligned16(gamma)) || (beta && !aligned16(beta)))
     return ATTN_ERR_INVALID_ARG;
