@@ -38,6 +38,17 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 (gfx950): every lane names an 8-byte row of four 16-bit
+// elements; within each group of 16 lanes, lane 4m+c receives element c of
+// the rows named by lanes m, m+4, m+8 and m+12 (in that order).  `p` must
+// point into LDS.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const char *p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

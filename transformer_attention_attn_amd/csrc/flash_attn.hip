@@ -28,11 +28,14 @@
 //   rows on N): P never leaves registers; the row sum is taken on the packed
 //   bf16 P with v_dot2_f32_bf16, so it normalises exactly the values that were
 //   multiplied into V.
-// K tiles sit in LDS as [key][d] (16-byte chunks XOR-swizzled by key), V tiles
-// as V^T [d][key] with keys permuted so each lane's 8 keys of a PV step are
-// one contiguous 16-byte read.  Global loads for the next PF tiles stay in
-// flight in registers (uniform 64-bit base + 32-bit per-thread offset) while a
-// tile is computed from one LDS stage and the next is written to the other.
+// K tiles sit in LDS as [key][d] (16-byte chunks XOR-swizzled by key); V tiles
+// as [key][d] too, rows padded by 64 bytes, and the A operand of the PV MFMA
+// (d on M, keys on K) is read transposed with ds_read_b64_tr_b16: the padding
+// puts the four keys one read touches in four different 64-byte bank groups,
+// so both the plain 16-byte V writes and the transposing reads are
+// conflict-free.  Global loads for the next PF tiles stay in flight in
+// registers (uniform 64-bit base + 32-bit per-thread offset) while a tile is
+// computed from one LDS stage and the next is written to the other.
 #include "device_common.h"
 #include "launch.h"
 
@@ -49,45 +52,21 @@ struct Geo {
   static constexpr int WPE = OCC_;  // waves per SIMD the kernel is compiled for (register budget 512 / WPE)
   static constexpr int BM = 32 * NT * RG;
   static constexpr int KT = BN * D * 2;  // bytes of one bf16 K tile
-  static constexpr int VT = D * BN * 2;  // bytes of one bf16 V^T tile
+  static constexpr int VROW = D * 2 + 64;  // bytes per key row of a V tile (64-byte pad: an odd multiple of 64 mod 256)
+  static constexpr int VT = BN * VROW;   // bytes of one bf16 V tile
   static constexpr int SPLIT_BYTES = KT + VT;
   static constexpr int STAGE = NSPLIT * SPLIT_BYTES;
   static constexpr int LDS = 2 * STAGE;
   static constexpr int KB = BN / 32;  // 32-key blocks per tile
   static constexpr int SD = D / 16;   // k-steps of the QK^T contraction
   static constexpr int MT = D / 32;   // d tiles of O^T
-  static constexpr int VROWS = (BN * 2 >= 128) ? 1 : 128 / (BN * 2);
-  static constexpr int VCH = BN / 8;  // 16-byte chunks per V^T row
-  static constexpr int VSW = VCH < 8 ? VCH : 8;
   static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
   static_assert(LDS <= 160 * 1024, "LDS budget (gfx950: 160 KiB per workgroup)");
+  static_assert((VROW / 64) % 2 == 1 && VROW % 256 != 0, "V row pad");
 
   // byte offset of 16-byte chunk c of key row `key` in a K tile
   static __device__ __forceinline__ int k_off(int key, int c) { return key * (D * 2) + ((c ^ (key & 7)) << 4); }
-  // byte offset of 16-byte chunk c of d-row `d` in a V^T tile
-  static __device__ __forceinline__ int v_off(int d, int c) {
-    return d * (BN * 2) + ((c ^ ((d / VROWS) % VSW)) << 4);
-  }
-  // storage position of key t of a tile: swap bits 2 and 3 so that the 8 keys
-  // lane-half h feeds to PV step kk of block kb are positions kb*32+16kk+8h+0..7
-  static __device__ __forceinline__ int vpos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
-  // V unit w (2 keys x 8 d) -> key pair p2, d-chunk c8: 8 key pairs x 8 chunks
-  // per wave, so that the transposed LDS writes of a wave spread over banks.
-  static __device__ __forceinline__ unsigned v_pair(unsigned w) { return (w % 8) + 8 * ((w / 64) % (BN / 16)); }
-  static __device__ __forceinline__ unsigned v_chunk(unsigned w) { return ((w / 8) % 8) + 8 * (w / (64 * (BN / 16))); }
 };
-
-// Write the 8 (key 2p, key 2p+1) bf16 pairs of d-rows d0..d0+7 into a V^T tile.
-template <class G>
-__device__ __forceinline__ void store_vt_pairs(char *vt, int p2, int c8, const u32x4_t &a, const u32x4_t &b) {
-  const int pos = G::vpos(2 * p2);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t lo = (i & 1) ? (a[i >> 1] >> 16) : (a[i >> 1] & 0xffffu);
-    const uint32_t hi = (i & 1) ? (b[i >> 1] & 0xffff0000u) : (b[i >> 1] << 16);
-    *reinterpret_cast<uint32_t *>(vt + G::v_off(8 * c8 + i, pos >> 3) + (pos & 7) * 2) = lo | hi;
-  }
-}
 
 // ------------------------------------------------------------------ sources
 
@@ -102,16 +81,13 @@ struct EncSrc {
   int n_keys;
   const float *mask;         // nullable: V rows of -inf-masked keys are not loaded (zeros)
   static constexpr int ES = F32 ? 4 : 2;
-  static constexpr int KU = G::BN * (G::D / 8);        // K units (8 elements) per tile
-  static constexpr int VU = (G::BN / 2) * (G::D / 8);  // V units (2 keys x 8 elements)
+  static constexpr int KU = G::BN * (G::D / 8);  // K (and V) units of 8 elements of one key per tile
   static constexpr int UK = G::NSPLIT * KU / G::THREADS;
-  static constexpr int UV = G::NSPLIT * VU / G::THREADS;
-  static_assert(UK * G::THREADS == G::NSPLIT * KU && UV * G::THREADS == G::NSPLIT * VU, "units");
-  static_assert(VU % 64 == 0 && (G::D / 8) % 8 == 0, "V unit mapping");
+  static_assert(UK * G::THREADS == G::NSPLIT * KU, "units");
   static constexpr int W = F32 ? 2 : 1;  // 16-byte loads per 8 elements
   struct Stage {
     u32x4_t k[UK][W];
-    u32x4_t v[UV][2][W];
+    u32x4_t v[UK][W];
   };
 
   __device__ __forceinline__ int64_t tile_base(int) const { return 0; }
@@ -132,18 +108,15 @@ struct EncSrc {
         st.k[j][x] = key_it + t < n_keys ? ldg<u32x4_t>(kbase + off + 16 * x) : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int j = 0; j < UV; ++j) {
+    for (int j = 0; j < UK; ++j) {
       const int u = tid + j * G::THREADS;
-      const int sp = u / VU, w = u % VU;
-      const int t0 = sp * G::BN + 2 * G::v_pair(w), c8 = G::v_chunk(w);
+      const int sp = u / KU, w = u % KU;
+      const int t = sp * G::BN + w / (G::D / 8), c = w % (G::D / 8);
+      const uint32_t off = (uint32_t)(t * vs + 8 * c) * ES;
+      const int key = key_it + t;
+      const bool live = key < n_keys && (mask == nullptr || mask[key] != -INFINITY);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const uint32_t off = (uint32_t)((t0 + r) * vs + 8 * c8) * ES;
-        const int key = key_it + t0 + r;
-        const bool live = key < n_keys && (mask == nullptr || mask[key] != -INFINITY);
-#pragma unroll
-        for (int x = 0; x < W; ++x) st.v[j][r][x] = live ? ldg<u32x4_t>(vbase + off + 16 * x) : u32x4_t{0, 0, 0, 0};
-      }
+      for (int x = 0; x < W; ++x) st.v[j][x] = live ? ldg<u32x4_t>(vbase + off + 16 * x) : u32x4_t{0, 0, 0, 0};
     }
   }
 
@@ -166,20 +139,15 @@ struct EncSrc {
       const int u = tid + j * G::THREADS;
       const int sp = u / KU, w = u % KU;
       const int t = w / (G::D / 8), c = w % (G::D / 8);
-      *reinterpret_cast<u32x4_t *>(stage + sp * G::SPLIT_BYTES + G::k_off(t, c)) = to_bf16(st.k[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < UV; ++j) {
-      const int u = tid + j * G::THREADS;
-      const int sp = u / VU, w = u % VU;
-      store_vt_pairs<G>(stage + sp * G::SPLIT_BYTES + G::KT, G::v_pair(w), G::v_chunk(w), to_bf16(st.v[j][0]),
-                        to_bf16(st.v[j][1]));
+      char *split = stage + sp * G::SPLIT_BYTES;
+      *reinterpret_cast<u32x4_t *>(split + G::k_off(t, c)) = to_bf16(st.k[j]);
+      *reinterpret_cast<u32x4_t *>(split + G::KT + t * G::VROW + 16 * c) = to_bf16(st.v[j]);
     }
   }
 };
 
-// Paged FP8 K/V: cache [num_blocks, Hkv, bs, D] e4m3fn; a K unit is 16 fp8 of
-// one key, a V unit 2 keys x 8 fp8.  Converted to bf16 exactly on store.
+// Paged FP8 K/V: cache [num_blocks, Hkv, bs, D] e4m3fn; a K or V unit is 16
+// fp8 of one key.  Converted to bf16 exactly on store.
 template <class G>
 struct PagedSrc {
   const uint8_t *kc, *vc;
@@ -188,14 +156,12 @@ struct PagedSrc {
   int64_t blk_stride;  // Hkv * bs * D
   int bs, n_keys;
   static constexpr int KU = G::BN * (G::D / 16);
-  static constexpr int VU = (G::BN / 2) * (G::D / 8);
   static constexpr int UK = KU / G::THREADS;
-  static constexpr int UV = VU / G::THREADS;
   static_assert(G::NSPLIT == 1, "paged source is single-split");
-  static_assert(UK * G::THREADS == KU && UV * G::THREADS == VU, "units");
+  static_assert(UK * G::THREADS == KU, "units");
   struct Stage {
     u32x4_t k[UK];
-    u32x2_t v[UV][2];
+    u32x4_t v[UK];
   };
 
   // Physical block of the tile `it` (uniform): a scalar load from the block
@@ -216,16 +182,9 @@ struct PagedSrc {
     for (int j = 0; j < UK; ++j) {
       const unsigned u = tid + j * G::THREADS;
       const unsigned t = u / (G::D / 16), c = u % (G::D / 16);
-      st.k[j] = key0 + t < (unsigned)n_keys ? ldg<u32x4_t>(kbase + (t * G::D + 16 * c)) : u32x4_t{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < UV; ++j) {
-      const unsigned w = tid + j * G::THREADS;
-      const unsigned t0 = 2 * G::v_pair(w), c8 = G::v_chunk(w);
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-        st.v[j][r] = key0 + t0 + r < (unsigned)n_keys ? ldg<u32x2_t>(vbase + ((t0 + r) * G::D + 8 * c8))
-                                                       : u32x2_t{0, 0};
+      const bool live = key0 + t < (unsigned)n_keys;
+      st.k[j] = live ? ldg<u32x4_t>(kbase + (t * G::D + 16 * c)) : u32x4_t{0, 0, 0, 0};
+      st.v[j] = live ? ldg<u32x4_t>(vbase + (t * G::D + 16 * c)) : u32x4_t{0, 0, 0, 0};
     }
   }
 
@@ -235,24 +194,22 @@ struct PagedSrc {
     for (int j = 0; j < UK; ++j) {
       const int u = tid + j * G::THREADS;
       const int t = u / (G::D / 16), c = u % (G::D / 16);
-      const u32x4_t x = st.k[j];
-      const u32x4_t lo = {e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]),
-                          e4m3x2_to_bf16x2<false>(x[1]), e4m3x2_to_bf16x2<true>(x[1])};
-      const u32x4_t hi = {e4m3x2_to_bf16x2<false>(x[2]), e4m3x2_to_bf16x2<true>(x[2]),
-                          e4m3x2_to_bf16x2<false>(x[3]), e4m3x2_to_bf16x2<true>(x[3])};
-      *reinterpret_cast<u32x4_t *>(stage + G::k_off(t, 2 * c)) = lo;
-      *reinterpret_cast<u32x4_t *>(stage + G::k_off(t, 2 * c + 1)) = hi;
+      *reinterpret_cast<u32x4_t *>(stage + G::k_off(t, 2 * c)) = lo16(st.k[j]);
+      *reinterpret_cast<u32x4_t *>(stage + G::k_off(t, 2 * c + 1)) = hi16(st.k[j]);
+      char *vrow = stage + G::KT + t * G::VROW + 32 * c;
+      *reinterpret_cast<u32x4_t *>(vrow) = lo16(st.v[j]);
+      *reinterpret_cast<u32x4_t *>(vrow + 16) = hi16(st.v[j]);
     }
-#pragma unroll
-    for (int j = 0; j < UV; ++j) {
-      const int w = tid + j * G::THREADS;
-      const u32x2_t xa = st.v[j][0], xb = st.v[j][1];
-      const u32x4_t a = {e4m3x2_to_bf16x2<false>(xa[0]), e4m3x2_to_bf16x2<true>(xa[0]),
-                         e4m3x2_to_bf16x2<false>(xa[1]), e4m3x2_to_bf16x2<true>(xa[1])};
-      const u32x4_t b = {e4m3x2_to_bf16x2<false>(xb[0]), e4m3x2_to_bf16x2<true>(xb[0]),
-                         e4m3x2_to_bf16x2<false>(xb[1]), e4m3x2_to_bf16x2<true>(xb[1])};
-      store_vt_pairs<G>(stage + G::KT, G::v_pair(w), G::v_chunk(w), a, b);
-    }
+  }
+
+  // fp8 bytes 0..7 / 8..15 of a unit -> 8 bf16 (exact)
+  static __device__ __forceinline__ u32x4_t lo16(const u32x4_t &x) {
+    return u32x4_t{e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]), e4m3x2_to_bf16x2<false>(x[1]),
+                   e4m3x2_to_bf16x2<true>(x[1])};
+  }
+  static __device__ __forceinline__ u32x4_t hi16(const u32x4_t &x) {
+    return u32x4_t{e4m3x2_to_bf16x2<false>(x[2]), e4m3x2_to_bf16x2<true>(x[2]), e4m3x2_to_bf16x2<false>(x[3]),
+                   e4m3x2_to_bf16x2<true>(x[3])};
   }
 };
 
@@ -410,20 +367,24 @@ __device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&q
     ws.l[nt] = lsum;
   }
 
-  // PV: fragment f = (kb*2 + kk)*MT + mt of V^T, same read-ahead ordering.
+  // PV: fragment f = (kb*2 + kk)*MT + mt, same read-ahead ordering.  The A
+  // fragment (d rows mt*32 + l32, k-slots j = 0..7 of lane-half h) must hold
+  // the keys that P's B fragment holds: kb*32 + 16kk + 8(j/4) + 4h + j%4.  Two
+  // transposing reads (t = j/4) fetch it: in 16-lane group g the reading lane
+  // 4m + j names the 8 bytes V[kb*32 + 16kk + 8t + 4h + j][mt*32 + 16(g%2) + 4m ..],
+  // and output lane 16g + 4m + c receives element c of those four rows.
   {
     constexpr int NF = G::KB * 2 * G::MT, RA = G::GRP < NF ? G::GRP : NF;
-    // V^T fragment (mt, kb, kk): row mt*32 + l32, chunk kb*4 + kk*2 + h; the
-    // swizzle depends on the lane only, so KB*2 per-lane bases + offsets.
-    const int vsw = (l32 / G::VROWS) % G::VSW;
-    int vbase[G::KB * 2];
-#pragma unroll
-    for (int j = 0; j < G::KB * 2; ++j) vbase[j] = l32 * (G::BN * 2) + (((2 * j + h) ^ vsw) << 4);
+    const int vlane = (4 * h + ((lane >> 2) & 3)) * G::VROW + (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
     __builtin_amdgcn_sched_barrier(0);
     u32x4_t fb[NF];
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
-      fb[f] = *reinterpret_cast<const u32x4_t *>(vt + vbase[f / G::MT] + (f % G::MT) * 32 * G::BN * 2);
+    for (int f = 0; f < NF; ++f) {
+      const int mt = f % G::MT, kk = (f / G::MT) % 2, kb = f / (2 * G::MT);
+      const char *p = vt + vlane + (kb * 32 + kk * 16) * G::VROW + mt * 64;
+      const u32x2_t a0 = lds_read_tr16(p), a1 = lds_read_tr16(p + 8 * G::VROW);
+      fb[f] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    }
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int mt = f % G::MT, kk = (f / G::MT) % 2, kb = f / (2 * G::MT);
@@ -431,11 +392,11 @@ __device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&q
       for (int nt = 0; nt < G::NT; ++nt)
         ws.o[nt][mt] = mfma32(as_bf16x8(fb[f]), as_bf16x8(pb[nt][kb][kk]), ws.o[nt][mt]);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RA, 0);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       __builtin_amdgcn_sched_group_barrier(0x008, G::NT, 0);
-      if (f + RA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (f + RA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
