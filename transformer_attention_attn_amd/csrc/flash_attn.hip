@@ -28,95 +28,142 @@
 //   rows on N): P never leaves registers; the row sum is taken on the packed
 //   bf16 P with v_dot2_f32_bf16, so it normalises exactly the values that were
 //   multiplied into V.
-// K tiles sit in LDS as [key][d] (16-byte chunks XOR-swizzled by key); V tiles
-// as [key][d] too, rows padded by 64 bytes, and the A operand of the PV MFMA
-// (d on M, keys on K) is read transposed with ds_read_b64_tr_b16: the padding
-// puts the four keys one read touches in four different 64-byte bank groups,
-// so both the plain 16-byte V writes and the transposing reads are
-// conflict-free.  Global loads for the next PF tiles stay in flight in
-// registers (uniform 64-bit base + 32-bit per-thread offset) while a tile is
-// computed from one LDS stage and the next is written to the other.
+//
+// Software pipeline: K tiles sit one tile ahead of V tiles in LDS, so while a
+// wave's MFMAs compute S for tile i+1, its VALU runs the softmax of tile i;
+// then the PV MFMAs of tile i run while the staged global loads are written
+// to LDS and the next ones are issued.  One barrier per tile.
+//
+// LDS: K and V tiles as [key][d] with padded rows, V read as the A operand
+// of the PV MFMA (d on M, keys on K) with ds_read_b64_tr_b16.  The pads make
+// the 16-byte K reads, the transposing V reads and the 16-byte writes all
+// bank-conflict-free while every fragment address stays one per-lane base
+// plus an immediate.  Global
+// K/V loads are raw buffer loads whose range ends at the last valid key, so
+// out-of-range keys read as zeros without a branch.
 #include "device_common.h"
 #include "launch.h"
 
 namespace mi355 {
 
-constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
+constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family: 32-bit data format, no swizzle)
 
-template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int PF_, int OCC_ = 2>
+// Raw buffer resource over [base, base + bytes).  Both are uniform at every
+// call; readfirstlane makes that visible to the compiler, which otherwise may
+// compute them in vector registers and wrap each load in a waterfall loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+// 16 bytes at byte offset `off`; zeros when the range check fails
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int OCC_>
 struct Geo {
   static constexpr int D = D_, BN = BN_, NT = NT_, RG = RG_, NSPLIT = NSPLIT_;
-  static constexpr int GRP = GRP_;  // LDS fragments read per pipelined group
-  static constexpr int PF = PF_;    // key tiles in flight in registers (global-load prefetch depth)
-  static constexpr int WAVES = RG * NSPLIT, THREADS = 64 * WAVES;
+  static constexpr int GRP = GRP_;  // LDS fragments read ahead of the MFMAs that use them
   static constexpr int WPE = OCC_;  // waves per SIMD the kernel is compiled for (register budget 512 / WPE)
+  static constexpr int WAVES = RG * NSPLIT, THREADS = 64 * WAVES;
   static constexpr int BM = 32 * NT * RG;
-  static constexpr int KT = BN * D * 2;  // bytes of one bf16 K tile
-  static constexpr int VROW = D * 2 + 64;  // bytes per key row of a V tile (64-byte pad: an odd multiple of 64 mod 256)
-  static constexpr int VT = BN * VROW;   // bytes of one bf16 V tile
-  static constexpr int SPLIT_BYTES = KT + VT;
-  static constexpr int STAGE = NSPLIT * SPLIT_BYTES;
-  static constexpr int LDS = 2 * STAGE;
+  // K rows: D bf16 + one 16-byte pad chunk, so 16 consecutive rows start in 16
+  // different 16-byte bank groups.  V rows: D bf16, plus 64 bytes after every
+  // row (D >= 128) or every second row (D = 64), so the 4 consecutive rows one
+  // transposing read touches start in 4 different 64-byte bank groups.
+  static constexpr int KROW = D * 2 + 16;
+  static constexpr int VSH = (D * 2) % 256 == 0 ? 0 : 1;
+  static constexpr int KTILE = BN * KROW;
+  static constexpr int VTILE = BN * D * 2 + (BN >> VSH) * 64;
+  static constexpr int KSLOT = NSPLIT * KTILE;                    // one K buffer: every split's tile
+  static constexpr int VSLOT = NSPLIT * VTILE + NSPLIT * BN * 4;  // one V buffer, then the tiles' staged key mask
+  static constexpr int LDS = 2 * (KSLOT + VSLOT);          // K and V double-buffered
   static constexpr int KB = BN / 32;  // 32-key blocks per tile
   static constexpr int SD = D / 16;   // k-steps of the QK^T contraction
   static constexpr int MT = D / 32;   // d tiles of O^T
-  static_assert(D % 64 == 0 && BN % 32 == 0, "tile shape");
+  static constexpr int NFQ = SD * KB, NFV = 2 * KB * MT;  // LDS fragments per tile: QK, PV
+  // softmax VALU instructions issued between consecutive QK MFMA groups
+  static constexpr int VPM = (NT * (7 * BN / 4 + 8) + NFQ - 1) / NFQ;
+  static_assert(D % 64 == 0 && BN % 32 == 0 && (VSH == 0 || D == 64), "tile shape");
   static_assert(LDS <= 160 * 1024, "LDS budget (gfx950: 160 KiB per workgroup)");
-  static_assert((VROW / 64) % 2 == 1 && VROW % 256 != 0, "V row pad");
 
-  // byte offset of 16-byte chunk c of key row `key` in a K tile
-  static __device__ __forceinline__ int k_off(int key, int c) { return key * (D * 2) + ((c ^ (key & 7)) << 4); }
+  static __device__ __forceinline__ int k_row(int key) { return key * KROW; }
+  static __device__ __forceinline__ int v_row(int key) { return key * (D * 2) + (key >> VSH) * 64; }
 };
 
 // ------------------------------------------------------------------ sources
+//
+// A source loads the K and V tiles of iteration `it` (every split's tile,
+// keys it*NSPLIT*BN ...) into a register stage and writes them to an LDS
+// buffer.  Keys past n_keys read as zeros (buffer range check).
 
-// Encoder K/V: [B,H,S_kv,D] strided, bf16 or fp32 (fp32 rounded to bf16 here).
-// Unit u of an iteration belongs to split u / KU; its key row is fixed per
-// thread, so the address is base(iteration) + a 32-bit per-thread offset.
-template <class G, bool F32>
+// Encoder K/V: [B,H,S_kv,D] strided, bf16 or fp32 (fp32 rounded to bf16 on
+// the LDS write).  A unit is 8 elements of one key; unit u of an iteration is
+// key (u / KU)*BN + (u % KU)/(D/8) of the iteration, chunk u % (D/8).
+template <class G, bool F32, bool HAS_MASK>
 struct EncSrc {
-  const char *kb, *vb;       // this (b,h)'s K and V base
-  int64_t kstep, vstep;      // bytes between consecutive iterations (NSPLIT*BN keys)
-  int64_t ks, vs;            // element stride between keys
+  const char *kb, *vb;    // this (b,h)'s K and V base
+  const float *mask;      // this batch row's additive mask (HAS_MASK)
+  int64_t kstep, vstep;   // bytes per iteration (NSPLIT*BN keys)
+  uint32_t krow, vrow;    // bytes between consecutive keys
   int n_keys;
-  const float *mask;         // nullable: V rows of -inf-masked keys are not loaded (zeros)
   static constexpr int ES = F32 ? 4 : 2;
-  static constexpr int KU = G::BN * (G::D / 8);  // K (and V) units of 8 elements of one key per tile
-  static constexpr int UK = G::NSPLIT * KU / G::THREADS;
-  static_assert(UK * G::THREADS == G::NSPLIT * KU, "units");
-  static constexpr int W = F32 ? 2 : 1;  // 16-byte loads per 8 elements
+  static constexpr int W = F32 ? 2 : 1;  // 16-byte loads per unit
+  static constexpr int CPR = G::D / 8;   // units per key row
+  static constexpr int KU = G::BN * CPR;
+  static constexpr int KEYS = G::NSPLIT * G::BN;
+  static constexpr int UK = KEYS * CPR / G::THREADS;
+  static_assert(UK >= 1 && UK * G::THREADS == KEYS * CPR, "units");
+  static_assert(KEYS <= G::THREADS, "mask staging: one key per thread");
+  static_assert(KEYS <= 128, "records(): KEYS * row bytes must stay below 2^31 (row < 2^24 bytes)");
   struct Stage {
-    u32x4_t k[UK][W];
-    u32x4_t v[UK][W];
+    u32x4_t k[UK][W], v[UK][W];
+    float vm[UK];  // mask value of each V unit's key
+    float m;       // mask value of key tid % KEYS
   };
 
+  static __device__ __forceinline__ unsigned key_of(unsigned u) { return (u / KU) * G::BN + (u % KU) / CPR; }
+  static __device__ __forceinline__ unsigned chunk_of(unsigned u) { return u % CPR; }
+
+  // bytes of the iteration's keys that exist (the key stride is below 2^24
+  // bytes, checked on the host)
+  __device__ __forceinline__ uint32_t records(int it, uint32_t row) const {
+    const int rem = min(max(n_keys - it * KEYS, 0), KEYS);
+    return (uint32_t)rem * row;
+  }
   __device__ __forceinline__ int64_t tile_base(int) const { return 0; }
 
-  __device__ __forceinline__ void load(Stage &st, int it, int64_t, int tid) const {
-    asm volatile("" : "+v"(tid));  // per-thread offsets are cheap 32-bit math: recompute, don't keep live
-    const char *kbase = kb + it * kstep;
-    const char *vbase = vb + it * vstep;
-    const int key_it = it * G::NSPLIT * G::BN;
+  __device__ __forceinline__ void load_k(Stage &st, int it, int64_t, unsigned tid) const {
+    const auto r = make_rsrc(kb + it * kstep, records(it, krow));
 #pragma unroll
     for (int j = 0; j < UK; ++j) {
-      const int u = tid + j * G::THREADS;
-      const int sp = u / KU, w = u % KU;
-      const int t = sp * G::BN + w / (G::D / 8), c = w % (G::D / 8);
-      const uint32_t off = (uint32_t)(t * ks + 8 * c) * ES;
+      const unsigned u = tid + j * G::THREADS;
+      const uint32_t off = key_of(u) * krow + chunk_of(u) * (8 * ES);
 #pragma unroll
-      for (int x = 0; x < W; ++x)
-        st.k[j][x] = key_it + t < n_keys ? ldg<u32x4_t>(kbase + off + 16 * x) : u32x4_t{0, 0, 0, 0};
+      for (int x = 0; x < W; ++x) st.k[j][x] = buf_load16(r, off + 16 * x);
     }
+  }
+  __device__ __forceinline__ void load_v(Stage &st, int it, int64_t, unsigned tid) const {
+    const auto r = make_rsrc(vb + it * vstep, records(it, vrow));
 #pragma unroll
     for (int j = 0; j < UK; ++j) {
-      const int u = tid + j * G::THREADS;
-      const int sp = u / KU, w = u % KU;
-      const int t = sp * G::BN + w / (G::D / 8), c = w % (G::D / 8);
-      const uint32_t off = (uint32_t)(t * vs + 8 * c) * ES;
-      const int key = key_it + t;
-      const bool live = key < n_keys && (mask == nullptr || mask[key] != -INFINITY);
+      const unsigned u = tid + j * G::THREADS;
+      const uint32_t off = key_of(u) * vrow + chunk_of(u) * (8 * ES);
 #pragma unroll
-      for (int x = 0; x < W; ++x) st.v[j][x] = live ? ldg<u32x4_t>(vbase + off + 16 * x) : u32x4_t{0, 0, 0, 0};
+      for (int x = 0; x < W; ++x) st.v[j][x] = buf_load16(r, off + 16 * x);
+    }
+    if constexpr (HAS_MASK) {
+      const auto rm = make_rsrc(mask + (int64_t)it * KEYS, records(it, 4));
+#pragma unroll
+      for (int j = 0; j < UK; ++j) st.vm[j] = buf_load_f32(rm, key_of(tid + j * G::THREADS) * 4);
+      st.m = buf_load_f32(rm, (tid % KEYS) * 4);
     }
   }
 
@@ -132,22 +179,40 @@ struct EncSrc {
     }
   }
 
-  __device__ __forceinline__ void store(const Stage &st, char *stage, int tid) const {
-    asm volatile("" : "+v"(tid));
+  __device__ __forceinline__ void store_k(const Stage &st, char *slot, unsigned tid) const {
 #pragma unroll
     for (int j = 0; j < UK; ++j) {
-      const int u = tid + j * G::THREADS;
-      const int sp = u / KU, w = u % KU;
-      const int t = w / (G::D / 8), c = w % (G::D / 8);
-      char *split = stage + sp * G::SPLIT_BYTES;
-      *reinterpret_cast<u32x4_t *>(split + G::k_off(t, c)) = to_bf16(st.k[j]);
-      *reinterpret_cast<u32x4_t *>(split + G::KT + t * G::VROW + 16 * c) = to_bf16(st.v[j]);
+      const unsigned u = tid + j * G::THREADS;
+      const unsigned t = (u % KU) / CPR;
+      *reinterpret_cast<u32x4_t *>(slot + (u / KU) * G::KTILE + G::k_row(t) + 16 * chunk_of(u)) = to_bf16(st.k[j]);
+    }
+  }
+  // V rows of keys the mask removes are written as zeros (p = 0 there, and a
+  // non-finite V must not turn 0 * V into NaN); the staged mask is in log2
+  // units, -inf for removed keys and keys past n_keys.
+  __device__ __forceinline__ void store_v(const Stage &st, char *slot, int it, unsigned tid) const {
+#pragma unroll
+    for (int j = 0; j < UK; ++j) {
+      const unsigned u = tid + j * G::THREADS;
+      const unsigned t = (u % KU) / CPR;
+      u32x4_t x = to_bf16(st.v[j]);
+      if constexpr (HAS_MASK) x = st.vm[j] == -INFINITY ? u32x4_t{0, 0, 0, 0} : x;
+      *reinterpret_cast<u32x4_t *>(slot + (u / KU) * G::VTILE + G::v_row(t) + 16 * chunk_of(u)) = x;
+    }
+    if constexpr (HAS_MASK) {
+      // every thread writes key tid % KEYS (identical values where threads coincide)
+      const unsigned t = tid % KEYS;
+      const bool live = it * KEYS + (int)t < n_keys && st.m != -INFINITY;
+      reinterpret_cast<float *>(slot + G::NSPLIT * G::VTILE)[t] = live ? st.m * kLog2e : -INFINITY;
     }
   }
 };
 
-// Paged FP8 K/V: cache [num_blocks, Hkv, bs, D] e4m3fn; a K or V unit is 16
-// fp8 of one key.  Converted to bf16 exactly on store.
+// Paged FP8 K/V: cache [num_blocks, Hkv, bs, D] e4m3fn.  A unit is 8 fp8 of
+// each half of one key row: lane i of a row's D/16 lanes takes bytes
+// [8i, 8i+8) and [D/2 + 8i, D/2 + 8i + 8), so that in LDS (bf16, converted
+// exactly) consecutive lanes write consecutive 16-byte chunks.  A tile (BN
+// keys) never straddles a cache block (bs is a multiple of BN).
 template <class G>
 struct PagedSrc {
   const uint8_t *kc, *vc;
@@ -155,65 +220,75 @@ struct PagedSrc {
   int64_t head_off;    // kvh * bs * D
   int64_t blk_stride;  // Hkv * bs * D
   int bs, n_keys;
-  static constexpr int KU = G::BN * (G::D / 16);
+  static constexpr int LPR = G::D / 16;  // lanes per key row
+  static constexpr int KU = G::BN * LPR;
   static constexpr int UK = KU / G::THREADS;
   static_assert(G::NSPLIT == 1, "paged source is single-split");
-  static_assert(UK * G::THREADS == KU, "units");
+  static_assert(UK >= 1 && UK * G::THREADS == KU, "units");
   struct Stage {
-    u32x4_t k[UK];
-    u32x4_t v[UK];
+    u32x2_t k[UK][2], v[UK][2];
   };
 
-  // Physical block of the tile `it` (uniform): a scalar load from the block
-  // table (read-only for the whole launch, so it may use the constant path).
+  // Byte offset of tile `it` in a cache (uniform): a scalar load from the
+  // block table (read-only for the whole launch, so it may use the constant
+  // path).  Tiles past the last live one reuse its block, so the lookup stays
+  // inside the table; their loads read nothing (zero range).
   __device__ __forceinline__ int64_t tile_base(int it) const {
-    const int last = (n_keys - 1) / G::BN;  // padding tiles reuse the last live block: always inside the table
+    const int last = (n_keys - 1) / G::BN;
     const unsigned key0 = (unsigned)(it < last ? it : last) * G::BN;
     const int32_t phys = bt[key0 / (unsigned)bs];
     return (int64_t)phys * blk_stride + head_off + (int64_t)(key0 % (unsigned)bs) * G::D;
   }
-
-  // `base` is tile_base(it), computed one tile ahead by the caller.
-  __device__ __forceinline__ void load(Stage &st, int it, int64_t base, unsigned tid) const {
-    asm volatile("" : "+v"(tid));
-    const unsigned key0 = (unsigned)it * G::BN;
-    const uint8_t *kbase = kc + base, *vbase = vc + base;
+  __device__ __forceinline__ uint32_t records(int it) const {
+    return (uint32_t)min(max(n_keys - it * G::BN, 0), G::BN) * G::D;
+  }
+  static __device__ __forceinline__ u32x2_t load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
+  __device__ __forceinline__ void load(u32x2_t (&x)[UK][2], const uint8_t *cache, int it, int64_t base,
+                                       unsigned tid) const {
+    const auto r = make_rsrc(cache + base, records(it));
 #pragma unroll
     for (int j = 0; j < UK; ++j) {
       const unsigned u = tid + j * G::THREADS;
-      const unsigned t = u / (G::D / 16), c = u % (G::D / 16);
-      const bool live = key0 + t < (unsigned)n_keys;
-      st.k[j] = live ? ldg<u32x4_t>(kbase + (t * G::D + 16 * c)) : u32x4_t{0, 0, 0, 0};
-      st.v[j] = live ? ldg<u32x4_t>(vbase + (t * G::D + 16 * c)) : u32x4_t{0, 0, 0, 0};
+      const uint32_t off = (u / LPR) * G::D + (u % LPR) * 8;
+      x[j][0] = load8(r, off);
+      x[j][1] = load8(r, off + G::D / 2);
     }
   }
-
-  __device__ __forceinline__ void store(const Stage &st, char *stage, int tid) const {
-    asm volatile("" : "+v"(tid));
-#pragma unroll
-    for (int j = 0; j < UK; ++j) {
-      const int u = tid + j * G::THREADS;
-      const int t = u / (G::D / 16), c = u % (G::D / 16);
-      *reinterpret_cast<u32x4_t *>(stage + G::k_off(t, 2 * c)) = lo16(st.k[j]);
-      *reinterpret_cast<u32x4_t *>(stage + G::k_off(t, 2 * c + 1)) = hi16(st.k[j]);
-      char *vrow = stage + G::KT + t * G::VROW + 32 * c;
-      *reinterpret_cast<u32x4_t *>(vrow) = lo16(st.v[j]);
-      *reinterpret_cast<u32x4_t *>(vrow + 16) = hi16(st.v[j]);
-    }
+  __device__ __forceinline__ void load_k(Stage &st, int it, int64_t base, unsigned tid) const {
+    load(st.k, kc, it, base, tid);
+  }
+  __device__ __forceinline__ void load_v(Stage &st, int it, int64_t base, unsigned tid) const {
+    load(st.v, vc, it, base, tid);
   }
 
-  // fp8 bytes 0..7 / 8..15 of a unit -> 8 bf16 (exact)
-  static __device__ __forceinline__ u32x4_t lo16(const u32x4_t &x) {
+  // 8 fp8 -> 8 bf16 (exact)
+  static __device__ __forceinline__ u32x4_t cvt8(const u32x2_t &x) {
     return u32x4_t{e4m3x2_to_bf16x2<false>(x[0]), e4m3x2_to_bf16x2<true>(x[0]), e4m3x2_to_bf16x2<false>(x[1]),
                    e4m3x2_to_bf16x2<true>(x[1])};
   }
-  static __device__ __forceinline__ u32x4_t hi16(const u32x4_t &x) {
-    return u32x4_t{e4m3x2_to_bf16x2<false>(x[2]), e4m3x2_to_bf16x2<true>(x[2]), e4m3x2_to_bf16x2<false>(x[3]),
-                   e4m3x2_to_bf16x2<true>(x[3])};
+  __device__ __forceinline__ void store_k(const Stage &st, char *slot, unsigned tid) const {
+#pragma unroll
+    for (int j = 0; j < UK; ++j) {
+      const unsigned u = tid + j * G::THREADS;
+      char *p = slot + G::k_row(u / LPR) + 16 * (u % LPR);
+      *reinterpret_cast<u32x4_t *>(p) = cvt8(st.k[j][0]);
+      *reinterpret_cast<u32x4_t *>(p + G::D) = cvt8(st.k[j][1]);
+    }
+  }
+  __device__ __forceinline__ void store_v(const Stage &st, char *slot, int, unsigned tid) const {
+#pragma unroll
+    for (int j = 0; j < UK; ++j) {
+      const unsigned u = tid + j * G::THREADS;
+      char *p = slot + G::v_row(u / LPR) + 16 * (u % LPR);
+      *reinterpret_cast<u32x4_t *>(p) = cvt8(st.v[j][0]);
+      *reinterpret_cast<u32x4_t *>(p + G::D) = cvt8(st.v[j][1]);
+    }
   }
 };
 
-// ------------------------------------------------------------------ core loop
+// ------------------------------------------------------------------ per-tile pieces
 
 template <class G>
 struct WaveState {
@@ -231,73 +306,33 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One key tile for one wave.  c = softmax_scale*log2(e) > 0.  `mask` (only
-// read when HAS_MASK) is the additive key mask of this batch row, natural-log
-// units; keys >= n_keys are removed.
-template <class G, bool HAS_MASK>
-__device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&qf)[G::NT][G::SD],
-                                             const char *kt, const char *vt, int key0, int n_keys,
-                                             float c, const float *mask, int lane) {
-  asm volatile("" : "+v"(lane));  // lane-derived LDS offsets are recomputed per tile, not kept live
-  const int l32 = lane & 31, h = lane >> 5;
-  f32x16_t s[G::NT][G::KB];
+// S^T of one tile: s[nt][kb] = K-block kb . Q^T.  K fragment (kb, sd) is the
+// 16 bytes at d = 16*sd + 8*(lane/32) of row kb*32 + lane%32.
+template <class G>
+__device__ __forceinline__ void qk_tile(f32x16_t (&s)[G::NT][G::KB], const u32x4_t (&qf)[G::NT][G::SD],
+                                        const char *kt, int lane) {
+  const char *base = kt + (lane & 31) * G::KROW + 16 * (lane >> 5);
+  u32x4_t fb[G::NFQ];
 #pragma unroll
-  for (int nt = 0; nt < G::NT; ++nt)
-#pragma unroll
-    for (int kb = 0; kb < G::KB; ++kb) s[nt][kb] = f32x16_t{};
-
-  // QK^T: fragment f = sd*KB + kb feeds NT MFMAs.  All fragments are
-  // written as loads up front; the scheduling groups below order them as
-  // RA reads ahead, then (MFMA x NT, next read) pairs, so RA LDS reads stay in
-  // flight behind the MFMAs while only RA+1 fragments are live.
-  {
-    constexpr int NF = G::SD * G::KB, RA = G::GRP < NF ? G::GRP : NF;
-    // K fragment (kb, sd): row kb*32 + l32, chunk 2*sd + h.  The XOR swizzle
-    // only touches the low 3 chunk bits, so the address is one of 4 per-lane
-    // bases plus a compile-time offset.
-    int kbase[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kbase[j] = l32 * (G::D * 2) + (((2 * j + h) ^ (l32 & 7)) << 4);
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4_t fb[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int kb = f % G::KB, sd = f / G::KB;
-      fb[f] = *reinterpret_cast<const u32x4_t *>(kt + kbase[sd & 3] + kb * 32 * G::D * 2 + (sd >> 2) * 128);
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int nt = 0; nt < G::NT; ++nt)
-        s[nt][f % G::KB] = mfma32(as_bf16x8(fb[f]), as_bf16x8(qf[nt][f / G::KB]), s[nt][f % G::KB]);
-    __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      __builtin_amdgcn_sched_group_barrier(0x008, G::NT, 0);
-      if (f + RA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+  for (int f = 0; f < G::NFQ; ++f) {
+    const int kb = f % G::KB, sd = f / G::KB;
+    fb[f] = *reinterpret_cast<const u32x4_t *>(base + kb * 32 * G::KROW + 32 * sd);
   }
+#pragma unroll
+  for (int f = 0; f < G::NFQ; ++f) {
+    const int kb = f % G::KB, sd = f / G::KB;
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt)
+      s[nt][kb] = mfma32(as_bf16x8(fb[f]), as_bf16x8(qf[nt][sd]), sd == 0 ? f32x16_t{} : s[nt][kb]);
+  }
+}
 
-  // Scores into log2 units.  Without a mask the row max is taken on the raw
-  // scores and the scale is folded into the exp2 argument (one FMA per score);
-  // with a mask the scaled, masked score is formed first.
-  if constexpr (HAS_MASK) {
-#pragma unroll
-    for (int kb = 0; kb < G::KB; ++kb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int key = key0 + kb * 32 + r4 * 8 + 4 * h;
-        float mk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mk[i] = key + i < n_keys ? mask[key + i] * kLog2e : -INFINITY;
-#pragma unroll
-        for (int nt = 0; nt < G::NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)  // removed keys stay -inf whatever their K holds
-            s[nt][kb][4 * r4 + i] = mk[i] == -INFINITY ? -INFINITY : __builtin_fmaf(s[nt][kb][4 * r4 + i], c, mk[i]);
-      }
-  } else if (key0 + G::BN > n_keys) {  // ragged last tile (uniform branch)
+// Remove keys >= n_keys from a tile whose keys start at key0 (no-mask kernels;
+// rare uniform branch: only the ragged last tile and padding tiles).
+template <class G>
+__device__ __forceinline__ void mask_tail(f32x16_t (&s)[G::NT][G::KB], int key0, int n_keys, int lane) {
+  if (key0 + G::BN > n_keys) {
+    const int h = lane >> 5;
 #pragma unroll
     for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
@@ -308,115 +343,253 @@ __device__ __forceinline__ void compute_tile(WaveState<G> &ws, const u32x4_t (&q
           if (key >= n_keys) s[nt][kb][v] = -INFINITY;
       }
   }
+}
 
-  float mx[G::NT];
+// Empty asm statements are ordered side effects: pin_in redefines a value at
+// a point (nothing that uses it can move above), pin_out consumes it (its
+// computation cannot sink below).  Together with sched_barrier they hold a
+// hand-interleaved MFMA / VALU sequence in place.
+template <class T>
+__device__ __forceinline__ void pin_in(T &x) {
+  asm volatile("" : "+v"(x));
+}
+template <class T>
+__device__ __forceinline__ void pin_out(const T &x) {
+  asm volatile("" ::"v"(x));
+}
+
+// Softmax state carried from phase A into phase B of a tile step: the packed
+// bf16 P words (w[nt][kb][i] holds keys 2i, 2i+1 of the lane's 16 in block kb),
+// the running row sum and the reference max used for this tile's exponents.
+template <class G>
+struct PCarry {
+  uint32_t w[G::NT][G::KB][8];
+  float lsum[G::NT], m_use[G::NT];
+};
+
+// exp2 / bf16 pack / row sum of P pair i8 of block (nt, kb), with the
+// reference max `mu` (a slot-local pinned copy).
+template <class G, bool HAS_MASK>
+__device__ __forceinline__ void p_pair(PCarry<G> &pc, const f32x16_t (&s)[G::NT][G::KB], int nt, int kb, int i8,
+                                       float mu, float c) {
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+  const float x0 = s[nt][kb][2 * i8], x1 = s[nt][kb][2 * i8 + 1];
+  const float e0 = HAS_MASK ? fast_exp2(x0 - mu) : fast_exp2(__builtin_fmaf(x0, c, -mu));
+  const float e1 = HAS_MASK ? fast_exp2(x1 - mu) : fast_exp2(__builtin_fmaf(x1, c, -mu));
+  pc.w[nt][kb][i8] = pack_bf16(e0, e1);
+  pc.lsum[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pc.w[nt][kb][i8]), ones, pc.lsum[nt], false);
+  pin_out(pc.w[nt][kb][i8]);
+}
+
+// P pairs [p0, p1) of one half (i8 < 4: the first 16 keys of each 32-key
+// block, i8 >= 4: the second), numbered over (nt, kb, i8 % 4).
+template <class G, bool HAS_MASK>
+__device__ __forceinline__ void p_pairs(PCarry<G> &pc, const f32x16_t (&s)[G::NT][G::KB], int half, int p0, int p1,
+                                        float c) {
+  float mu[G::NT];
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
-    float mloc = -INFINITY;
+    mu[nt] = pc.m_use[nt];
+    pin_in(mu[nt]);  // keeps this slot's exps from being hoisted into an earlier slot
+  }
+#pragma unroll
+  for (int a = p0; a < p1; ++a) {
+    const int nt = a / (G::KB * 4), kb = (a / 4) % G::KB, i8 = 4 * half + a % 4;
+    p_pair<G, HAS_MASK>(pc, s, nt, kb, i8, mu[nt], c);
+  }
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) pin_out(pc.lsum[nt]);
+}
+
+// u32x4 B fragment of P for (nt, kb, kk) from the packed words (bit-cast plain
+// scalars, never ext-vector elements: hipcc folded a bit_cast of pb[..][i] to
+// element 0 for every i)
+template <class G>
+__device__ __forceinline__ u32x4_t p_frag(const PCarry<G> &pc, int nt, int kb, int kk) {
+  return u32x4_t{pc.w[nt][kb][4 * kk], pc.w[nt][kb][4 * kk + 1], pc.w[nt][kb][4 * kk + 2], pc.w[nt][kb][4 * kk + 3]};
+}
+
+// Phase A of one tile step: S(next) = K(next) Q^T on MFMA, interleaved with
+// the online softmax of S (this tile) on the VALU.  c = softmax_scale*log2(e)
+// > 0.  With a mask, mk (LDS) holds this tile's additive mask in log2 units,
+// -inf for removed keys.  Computes the first half of P (the keys the first
+// PV MFMAs consume), updates m, and returns whether any row's reference max
+// moved (then O must be multiplied by alpha before PV).
+//
+// Slot f issues QK MFMA f and the K read GRP fragments ahead, then a slice of
+// the softmax: slot 0 the row max, slot 1 the cross-lane max, the rescale
+// decision and alpha, later slots the exp2 / bf16 pack / row sum of P pairs.
+// sched_barrier(0) and the pins hold that order, so this wave's MFMAs run
+// under its own VALU work; the second half of P is left to phase B, which
+// balances the VALU load of the two phases.
+//
+// Lazy rescale: the reference max m of a row only moves when the tile max
+// exceeds it by more than kTau, so p = 2^(s - m) <= 2^kTau and the O rescale
+// (a VALU pass over every accumulator) is rare.  Exact: the final O/l uses one
+// consistent reference per row.  The row sum is taken on the packed bf16 P
+// (v_dot2_f32_bf16), so it normalises exactly the values multiplied into V.
+template <class G, bool HAS_MASK>
+__device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_t (&sn)[G::NT][G::KB],
+                                        f32x16_t (&s)[G::NT][G::KB], float (&alpha)[G::NT],
+                                        const u32x4_t (&qf)[G::NT][G::SD], const char *kt, const float *mk, float c,
+                                        int lane) {
+  constexpr int RA = G::GRP < G::NFQ ? G::GRP : G::NFQ;
+  constexpr int NP = G::NT * G::KB * 4;  // P pairs of the first half
+  constexpr int SLOTS = G::NFQ - 2;
+  constexpr int PPS = (NP + SLOTS - 1) / SLOTS;
+  static_assert(SLOTS >= 1, "QK slots");
+  const int h = lane >> 5;
+  const char *kbase = kt + (lane & 31) * G::KROW + 16 * h;
+
+  u32x4_t fb[G::NFQ];
+  f32x4_t m4[G::KB][4];
+  float mx[G::NT];
+  bool any = false;
+
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int f = 0; f < RA; ++f)
+    fb[f] = *reinterpret_cast<const u32x4_t *>(kbase + (f % G::KB) * 32 * G::KROW + 32 * (f / G::KB));
+  if constexpr (HAS_MASK) {
 #pragma unroll
     for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) mloc = __builtin_fmaxf(mloc, __builtin_fmaxf(s[nt][kb][v], s[nt][kb][v + 1]));
-    mloc = pair_max(mloc);
-    mx[nt] = HAS_MASK ? mloc : mloc * c;  // -inf * c = -inf (c > 0)
+      for (int r4 = 0; r4 < 4; ++r4) m4[kb][r4] = *reinterpret_cast<const f32x4_t *>(mk + kb * 32 + r4 * 8 + 4 * h);
   }
+  __builtin_amdgcn_sched_barrier(0);
 
-  // Lazy rescale: the reference max m of a row only moves when the tile max
-  // exceeds it by more than kTau (log2 units), so p = 2^(s - m) <= 2^kTau and
-  // the O/l rescale (a VALU pass over every accumulator) is rare.  Exact: the
-  // final O/l uses one consistent reference per row.
-  bool grow = false;
 #pragma unroll
-  for (int nt = 0; nt < G::NT; ++nt) grow |= mx[nt] > ws.m[nt] + kTau;
-  if (__ballot(grow) != 0) {
-#pragma unroll
-    for (int nt = 0; nt < G::NT; ++nt) {
-      const float m_new = fmaxf(ws.m[nt], mx[nt]);
-      const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(ws.m[nt] - m_new);
-      ws.m[nt] = m_new;
-      ws.l[nt] *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] *= alpha;
-    }
-  }
-
-  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
-  u32x4_t pb[G::NT][G::KB][2];
-#pragma unroll
-  for (int nt = 0; nt < G::NT; ++nt) {
-    const float m_use = ws.m[nt] == -INFINITY ? 0.0f : ws.m[nt];
-    float lsum = ws.l[nt];
-#pragma unroll
-    for (int kb = 0; kb < G::KB; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        s[nt][kb][v] = HAS_MASK ? fast_exp2(s[nt][kb][v] - m_use) : fast_exp2(__builtin_fmaf(s[nt][kb][v], c, -m_use));
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // bit-cast plain scalars, never ext-vector elements: hipcc folded a
-        // bit_cast of pb[..][i] to element 0 for every i
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w[i] = pack_bf16(s[nt][kb][8 * kk + 2 * i], s[nt][kb][8 * kk + 2 * i + 1]);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), ones, lsum, false);
-        }
-        pb[nt][kb][kk] = u32x4_t{w[0], w[1], w[2], w[3]};
-      }
-    }
-    ws.l[nt] = lsum;
-  }
-
-  // PV: fragment f = (kb*2 + kk)*MT + mt, same read-ahead ordering.  The A
-  // fragment (d rows mt*32 + l32, k-slots j = 0..7 of lane-half h) must hold
-  // the keys that P's B fragment holds: kb*32 + 16kk + 8(j/4) + 4h + j%4.  Two
-  // transposing reads (t = j/4) fetch it: in 16-lane group g the reading lane
-  // 4m + j names the 8 bytes V[kb*32 + 16kk + 8t + 4h + j][mt*32 + 16(g%2) + 4m ..],
-  // and output lane 16g + 4m + c receives element c of those four rows.
-  {
-    constexpr int NF = G::KB * 2 * G::MT, RA = G::GRP < NF ? G::GRP : NF;
-    const int vlane = (4 * h + ((lane >> 2) & 3)) * G::VROW + (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4_t fb[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int mt = f % G::MT, kk = (f / G::MT) % 2, kb = f / (2 * G::MT);
-      const char *p = vt + vlane + (kb * 32 + kk * 16) * G::VROW + mt * 64;
-      const u32x2_t a0 = lds_read_tr16(p), a1 = lds_read_tr16(p + 8 * G::VROW);
-      fb[f] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int mt = f % G::MT, kk = (f / G::MT) % 2, kb = f / (2 * G::MT);
+  for (int f = 0; f < G::NFQ; ++f) {
+    {
+      const int kb = f % G::KB, sd = f / G::KB;
+      pin_in(fb[f]);
 #pragma unroll
       for (int nt = 0; nt < G::NT; ++nt)
-        ws.o[nt][mt] = mfma32(as_bf16x8(fb[f]), as_bf16x8(pb[nt][kb][kk]), ws.o[nt][mt]);
+        sn[nt][kb] = mfma32(as_bf16x8(fb[f]), as_bf16x8(qf[nt][sd]), sd == 0 ? f32x16_t{} : sn[nt][kb]);
+      if (f + RA < G::NFQ) {
+        const int g = f + RA;
+        fb[g] = *reinterpret_cast<const u32x4_t *>(kbase + (g % G::KB) * 32 * G::KROW + 32 * (g / G::KB));
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (f == 0) {
+      // scores into log2 units (mask path) and the in-lane row max
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      __builtin_amdgcn_sched_group_barrier(0x008, G::NT, 0);
-      if (f + RA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int nt = 0; nt < G::NT; ++nt) {
+        if constexpr (HAS_MASK) {
+#pragma unroll
+          for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {  // removed keys stay -inf whatever their K holds
+              const float mv = m4[kb][v / 4][v % 4];
+              s[nt][kb][v] = mv == -INFINITY ? -INFINITY : __builtin_fmaf(s[nt][kb][v], c, mv);
+            }
+        }
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; v += 2)
+            mloc = __builtin_fmaxf(mloc, __builtin_fmaxf(s[nt][kb][v], s[nt][kb][v + 1]));
+        mx[nt] = mloc;
+        pin_out(mx[nt]);
+      }
+    } else if (f == 1) {
+      bool grow = false;
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt) {
+        const float m2 = pair_max(mx[nt]);
+        mx[nt] = HAS_MASK ? m2 : m2 * c;  // -inf * c = -inf (c > 0)
+        grow |= mx[nt] > ws.m[nt] + kTau;
+      }
+      any = __ballot(grow) != 0;
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt) {
+        const float m_new = any ? fmaxf(ws.m[nt], mx[nt]) : ws.m[nt];
+        alpha[nt] = m_new == -INFINITY ? 1.0f : fast_exp2(ws.m[nt] - m_new);
+        ws.m[nt] = m_new;
+        pc.m_use[nt] = m_new == -INFINITY ? 0.0f : m_new;
+        pc.lsum[nt] = ws.l[nt] * alpha[nt];
+        pin_out(pc.m_use[nt]);
+        pin_out(pc.lsum[nt]);
+        pin_out(alpha[nt]);
+      }
+    } else {
+      const int p0 = (f - 2) * PPS, p1 = (f - 1) * PPS < NP ? (f - 1) * PPS : NP;
+      if (p0 < p1) p_pairs<G, HAS_MASK>(pc, s, 0, p0, p1, c);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  return any;
 }
 
-// The pipelined key loop shared by both kernels.  PF register stages keep
-// the global loads of the next PF tiles in flight while a tile is computed
-// from one LDS stage and the next is written to the other.  The iteration
-// count is padded to a multiple of PF (padding tiles are all-masked zeros),
-// so the body unrolls over the register stages with static indices and the
-// accumulators never meet a branch.  Returns with the LDS free (barrier
-// passed).
+// Phase B: O^T += V^T P^T for one tile.  Its first slots compute the second
+// half of P (needed from PV MFMA MT on), the next ones the staging work of the
+// tile step (`work(k)`, k = 0, 1, 2).  The A fragment (d rows mt*32 + lane%32,
+// k-slots j = 0..7 of lane-half h) must hold the keys P's B fragment holds:
+// kb*32 + 16kk + 8(j/4) + 4h + j%4.  Two transposing reads (t = j/4) fetch
+// it: in 16-lane group g the reading lane 4m + j names the 8 bytes
+// V[kb*32 + 16kk + 8t + 4h + j][mt*32 + 16(g%2) + 4m ..], and output lane
+// 16g + 4m + c receives element c of those four rows.  Row bases are
+// multiples of 4, so v_row(base + j) = v_row(base) + v_row(j).
+template <class G, bool HAS_MASK, class Work>
+__device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f32x16_t (&s)[G::NT][G::KB],
+                                        float c, const char *vt, int lane, Work &&work) {
+  constexpr int RA = G::GRP < G::NFV ? G::GRP : G::NFV;
+  constexpr int NP = G::NT * G::KB * 4;                 // P pairs of the second half
+  constexpr int PPS = (NP + G::MT - 1) / G::MT;          // spread over the first MT slots
+  constexpr int PSLOTS = (NP + PPS - 1) / PPS;
+  const int h = lane >> 5, j = (lane >> 2) & 3, m = lane & 3, g2 = (lane >> 4) & 1;
+  const char *vbase = vt + G::v_row(4 * h) + G::v_row(j) + 32 * g2 + 8 * m;
+  u32x4_t fb[G::NFV];
+  auto read = [&](int q) {
+    const int mt = q % G::MT, kk = (q / G::MT) % 2, kb = q / (2 * G::MT);
+    const char *p = vbase + G::v_row(kb * 32 + kk * 16) + 64 * mt;
+    const u32x2_t a0 = lds_read_tr16(p), a1 = lds_read_tr16(p + G::v_row(8));
+    fb[q] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+  };
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < RA; ++q) read(q);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < G::NFV; ++q) {
+    const int mt = q % G::MT, kk = (q / G::MT) % 2, kb = q / (2 * G::MT);
+    pin_in(fb[q]);
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) ws.o[nt][mt] = mfma32(as_bf16x8(fb[q]), as_bf16x8(p_frag(pc, nt, kb, kk)), ws.o[nt][mt]);
+    if (q + RA < G::NFV) read(q + RA);
+    __builtin_amdgcn_sched_barrier(0);
+    if (q < PSLOTS) {
+      p_pairs<G, HAS_MASK>(pc, s, 1, q * PPS, (q + 1) * PPS < NP ? (q + 1) * PPS : NP, c);
+    } else {
+      const int k = q - PSLOTS;
+      if (k <= 2) work(k);
+      if (q == G::NFV - 1)  // fewer slots than work items: the rest goes here
+        for (int r = k + 1; r <= 2; ++r) work(r);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) ws.l[nt] = pc.lsum[nt];
+}
+
+// ------------------------------------------------------------------ core loop
+
+// The pipelined key loop shared by both kernels.  LDS holds two K buffers and
+// two V buffers; iteration `it` (every split's tile `it`) reads K(it+1) and
+// V(it), writes K(it+2) into the K buffer K(it) used and V(it+1) into the
+// other V buffer, and issues the global loads of K(it+3) and V(it+2) into the
+// register stage.  Tiles past the last one read as zeros and are fully
+// masked (p = 0).  Returns with the LDS free (barrier passed).
 template <class G, bool HAS_MASK, class Src>
 __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, const u32x4_t (&qf)[G::NT][G::SD],
-                                           char *smem, float c, const float *mask) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sp = wave / G::RG;
+                                           char *smem, float c) {
+  const unsigned tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int sp = __builtin_amdgcn_readfirstlane((int)(tid >> 6)) / G::RG;
   const int n_tiles = (src.n_keys + G::BN - 1) / G::BN;
   const int n_iter = (n_tiles + G::NSPLIT - 1) / G::NSPLIT;
-  const int n_pad = (n_iter + G::PF - 1) / G::PF * G::PF;
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
     ws.m[nt] = -INFINITY;
@@ -426,29 +599,61 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
   }
   if (n_iter <= 0) return;
 
-  typename Src::Stage st[G::PF];
-#pragma unroll
-  for (int u = 0; u < G::PF; ++u) src.load(st[u], u, src.tile_base(u), tid);
-  int64_t next_base = src.tile_base(G::PF);  // address base of the next tile to load, looked up one tile early
-  src.store(st[0], smem, tid);
+  char *const kbuf = smem, *const vbuf = smem + 2 * G::KSLOT;
+  typename Src::Stage st;
+  const int64_t b0 = src.tile_base(0), b1 = src.tile_base(1);
+  src.load_k(st, 0, b0, tid);
+  src.load_v(st, 0, b0, tid);
+  src.store_k(st, kbuf, tid);
+  src.store_v(st, vbuf, 0, tid);
+  src.load_k(st, 1, b1, tid);
+  src.store_k(st, kbuf + G::KSLOT, tid);
+  int64_t bv = src.tile_base(2);  // V(it+2) base
+  src.load_k(st, 2, bv, tid);
+  src.load_v(st, 1, b1, tid);
+  int64_t bk = src.tile_base(3);  // K(it+3) base
   __syncthreads();
-  for (int it0 = 0; it0 < n_pad; it0 += G::PF) {
+
+  f32x16_t s[G::NT][G::KB];
+  qk_tile<G>(s, qf, kbuf + sp * G::KTILE, lane);
+  if constexpr (!HAS_MASK) mask_tail<G>(s, sp * G::BN, src.n_keys, lane);
+
+  for (int it = 0; it < n_iter; ++it) {
+    const int cur = it & 1;
+    char *const kcur = kbuf + cur * G::KSLOT, *const knext = kbuf + (cur ^ 1) * G::KSLOT;
+    char *const vcur = vbuf + cur * G::VSLOT, *const vnext = vbuf + (cur ^ 1) * G::VSLOT;
+
+    f32x16_t sn[G::NT][G::KB];
+    PCarry<G> pc;
+    float alpha[G::NT];
+    const bool any =
+        phase_a<G, HAS_MASK>(ws, pc, sn, s, alpha, qf, knext + sp * G::KTILE,
+                             reinterpret_cast<const float *>(vcur + G::NSPLIT * G::VTILE) + sp * G::BN, c, lane);
+    if (any) {
 #pragma unroll
-    for (int u = 0; u < G::PF; ++u) {
-      const int it = it0 + u;
-      // register stage u held tile `it`, already written to LDS: refill it
-      if (it + G::PF < n_pad) {
-        src.load(st[u], it + G::PF, next_base, tid);
-        next_base = src.tile_base(it + G::PF + 1);
-      }
-      // A split whose tile index runs past the last tile computes on an
-      // all-zero, fully masked tile (p = 0).
-      const int ti = it * G::NSPLIT + sp;
-      const char *base = smem + (it & 1) * G::STAGE + sp * G::SPLIT_BYTES;
-      compute_tile<G, HAS_MASK>(ws, qf, base, base + G::KT, ti * G::BN, src.n_keys, c, mask, lane);
-      if (it + 1 < n_pad) src.store(st[(u + 1) % G::PF], smem + ((it + 1) & 1) * G::STAGE, tid);
-      __syncthreads();
+      for (int nt = 0; nt < G::NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] *= alpha[nt];
     }
+
+    // PV(it); stage K(it+2) and V(it+1); issue K(it+3) and V(it+2)
+    phase_b<G, HAS_MASK>(ws, pc, s, c, vcur + sp * G::VTILE, lane, [&](int k) {
+      if (k == 0) src.store_k(st, kcur, tid);
+      if (k == 1) src.store_v(st, vnext, it + 1, tid);
+      if (k == 2) {
+        src.load_k(st, it + 3, bk, tid);
+        src.load_v(st, it + 2, bv, tid);
+        bv = bk;
+        bk = src.tile_base(it + 4);
+      }
+    });
+    __syncthreads();
+
+    if constexpr (!HAS_MASK) mask_tail<G>(sn, ((it + 1) * G::NSPLIT + sp) * G::BN, src.n_keys, lane);
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt)
+#pragma unroll
+      for (int kb = 0; kb < G::KB; ++kb) s[nt][kb] = sn[nt][kb];
   }
 }
 
@@ -553,19 +758,18 @@ void encoder_fwd_kernel(EncoderLaunch a) {
     }
   }
 
-  EncSrc<G, F32IN> src;
+  EncSrc<G, F32IN, HAS_MASK> src;
   src.kb = reinterpret_cast<const char *>(a.k) + (b * a.ks[0] + h * a.ks[1]) * ES;
   src.vb = reinterpret_cast<const char *>(a.v) + (b * a.vs[0] + h * a.vs[1]) * ES;
-  src.ks = a.ks[2];
-  src.vs = a.vs[2];
+  src.krow = (uint32_t)(a.ks[2] * ES);
+  src.vrow = (uint32_t)(a.vs[2] * ES);
   src.kstep = (int64_t)G::NSPLIT * G::BN * a.ks[2] * ES;
   src.vstep = (int64_t)G::NSPLIT * G::BN * a.vs[2] * ES;
   src.n_keys = a.Skv;
-  const float *mask = HAS_MASK ? a.mask + b * a.mask_sb : nullptr;
-  src.mask = mask;
+  src.mask = HAS_MASK ? a.mask + b * a.mask_sb : nullptr;
 
   WaveState<G> ws;
-  flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c, mask);
+  flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c);
   merge_splits<G>(ws, smem);
   if (sp != 0) return;
 
@@ -639,7 +843,7 @@ void prefill_paged_kernel(PrefillLaunch a) {
   src.n_keys = a.L_act;
 
   WaveState<G> ws;
-  flash_loop<G, false>(ws, src, qf, smem, a.c, nullptr);
+  flash_loop<G, false>(ws, src, qf, smem, a.c);
 
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
@@ -662,9 +866,10 @@ void prefill_paged_kernel(PrefillLaunch a) {
 
 // ------------------------------------------------------------------ launchers
 
-using EncGeo = Geo<64, 64, 1, 4, 2, 4, 2>;     // BM 128, 8 waves, 2 key splits, 2 tiles in flight
-using EncGeoF32 = Geo<64, 64, 1, 4, 2, 4, 1>;  // fp32 inputs: twice the staging registers per tile
-using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 1>;   // BM 256, 8 waves of 32 rows, 2 waves per SIMD
+using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4>;      // BM 128, 8 waves: 4 row groups x 2 key splits, 32-key tiles, 4 waves/SIMD
+using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2>;  // masked: mask values held in registers, 2 waves/SIMD
+using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2>;   // fp32 inputs: twice the staging registers per tile
+using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2>;    // BM 256, 8 waves of 32 rows, 2 waves per SIMD
 
 // Launch with G::LDS bytes of dynamic LDS; kernels above 64 KiB are opted in
 // once per process (hipFuncSetAttribute is per function, not per device).
@@ -683,10 +888,11 @@ hipError_t launch_encoder(const EncoderLaunch &a, bool f32_in, hipStream_t strea
   const int n_qt = (a.Sq + EncGeo::BM - 1) / EncGeo::BM;
   const dim3 grid(n_qt * a.H * a.B);
   static_assert(EncGeo::BM == EncGeoF32::BM && EncGeo::THREADS == EncGeoF32::THREADS, "same launch shape");
+  static_assert(EncGeo::BM == EncGeoMask::BM && EncGeo::THREADS == EncGeoMask::THREADS, "same launch shape");
   if (f32_in)
     return a.mask ? launch_lds<EncGeoF32>(encoder_fwd_kernel<EncGeoF32, true, true>, grid, a, stream)
                   : launch_lds<EncGeoF32>(encoder_fwd_kernel<EncGeoF32, true, false>, grid, a, stream);
-  return a.mask ? launch_lds<EncGeo>(encoder_fwd_kernel<EncGeo, false, true>, grid, a, stream)
+  return a.mask ? launch_lds<EncGeoMask>(encoder_fwd_kernel<EncGeoMask, false, true>, grid, a, stream)
                 : launch_lds<EncGeo>(encoder_fwd_kernel<EncGeo, false, false>, grid, a, stream);
 }
 
