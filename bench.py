@@ -109,6 +109,79 @@ def cpu_baseline(pre, n_rows: int):
                       f"(fp64 C oracle incl. KV decode), {dt:.1f} s wall"}
 
 
+def _short(name: str) -> str:
+    """Kernel family name from a demangled rocprofv3 kernel name."""
+    for k in ("prefill_paged_kernel", "encoder_fwd_kernel", "res_ln_kernel", "decode_split_kernel",
+              "decode_combine_kernel", "copyBuffer"):
+        if k in name:
+            return k
+    return None
+
+
+def summarize(prof_dir: str) -> None:
+    """Turn the rocprofv3 CSV output of the profiling commands (kernel trace in
+    <dir>/trace, FETCH_SIZE / WRITE_SIZE passes of the bench in <dir>/<C> and of
+    --copy-calibration in <dir>/<C>_copy) into profiles/traffic.json, and print
+    the per-kernel duration and traffic tables.  Reads CSV only; no GPU."""
+    import csv
+    import glob
+
+    def one(pattern):
+        hits = sorted(glob.glob(os.path.join(prof_dir, pattern)))
+        if not hits:
+            raise SystemExit(f"summarize: no {pattern} under {prof_dir}")
+        return hits[0]
+
+    def per_dispatch(path):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        fam = {}
+        for (_, name), v in vals.items():
+            if _short(name):
+                fam.setdefault(_short(name), []).append(v)
+        return {k: statistics.fmean(v) for k, v in fam.items()}
+
+    stats = {}
+    for r in csv.DictReader(open(one("trace/*kernel_stats.csv"))):
+        if not _short(r["Name"]):  # not one of this library's kernels (e.g. the cache flush)
+            continue
+        stats[_short(r["Name"])] = {"kernel": r["Name"], "calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
+                                    "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        kib = per_dispatch(one(f"{c}_copy/*counter_collection.csv"))["copyBuffer"]
+        cal[c] = kib * 1024 / COPY_BYTES
+    fetch = per_dispatch(one("FETCH_SIZE/*counter_collection.csv"))
+    write = per_dispatch(one("WRITE_SIZE/*counter_collection.csv"))
+    kernels = {}
+    for k, st in stats.items():
+        if k == "copyBuffer" or k not in fetch or k not in write:
+            continue
+        kernels[k] = {"kernel": st["kernel"], "fetch_kib_raw": fetch[k], "write_kib_raw": write[k],
+                      "hbm_bytes_per_launch": int(fetch[k] * 1024 / cal["FETCH_SIZE"] + write[k] * 1024 / cal["WRITE_SIZE"]),
+                      "avg_duration_ns": st["avg_ns"]}
+    out = {"source_hash": kernel_source_hash(),
+           "note": "rocprofv3 FETCH_SIZE/WRITE_SIZE (KiB per dispatch, L2 <-> memory fabric) divided by the ratio "
+                   "the same counter reads for a 1 GiB device copy",
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_ratio": cal["FETCH_SIZE"], "write_ratio": cal["WRITE_SIZE"]},
+           "kernels": kernels}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(f"wrote {path} (sources {out['source_hash']}; copy calibration fetch x{cal['FETCH_SIZE']:.4f}, "
+          f"write x{cal['WRITE_SIZE']:.4f})")
+    print("\n| kernel | calls | avg (us) | min (us) | max (us) |\n|---|---|---|---|---|")
+    for k, st in sorted(stats.items(), key=lambda kv: -kv[1]["avg_ns"] * kv[1]["calls"]):
+        print(f"| `{st['kernel']}` | {st['calls']} | {st['avg_ns'] / 1e3:.2f} | {st['min_ns'] / 1e3:.2f} | "
+              f"{st['max_ns'] / 1e3:.2f} |")
+    print("\n| kernel | FETCH_SIZE raw (KiB) | WRITE_SIZE raw (KiB) | scaled bytes / launch |\n|---|---|---|---|")
+    for k, v in kernels.items():
+        print(f"| {k} | {v['fetch_kib_raw']:.1f} | {v['write_kib_raw']:.1f} | {v['hbm_bytes_per_launch'] / 1e6:.1f} MB |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,7 +193,12 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (scales the rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="no GPU: write profiles/traffic.json and print tables from rocprofv3 CSV output in DIR")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, device="cuda:0")
         dst = torch.empty_like(src)
@@ -159,6 +237,9 @@ def main():
 
     p_q, p_k, p_v, p_bt = (t.to(dev) for t in (pre.q, pre.k_cache, pre.v_cache, pre.block_table))
     p_out = torch.empty_like(p_q)
+    # 512 MiB written before every decode call (outside its timer), so its
+    # ~134 MB of K/V come from HBM and not from the 256 MB Infinity Cache
+    flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
     torch.cuda.synchronize()
 
     t_enc, t_dec, t_pre = Timer(), Timer(), Timer()
@@ -174,6 +255,7 @@ def main():
             if timed:
                 t_enc.stop(s)
         if run_dec:
+            flush.zero_()
             s = t_dec.start() if timed else None
             taa.attn_decode_gqa(d_q, d_k, d_v, d_m, dec.scale, dec.G, out=d_out, workspace=d_ws)
             if timed:

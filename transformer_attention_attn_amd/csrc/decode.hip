@@ -6,15 +6,18 @@
 // "Perf caveat" and "Future performance follow-on" note that one program
 // re-streaming the whole cache is bandwidth-starved and that the KV stream
 // should be sharded over many programs.  Here every (batch, KV head, chunk of
-// 128 keys) is its own workgroup, the G query heads of a KV head share the
+// 64 keys) is its own workgroup, the G query heads of a KV head share the
 // one pass over its K/V, and a second kernel merges the chunk partials.
 //
-// Split kernel, per workgroup (4 waves, 32 keys each as 2 rounds of 16):
+// Split kernel, per workgroup (4 waves of kDecNG groups of 16 keys; with more
+// than one group the loads of group g+1 are in flight while group g is
+// computed, and an online softmax runs across the groups):
 //   QK^T : v_mfma_f32_16x16x32_bf16 with the 16 keys on M and the G query
 //          heads on N (padded to 16), K streamed straight from HBM into the
 //          A operand (64 contiguous bytes per key per load);
-//   mask : additive, in log2 units; a round whose 16 mask entries are all
-//          -inf issues no K/V loads, a chunk with no live key exits at once;
+//   mask : additive, in log2 units; keys it removes are never fetched (their
+//          buffer offsets fall out of range), a wave with no live key skips
+//          the loads;
 //   PV   : on the VALU, each lane owning 4 of the 256 output columns, V read
 //          with 512 contiguous bytes per key per wave;
 //   merge: the 4 wave partials combine through LDS; the chunk partial
@@ -27,29 +30,98 @@
 namespace mi355 {
 
 constexpr int kDecD = 256;
-constexpr int kDecChunk = 128;  // keys per workgroup
-constexpr int kDecGmax = 8;     // query heads per KV head supported
+constexpr int kDecKW = 16;                      // keys per group (one 16-key MFMA block)
+constexpr int kDecNG = 1;                       // groups per wave
+constexpr int kDecWaves = 4;                    // waves per workgroup
+constexpr int kDecChunk = kDecWaves * kDecNG * kDecKW;  // keys per workgroup
+constexpr int kDecGmax = 8;                     // query heads per KV head supported
+constexpr uint32_t kOOB = 0x80000000u;          // buffer offset past any range: the load returns zeros
+// K and V are read exactly once: non-temporal loads (cache policy "nt").  On
+// this part they stream at about twice the rate of default-policy loads.
+constexpr int kNT = 2;
+
+// Raw buffer resource over [base, base + bytes) (uniform arguments; see the
+// flash kernels for why readfirstlane).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dec_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p), hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// One group of 16 keys in registers: K as the A operand of the QK MFMA
+// (lane l: key l%16, d = 32s + 8(l/16) .. +7) and V as 16 rows of the lane's
+// 4 output columns.
+struct DecStage {
+  u32x4_t k[kDecD / 32];
+  u32x2_t v[kDecKW];
+};
+
+// Issue the loads of group g (keys g*16 .. g*16+15 of the wave); keys the
+// mask removes get an out-of-range offset and are never fetched.
+__device__ __forceinline__ void dec_load(DecStage &st, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                         uint64_t live, int g, int lane) {
+  const int gq = lane & 15, quad = lane >> 4;
+  const int kk = g * kDecKW + gq;
+  const uint32_t koff = ((live >> kk) & 1) ? kk * (kDecD * 2) + 16 * quad : kOOB;
+#pragma unroll
+  for (int s = 0; s < kDecD / 32; ++s)
+    st.k[s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * s, 0, kNT));
+#pragma unroll
+  for (int j = 0; j < kDecKW; ++j) {
+    const int kj = g * kDecKW + j;
+    const uint32_t voff = ((live >> kj) & 1) ? kj * (kDecD * 2) + 8 * lane : kOOB;
+    st.v[j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 0, kNT));
+  }
+}
 
 template <int G>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeLaunch a) {
-  constexpr int KW = kDecChunk / 4;  // keys per wave (two MFMA groups of 16)
-  __shared__ __attribute__((aligned(16))) float sc[4][G][KW];
-  __shared__ __attribute__((aligned(16))) float red_o[4][G][kDecD];
-  __shared__ float red_ml[4][G][2];
+__global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecodeLaunch a) {
+  constexpr int KW = kDecKW, NW = kDecWaves, NG = kDecNG, WK = NG * KW;  // WK: keys per wave
+  static_assert(WK <= 64, "one liveness bit per lane");
+  __shared__ __attribute__((aligned(16))) float sc[NW][G][KW];
+  __shared__ __attribute__((aligned(16))) float red_o[NW][G][kDecD];
+  __shared__ float red_ml[NW][G][2];
 
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *mrow = a.mask ? a.mask + (int64_t)b * a.S_ctx : nullptr;
   const int64_t part0 = ((int64_t)b * a.Hq + (int64_t)kvh * G) * a.n_chunks + chunk;  // head g adds g*n_chunks
-  const int key0 = chunk * kDecChunk + wave * KW;
+  const int key0 = chunk * kDecChunk + wave * WK;
 
-  // Liveness of this wave's 32 keys (one mask read per lane, then a vote).
-  bool kl = false;
-  if (lane < KW) {
-    const int key = key0 + lane;
-    kl = key < a.S_ctx && (mrow == nullptr || mrow[key] != -INFINITY);
+  // Every wave reads the mask of the whole chunk (lane l: key l of the chunk,
+  // log2 units, -inf where removed) and votes: a chunk with no live key
+  // writes its empty statistics and exits without touching K/V or the LDS.
+  static_assert(kDecChunk <= 64, "one chunk key per lane");
+  float mk_lane = -INFINITY;
+  if (lane < kDecChunk) {
+    const int key = chunk * kDecChunk + lane;
+    const float mv = key < a.S_ctx ? (mrow ? mrow[key] : 0.0f) : -INFINITY;
+    mk_lane = mv == -INFINITY ? -INFINITY : mv * kLog2e;
   }
-  const uint64_t live = __ballot(kl);
+  const uint64_t live_chunk = __ballot(mk_lane != -INFINITY);
+  if (live_chunk == 0) {
+    if (tid < G) {
+      const int64_t part = part0 + (int64_t)tid * a.n_chunks;
+      a.ws_ml[part * 2 + 0] = -INFINITY;
+      a.ws_ml[part * 2 + 1] = 0.0f;
+    }
+    return;
+  }
+  const uint64_t live = (live_chunk >> (wave * WK)) & ((WK == 64) ? ~0ull : ((1ull << WK) - 1));
+
+  // q^T as the B operand: lane l holds q[g = l%16][32s + 8(l/16) .. +7], zero
+  // for g >= G (those lanes fetch nothing: out-of-range offset).  Issued
+  // before the liveness vote is used, so its latency overlaps the mask read.
+  const int gq = lane & 15, quad = lane >> 4;
+  u32x4_t qf[kDecD / 32];
+  {
+    const auto rq = dec_rsrc(a.q + ((int64_t)b * a.Hq + (int64_t)kvh * G) * kDecD, G * kDecD * 2);
+    const uint32_t qoff = gq < G ? gq * (kDecD * 2) + 16 * quad : kOOB;
+#pragma unroll
+    for (int s = 0; s < kDecD / 32; ++s)
+      qf[s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * s, 0, 0));
+  }
 
   float m[G], l[G];
   f32x4_t o[G];
@@ -61,85 +133,66 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeLaunch a) {
   }
 
   if (live != 0) {
-    const int gq = lane & 15, quad = lane >> 4;
-    const int64_t kv_off = ((int64_t)b * a.Hkv + kvh) * a.S_ctx * kDecD;
-    const __bf16 *kbase = a.k + kv_off;
-    const __bf16 *vbase = a.v + kv_off;
-    // All K/V loads of the wave go out together; dead keys are not loaded.
-    u32x4_t kf[2][kDecD / 32];
-#pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      const bool kin = (live >> (grp * 16 + gq)) & 1;
-#pragma unroll
-      for (int s = 0; s < kDecD / 32; ++s)
-        kf[grp][s] = kin ? ldg<u32x4_t>(kbase + (int64_t)(key0 + grp * 16 + gq) * kDecD + 32 * s + 8 * quad)
-                         : u32x4_t{0, 0, 0, 0};
-    }
-    u32x2_t vf[KW];
-#pragma unroll
-    for (int j = 0; j < KW; ++j)
-      vf[j] = ((live >> j) & 1) ? ldg<u32x2_t>(vbase + (int64_t)(key0 + j) * kDecD + 4 * lane) : u32x2_t{0, 0};
-    // q^T as the B operand: lane l holds q[g = l%16][32s + 8(l/16) .. +7], zero for g >= G.
-    u32x4_t qf[kDecD / 32];
-    const __bf16 *qrow = a.q + ((int64_t)b * a.Hq + (int64_t)kvh * G + gq) * kDecD;
-#pragma unroll
-    for (int s = 0; s < kDecD / 32; ++s)
-      qf[s] = gq < G ? ldg<u32x4_t>(qrow + 32 * s + 8 * quad) : u32x4_t{0, 0, 0, 0};
+    const int64_t row0 = ((int64_t)b * a.Hkv + kvh) * a.S_ctx + key0;
+    const uint32_t span = (uint32_t)max(min(WK, a.S_ctx - key0), 0) * (kDecD * 2);
+    const auto rk = dec_rsrc(a.k + row0 * kDecD, span), rv = dec_rsrc(a.v + row0 * kDecD, span);
+    DecStage st[NG < 2 ? 1 : 2];
+    dec_load(st[0], rk, rv, live, 0, lane);
 
 #pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
+    for (int grp = 0; grp < NG; ++grp) {
+      if (grp + 1 < NG) dec_load(st[(grp + 1) & 1], rk, rv, live, grp + 1, lane);
+      const DecStage &cs = st[NG < 2 ? 0 : grp & 1];
       f32x4_t s4 = {0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < kDecD / 32; ++s) s4 = mfma16(as_bf16x8(kf[grp][s]), as_bf16x8(qf[s]), s4);
-      // lane l holds S^T[key = grp*16 + 4*(l/16) + i][head g = l%16]
-      if (gq < G) {
-        f32x4_t x;
+      for (int s = 0; s < kDecD / 32; ++s) s4 = mfma16(as_bf16x8(cs.k[s]), as_bf16x8(qf[s]), s4);
+      // lane l holds S^T[key = 4*(l/16) + i][head g = l%16]: scale, mask, to LDS
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kj = grp * 16 + 4 * quad + i;
-          const float mk = ((live >> kj) & 1) ? (mrow ? mrow[key0 + kj] : 0.0f) : -INFINITY;
-          x[i] = mk == -INFINITY ? -INFINITY : s4[i] * a.c + mk * kLog2e;
+      for (int i = 0; i < 4; ++i) {
+        const float mv = __shfl(mk_lane, wave * WK + grp * KW + 4 * quad + i);
+        s4[i] = mv == -INFINITY ? -INFINITY : __builtin_fmaf(s4[i], a.c, mv);
+      }
+      if (gq < G) *reinterpret_cast<f32x4_t *>(&sc[wave][gq][4 * quad]) = s4;
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+      // online softmax over the group for each head, PV on the VALU
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float p[KW];
+#pragma unroll
+        for (int q4 = 0; q4 < KW / 4; ++q4) {
+          const f32x4_t t = *reinterpret_cast<const f32x4_t *>(&sc[wave][g][4 * q4]);
+          p[4 * q4 + 0] = t[0];
+          p[4 * q4 + 1] = t[1];
+          p[4 * q4 + 2] = t[2];
+          p[4 * q4 + 3] = t[3];
         }
-        *reinterpret_cast<f32x4_t *>(&sc[wave][gq][grp * 16 + 4 * quad]) = x;
+        float mg = p[0];
+#pragma unroll
+        for (int j = 1; j < KW; ++j) mg = fmaxf(mg, p[j]);
+        const float m_new = fmaxf(m[g], mg);
+        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m[g] - m_new);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        m[g] = m_new;
+        float ls = l[g] * alpha;
+        f32x4_t acc = o[g] * alpha;
+#pragma unroll
+        for (int j = 0; j < KW; ++j) {
+          const float pj = fast_exp2(p[j] - m_use);
+          ls += pj;
+          acc[0] += pj * bf16_lo(cs.v[j][0]);
+          acc[1] += pj * bf16_hi(cs.v[j][0]);
+          acc[2] += pj * bf16_lo(cs.v[j][1]);
+          acc[3] += pj * bf16_hi(cs.v[j][1]);
+        }
+        l[g] = ls;
+        o[g] = acc;
       }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-
-    // Softmax over the wave's 32 keys for each head, then PV on the VALU.
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float p[KW];
-#pragma unroll
-      for (int q4 = 0; q4 < KW / 4; ++q4) {
-        const f32x4_t t = *reinterpret_cast<const f32x4_t *>(&sc[wave][g][4 * q4]);
-        p[4 * q4 + 0] = t[0];
-        p[4 * q4 + 1] = t[1];
-        p[4 * q4 + 2] = t[2];
-        p[4 * q4 + 3] = t[3];
-      }
-      float mr = p[0];
-#pragma unroll
-      for (int j = 1; j < KW; ++j) mr = fmaxf(mr, p[j]);
-      m[g] = mr;
-      const float m_use = mr == -INFINITY ? 0.0f : mr;
-      float ls = 0.0f;
-      f32x4_t acc = {0, 0, 0, 0};
-#pragma unroll
-      for (int j = 0; j < KW; ++j) {
-        const float pj = fast_exp2(p[j] - m_use);
-        ls += pj;
-        acc[0] += pj * bf16_lo(vf[j][0]);
-        acc[1] += pj * bf16_hi(vf[j][0]);
-        acc[2] += pj * bf16_lo(vf[j][1]);
-        acc[3] += pj * bf16_hi(vf[j][1]);
-      }
-      l[g] = ls;
-      o[g] = acc;
+      __builtin_amdgcn_wave_barrier();  // sc is rewritten by the next group
     }
   }
 
-  // Merge the 4 waves' partials (fixed order) and write the chunk partial.
+  // Merge the wave partials (fixed order) and write the chunk partial.
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     *reinterpret_cast<f32x4_t *>(&red_o[wave][g][4 * lane]) = o[g];
@@ -149,41 +202,47 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeLaunch a) {
     }
   }
   __syncthreads();
-  // thread tid handles column tid of every head
+  // thread t handles column t % D of heads t / D, t / D + NW*64/D, ...
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int g0 = 0; g0 < G; g0 += 64 * NW / kDecD) {
+    const int g = g0 + tid / kDecD, col = tid % kDecD;
+    if (g >= G) break;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_ml[w][g][0]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red_ml[w][g][0]);
     const float Mu = M == -INFINITY ? 0.0f : M;
     float L = 0.0f, acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float sw = fast_exp2(red_ml[w][g][0] - Mu);
       L += red_ml[w][g][1] * sw;
-      acc += red_o[w][g][tid] * sw;
+      acc += red_o[w][g][col] * sw;
     }
     const int64_t part = part0 + (int64_t)g * a.n_chunks;
-    if (M != -INFINITY) a.ws_o[part * kDecD + tid] = acc;
-    if (tid == 0) {
+    if (M != -INFINITY) a.ws_o[part * kDecD + col] = acc;
+    if (col == 0) {
       a.ws_ml[part * 2 + 0] = M;
       a.ws_ml[part * 2 + 1] = L;
     }
   }
 }
 
-// One workgroup per (batch, query head); thread d owns output column d.  The
-// chunk statistics are loaded first (independent loads), then every live
-// chunk's partial column, weighted by 2^(m_c - M); dead chunks (m_c = -inf,
-// whose partial was never written) are selected away, not branched around.
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeLaunch a) {
-  const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+// Combine: one 64-thread workgroup per (batch, query head, 64-column slice).
+// Lanes first read the chunk statistics in parallel (lane c: chunk c, c + 64,
+// ...), reduce the max across the wave, then every lane issues its column's
+// loads for all chunks before summing: the partials of dead chunks (m_c =
+// -inf, never written) are selected away, not branched around.  Chunk order
+// is fixed, so the result is deterministic.
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeLaunch a) {
+  const int slice = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int64_t p0 = ((int64_t)b * a.Hq + hq) * a.n_chunks;
   float M = -INFINITY;
-  for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, a.ws_ml[(p0 + c) * 2]);
+  for (int c = lane; c < a.n_chunks; c += 64) M = fmaxf(M, a.ws_ml[(p0 + c) * 2]);
+  M = wave_max(M);
   const float Mu = M == -INFINITY ? 0.0f : M;
+  const int d = slice * 64 + lane;
   float L = 0.0f, acc = 0.0f;
-#pragma unroll 8
+#pragma unroll 16
   for (int c = 0; c < a.n_chunks; ++c) {
     const float mc = a.ws_ml[(p0 + c) * 2];
     const float lc = a.ws_ml[(p0 + c) * 2 + 1];
@@ -198,7 +257,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeLaunch a) {
 }
 
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
-  const dim3 grid(a.n_chunks, a.Hkv, a.B), block(256);
+  const dim3 grid(a.n_chunks, a.Hkv, a.B), block(64 * kDecWaves);
   switch (a.G) {
     case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, block, 0, stream, a); break;
@@ -208,7 +267,7 @@ hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.Hq, a.B), dim3(kDecD), 0, stream, a);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(kDecD / 64, a.Hq, a.B), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -84,11 +84,12 @@ struct Geo {
   static constexpr int VTILE = BN * D * 2 + (BN >> VSH) * 64;
   static constexpr int KSLOT = NSPLIT * KTILE;                    // one K buffer: every split's tile
   static constexpr int VSLOT = NSPLIT * VTILE + NSPLIT * BN * 4;  // one V buffer, then the tiles' staged key mask
-  static constexpr int LDS = 2 * (KSLOT + VSLOT);          // K and V double-buffered
   static constexpr int KB = BN / 32;  // 32-key blocks per tile
   static constexpr int SD = D / 16;   // k-steps of the QK^T contraction
   static constexpr int MT = D / 32;   // d tiles of O^T
   static constexpr int NFQ = SD * KB, NFV = 2 * KB * MT;  // LDS fragments per tile: QK, PV
+  static constexpr int MERGE = (NSPLIT - 1) * RG * NT * (MT * 16 + 2) * 64 * 4;  // split partials (merge_splits)
+  static constexpr int LDS = 2 * (KSLOT + VSLOT) > MERGE ? 2 * (KSLOT + VSLOT) : MERGE;  // K/V double buffers
   // softmax VALU instructions issued between consecutive QK MFMA groups
   static constexpr int VPM = (NT * (7 * BN / 4 + 8) + NFQ - 1) / NFQ;
   static_assert(D % 64 == 0 && BN % 32 == 0 && (VSH == 0 || D == 64), "tile shape");
@@ -665,7 +666,7 @@ __device__ __forceinline__ void merge_splits(WaveState<G> &ws, char *smem) {
     const int rg = wave % G::RG, sp = wave / G::RG;
     constexpr int NREG = G::NT * (G::MT * 16 + 2);
     float *red = reinterpret_cast<float *>(smem);
-    static_assert((G::NSPLIT - 1) * G::RG * NREG * 64 * 4 <= G::LDS, "merge space");
+    static_assert((G::NSPLIT - 1) * G::RG * NREG * 64 * 4 <= G::LDS, "merge space");  // G::MERGE
     if (sp > 0) {
       float *dst = red + ((sp - 1) * G::RG + rg) * NREG * 64 + lane;
       int r = 0;
