@@ -372,7 +372,7 @@ struct PCarry {
 // reference max `mu` (a slot-local pinned copy).
 template <class G, bool HAS_MASK>
 __device__ __forceinline__ void p_pair(PCarry<G> &pc, const f32x16_t (&s)[G::NT][G::KB], int nt, int kb, int i8,
-                                       float mu, float c) {
+                                       float mu, float c) {  // mu: this slot's pinned reference max
   const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
   const float x0 = s[nt][kb][2 * i8], x1 = s[nt][kb][2 * i8 + 1];
   const float e0 = HAS_MASK ? fast_exp2(x0 - mu) : fast_exp2(__builtin_fmaf(x0, c, -mu));
@@ -387,16 +387,14 @@ __device__ __forceinline__ void p_pair(PCarry<G> &pc, const f32x16_t (&s)[G::NT]
 template <class G, bool HAS_MASK>
 __device__ __forceinline__ void p_pairs(PCarry<G> &pc, const f32x16_t (&s)[G::NT][G::KB], int half, int p0, int p1,
                                         float c) {
-  float mu[G::NT];
+  // re-pinning the reference max in place (no copy) keeps this slot's exps
+  // from being hoisted into an earlier slot
 #pragma unroll
-  for (int nt = 0; nt < G::NT; ++nt) {
-    mu[nt] = pc.m_use[nt];
-    pin_in(mu[nt]);  // keeps this slot's exps from being hoisted into an earlier slot
-  }
+  for (int nt = 0; nt < G::NT; ++nt) pin_in(pc.m_use[nt]);
 #pragma unroll
   for (int a = p0; a < p1; ++a) {
     const int nt = a / (G::KB * 4), kb = (a / 4) % G::KB, i8 = 4 * half + a % 4;
-    p_pair<G, HAS_MASK>(pc, s, nt, kb, i8, mu[nt], c);
+    p_pair<G, HAS_MASK>(pc, s, nt, kb, i8, pc.m_use[nt], c);
   }
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) pin_out(pc.lsum[nt]);
@@ -582,7 +580,8 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
 // V(it), writes K(it+2) into the K buffer K(it) used and V(it+1) into the
 // other V buffer, and issues the global loads of K(it+3) and V(it+2) into the
 // register stage.  Tiles past the last one read as zeros and are fully
-// masked (p = 0).  Returns with the LDS free (barrier passed).
+// masked (p = 0), including the padding step of an odd iteration count.
+// Returns with the LDS free (barrier passed).
 template <class G, bool HAS_MASK, class Src>
 __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, const u32x4_t (&qf)[G::NT][G::SD],
                                            char *smem, float c) {
@@ -619,16 +618,18 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
   qk_tile<G>(s, qf, kbuf + sp * G::KTILE, lane);
   if constexpr (!HAS_MASK) mask_tail<G>(s, sp * G::BN, src.n_keys, lane);
 
-  for (int it = 0; it < n_iter; ++it) {
+  // One tile step: S holds S(it) on entry, SN receives S(it+1).  The loop
+  // below alternates the two register sets instead of copying S each step;
+  // an odd iteration count is padded with one all-masked zero tile.
+  auto step = [&](int it, f32x16_t (&S)[G::NT][G::KB], f32x16_t (&SN)[G::NT][G::KB]) {
     const int cur = it & 1;
     char *const kcur = kbuf + cur * G::KSLOT, *const knext = kbuf + (cur ^ 1) * G::KSLOT;
     char *const vcur = vbuf + cur * G::VSLOT, *const vnext = vbuf + (cur ^ 1) * G::VSLOT;
 
-    f32x16_t sn[G::NT][G::KB];
     PCarry<G> pc;
     float alpha[G::NT];
     const bool any =
-        phase_a<G, HAS_MASK>(ws, pc, sn, s, alpha, qf, knext + sp * G::KTILE,
+        phase_a<G, HAS_MASK>(ws, pc, SN, S, alpha, qf, knext + sp * G::KTILE,
                              reinterpret_cast<const float *>(vcur + G::NSPLIT * G::VTILE) + sp * G::BN, c, lane);
     if (any) {
 #pragma unroll
@@ -638,7 +639,7 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
     }
 
     // PV(it); stage K(it+2) and V(it+1); issue K(it+3) and V(it+2)
-    phase_b<G, HAS_MASK>(ws, pc, s, c, vcur + sp * G::VTILE, lane, [&](int k) {
+    phase_b<G, HAS_MASK>(ws, pc, S, c, vcur + sp * G::VTILE, lane, [&](int k) {
       if (k == 0) src.store_k(st, kcur, tid);
       if (k == 1) src.store_v(st, vnext, it + 1, tid);
       if (k == 2) {
@@ -650,11 +651,14 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
     });
     __syncthreads();
 
-    if constexpr (!HAS_MASK) mask_tail<G>(sn, ((it + 1) * G::NSPLIT + sp) * G::BN, src.n_keys, lane);
-#pragma unroll
-    for (int nt = 0; nt < G::NT; ++nt)
-#pragma unroll
-      for (int kb = 0; kb < G::KB; ++kb) s[nt][kb] = sn[nt][kb];
+    if constexpr (!HAS_MASK) mask_tail<G>(SN, ((it + 1) * G::NSPLIT + sp) * G::BN, src.n_keys, lane);
+  };
+
+  f32x16_t s2[G::NT][G::KB];
+  const int n_even = (n_iter + 1) & ~1;
+  for (int it = 0; it < n_even; it += 2) {
+    step(it, s, s2);
+    step(it + 1, s2, s);
   }
 }
 
