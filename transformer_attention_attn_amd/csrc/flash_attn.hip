@@ -67,11 +67,15 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int OCC_>
+template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int OCC_, bool VFIRST_ = false>
 struct Geo {
   static constexpr int D = D_, BN = BN_, NT = NT_, RG = RG_, NSPLIT = NSPLIT_;
   static constexpr int GRP = GRP_;  // LDS fragments read ahead of the MFMAs that use them
   static constexpr int WPE = OCC_;  // waves per SIMD the kernel is compiled for (register budget 512 / WPE)
+  // Slot order of the pipelined phases: VALU slice before the slot's MFMA
+  // (hides the fragment read latency behind the VALU; best when the VALU work
+  // per MFMA is large, D = 64) or after it (best at D = 256).
+  static constexpr bool VFIRST = VFIRST_;
   static constexpr int WAVES = RG * NSPLIT, THREADS = 64 * WAVES;
   static constexpr int BM = 32 * NT * RG;
   // K rows: D bf16 + one 16-byte pad chunk, so 16 consecutive rows start in 16
@@ -415,9 +419,10 @@ __device__ __forceinline__ u32x4_t p_frag(const PCarry<G> &pc, int nt, int kb, i
 // PV MFMAs consume), updates m, and returns whether any row's reference max
 // moved (then O must be multiplied by alpha before PV).
 //
-// Slot f issues QK MFMA f and the K read GRP fragments ahead, then a slice of
-// the softmax: slot 0 the row max, slot 1 the cross-lane max, the rescale
-// decision and alpha, later slots the exp2 / bf16 pack / row sum of P pairs.
+// Slot f issues QK MFMA f and the K read GRP fragments ahead, and a slice of
+// the softmax (before or after the MFMA, G::VFIRST): slot 0 the row max, slot
+// 1 the cross-lane max, the rescale decision and alpha, later slots the exp2
+// / bf16 pack / row sum of P pairs.
 // sched_barrier(0) and the pins hold that order, so this wave's MFMAs run
 // under its own VALU work; the second half of P is left to phase B, which
 // balances the VALU load of the two phases.
@@ -457,20 +462,21 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
   }
   __builtin_amdgcn_sched_barrier(0);
 
+  auto qk_slot = [&](int f) {
+    const int kb = f % G::KB, sd = f / G::KB;
+    pin_in(fb[f]);
 #pragma unroll
-  for (int f = 0; f < G::NFQ; ++f) {
-    {
-      const int kb = f % G::KB, sd = f / G::KB;
-      pin_in(fb[f]);
-#pragma unroll
-      for (int nt = 0; nt < G::NT; ++nt)
-        sn[nt][kb] = mfma32(as_bf16x8(fb[f]), as_bf16x8(qf[nt][sd]), sd == 0 ? f32x16_t{} : sn[nt][kb]);
-      if (f + RA < G::NFQ) {
-        const int g = f + RA;
-        fb[g] = *reinterpret_cast<const u32x4_t *>(kbase + (g % G::KB) * 32 * G::KROW + 32 * (g / G::KB));
-      }
+    for (int nt = 0; nt < G::NT; ++nt)
+      sn[nt][kb] = mfma32(as_bf16x8(fb[f]), as_bf16x8(qf[nt][sd]), sd == 0 ? f32x16_t{} : sn[nt][kb]);
+    if (f + RA < G::NFQ) {
+      const int g = f + RA;
+      fb[g] = *reinterpret_cast<const u32x4_t *>(kbase + (g % G::KB) * 32 * G::KROW + 32 * (g / G::KB));
     }
     __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int f = 0; f < G::NFQ; ++f) {
+    if (!G::VFIRST) qk_slot(f);
     if (f == 0) {
       // scores into log2 units (mask path) and the in-lane row max
 #pragma unroll
@@ -518,6 +524,7 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
       if (p0 < p1) p_pairs<G, HAS_MASK>(pc, s, 0, p0, p1, c);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (G::VFIRST) qk_slot(f);
   }
   return any;
 }
@@ -551,14 +558,17 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
 #pragma unroll
   for (int q = 0; q < RA; ++q) read(q);
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int q = 0; q < G::NFV; ++q) {
+  auto pv_slot = [&](int q) {
     const int mt = q % G::MT, kk = (q / G::MT) % 2, kb = q / (2 * G::MT);
     pin_in(fb[q]);
 #pragma unroll
     for (int nt = 0; nt < G::NT; ++nt) ws.o[nt][mt] = mfma32(as_bf16x8(fb[q]), as_bf16x8(p_frag(pc, nt, kb, kk)), ws.o[nt][mt]);
     if (q + RA < G::NFV) read(q + RA);
     __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int q = 0; q < G::NFV; ++q) {
+    if (!G::VFIRST) pv_slot(q);
     if (q < PSLOTS) {
       p_pairs<G, HAS_MASK>(pc, s, 1, q * PPS, (q + 1) * PPS < NP ? (q + 1) * PPS : NP, c);
     } else {
@@ -568,6 +578,7 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
         for (int r = k + 1; r <= 2; ++r) work(r);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (G::VFIRST) pv_slot(q);
   }
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) ws.l[nt] = pc.lsum[nt];
@@ -600,14 +611,16 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
   if (n_iter <= 0) return;
 
   char *const kbuf = smem, *const vbuf = smem + 2 * G::KSLOT;
-  typename Src::Stage st;
+  // Prologue: K(0), V(0) and K(1) in one round trip (a second register stage
+  // that is only live here), then K(2), V(1) in flight.
+  typename Src::Stage st, st1;
   const int64_t b0 = src.tile_base(0), b1 = src.tile_base(1);
   src.load_k(st, 0, b0, tid);
   src.load_v(st, 0, b0, tid);
+  src.load_k(st1, 1, b1, tid);
   src.store_k(st, kbuf, tid);
   src.store_v(st, vbuf, 0, tid);
-  src.load_k(st, 1, b1, tid);
-  src.store_k(st, kbuf + G::KSLOT, tid);
+  src.store_k(st1, kbuf + G::KSLOT, tid);
   int64_t bv = src.tile_base(2);  // V(it+2) base
   src.load_k(st, 2, bv, tid);
   src.load_v(st, 1, b1, tid);
@@ -775,10 +788,27 @@ void encoder_fwd_kernel(EncoderLaunch a) {
 
   WaveState<G> ws;
   flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c);
+
+  // The residual rows are read before the split merge, so their latency
+  // overlaps it.
+  const int HD = a.H * G::D;
+  f32x4_t resv[G::NT][G::MT][4];
+  if (a.res_out && sp == 0) {
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) {
+      const int row = qt * G::BM + (rg * G::NT + nt) * 32 + l32;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int64_t off = ((int64_t)b * a.Sq + row) * HD + h * G::D + mt * 32 + r4 * 8 + 4 * hh;
+          resv[nt][mt][r4] = row < a.Sq ? ldg<f32x4_t>(a.res + off) : f32x4_t{0, 0, 0, 0};
+        }
+    }
+  }
   merge_splits<G>(ws, smem);
   if (sp != 0) return;
 
-  const int HD = a.H * G::D;
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
     const int row = qt * G::BM + (rg * G::NT + nt) * 32 + l32;
@@ -805,8 +835,7 @@ void encoder_fwd_kernel(EncoderLaunch a) {
         }
         if (a.res_out) {
           const int64_t off = ((int64_t)b * a.Sq + row) * HD + h * G::D + d0;
-          const f32x4_t r = ldg<f32x4_t>(a.res + off);
-          *reinterpret_cast<f32x4_t *>(a.res_out + off) = r + val;
+          *reinterpret_cast<f32x4_t *>(a.res_out + off) = resv[nt][mt][r4] + val;
         }
       }
   }
@@ -871,9 +900,9 @@ void prefill_paged_kernel(PrefillLaunch a) {
 
 // ------------------------------------------------------------------ launchers
 
-using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4>;      // BM 128, 8 waves: 4 row groups x 2 key splits, 32-key tiles, 4 waves/SIMD
-using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2>;  // masked: mask values held in registers, 2 waves/SIMD
-using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2>;   // fp32 inputs: twice the staging registers per tile
+using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true>;      // BM 128, 8 waves: 4 row groups x 2 key splits, 32-key tiles, 4 waves/SIMD
+using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: mask values held in registers, 2 waves/SIMD
+using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: twice the staging registers per tile
 using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2>;    // BM 256, 8 waves of 32 rows, 2 waves per SIMD
 
 // Launch with G::LDS bytes of dynamic LDS; kernels above 64 KiB are opted in
