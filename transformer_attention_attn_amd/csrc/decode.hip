@@ -76,12 +76,13 @@ __device__ __forceinline__ void dec_load(DecStage &st, __amdgpu_buffer_rsrc_t rk
 }
 
 template <int G>
-__global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecodeLaunch a) {
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(5))) void decode_split_kernel(DecodeLaunch a) {
   constexpr int KW = kDecKW, NW = kDecWaves, NG = kDecNG, WK = NG * KW;  // WK: keys per wave
   static_assert(WK <= 64, "one liveness bit per lane");
   __shared__ __attribute__((aligned(16))) float sc[NW][G][KW];
   __shared__ __attribute__((aligned(16))) float red_o[NW][G][kDecD];
   __shared__ float red_ml[NW][G][2];
+  __shared__ __attribute__((aligned(16))) __bf16 qs[NW][G][kDecD];  // each wave's copy of the G query rows
 
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -91,7 +92,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecodeLaun
 
   // Every wave reads the mask of the whole chunk (lane l: key l of the chunk,
   // log2 units, -inf where removed) and votes: a chunk with no live key
-  // writes its empty statistics and exits without touching K/V or the LDS.
+  // writes its empty statistics and exits without touching K/V or the LDS
+  // (every wave takes the same branch, no barrier needed).
   static_assert(kDecChunk <= 64, "one chunk key per lane");
   float mk_lane = -INFINITY;
   if (lane < kDecChunk) {
@@ -110,17 +112,20 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecodeLaun
   }
   const uint64_t live = (live_chunk >> (wave * WK)) & ((WK == 64) ? ~0ull : ((1ull << WK) - 1));
 
-  // q^T as the B operand: lane l holds q[g = l%16][32s + 8(l/16) .. +7], zero
-  // for g >= G (those lanes fetch nothing: out-of-range offset).  Issued
-  // before the liveness vote is used, so its latency overlaps the mask read.
+  // The G query rows (G * 512 B) are copied into this wave's LDS slice: the
+  // q^T B-operand fragments are read from there right before their MFMAs,
+  // which keeps them out of the registers.  Issued before the liveness vote
+  // is used, so the load latency overlaps the mask read.
   const int gq = lane & 15, quad = lane >> 4;
-  u32x4_t qf[kDecD / 32];
   {
     const auto rq = dec_rsrc(a.q + ((int64_t)b * a.Hq + (int64_t)kvh * G) * kDecD, G * kDecD * 2);
-    const uint32_t qoff = gq < G ? gq * (kDecD * 2) + 16 * quad : kOOB;
 #pragma unroll
-    for (int s = 0; s < kDecD / 32; ++s)
-      qf[s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * s, 0, 0));
+    for (int i = 0; i < (G * kDecD * 2 + 1023) / 1024; ++i) {
+      const uint32_t off = (lane + 64 * i) * 16;
+      if (off < G * kDecD * 2)
+        *reinterpret_cast<u32x4_t *>(reinterpret_cast<char *>(&qs[wave][0][0]) + off) =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    }
   }
 
   float m[G], l[G];
@@ -141,11 +146,24 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecodeLaun
 
 #pragma unroll
     for (int grp = 0; grp < NG; ++grp) {
-      if (grp + 1 < NG) dec_load(st[(grp + 1) & 1], rk, rv, live, grp + 1, lane);
+      if (grp + 1 < NG) {
+        // issue group grp+1 now, not earlier: the pinned copy of the liveness
+        // mask keeps the compiler from hoisting every group's loads to the top
+        uint64_t live_n = live;
+        asm volatile("" : "+s"(live_n));
+        dec_load(st[(grp + 1) & 1], rk, rv, live_n, grp + 1, lane);
+      }
       const DecStage &cs = st[NG < 2 ? 0 : grp & 1];
+      // q^T fragment: lane l holds q[g = l%16][32s + 8(l/16) .. +7], zero for g >= G
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's copy of q is in LDS
+      __builtin_amdgcn_wave_barrier();
+      const char *qrow = reinterpret_cast<const char *>(&qs[wave][gq < G ? gq : 0][0]) + 16 * quad;
       f32x4_t s4 = {0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < kDecD / 32; ++s) s4 = mfma16(as_bf16x8(cs.k[s]), as_bf16x8(qf[s]), s4);
+      for (int s = 0; s < kDecD / 32; ++s) {
+        const u32x4_t qv = *reinterpret_cast<const u32x4_t *>(qrow + 64 * s);
+        s4 = mfma16(as_bf16x8(cs.k[s]), as_bf16x8(gq < G ? qv : u32x4_t{0, 0, 0, 0}), s4);
+      }
       // lane l holds S^T[key = 4*(l/16) + i][head g = l%16]: scale, mask, to LDS
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -158,18 +176,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecodeLaun
       // online softmax over the group for each head, PV on the VALU
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float p[KW];
+        // two passes over the scores in LDS (max, then exp2): fewer live registers
+        float mg = -INFINITY;
 #pragma unroll
         for (int q4 = 0; q4 < KW / 4; ++q4) {
           const f32x4_t t = *reinterpret_cast<const f32x4_t *>(&sc[wave][g][4 * q4]);
-          p[4 * q4 + 0] = t[0];
-          p[4 * q4 + 1] = t[1];
-          p[4 * q4 + 2] = t[2];
-          p[4 * q4 + 3] = t[3];
+          mg = fmaxf(mg, fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
         }
-        float mg = p[0];
-#pragma unroll
-        for (int j = 1; j < KW; ++j) mg = fmaxf(mg, p[j]);
         const float m_new = fmaxf(m[g], mg);
         const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m[g] - m_new);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
@@ -178,7 +191,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecodeLaun
         f32x4_t acc = o[g] * alpha;
 #pragma unroll
         for (int j = 0; j < KW; ++j) {
-          const float pj = fast_exp2(p[j] - m_use);
+          const float pj = fast_exp2(sc[wave][g][j] - m_use);
           ls += pj;
           acc[0] += pj * bf16_lo(cs.v[j][0]);
           acc[1] += pj * bf16_hi(cs.v[j][0]);
@@ -227,30 +240,38 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(DecodeLaun
   }
 }
 
-// Combine: one 64-thread workgroup per (batch, query head, 64-column slice).
-// Lanes first read the chunk statistics in parallel (lane c: chunk c, c + 64,
-// ...), reduce the max across the wave, then every lane issues its column's
-// loads for all chunks before summing: the partials of dead chunks (m_c =
-// -inf, never written) are selected away, not branched around.  Chunk order
-// is fixed, so the result is deterministic.
+// Combine: one 64-thread workgroup per (batch, query head, 64-column slice),
+// 64 chunks per round.  Lane c reads chunk c's statistics; the max and the
+// weighted sum of l are wave reductions; every lane issues its column's loads
+// for all 64 chunks at once and weights them with the chunk weight broadcast
+// from lane c.  Dead chunks (m_c = -inf, partial never written) and chunks
+// whose weight underflows are selected away, not branched around.  The chunk
+// order is fixed, so the result is deterministic.
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeLaunch a) {
   const int slice = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int64_t p0 = ((int64_t)b * a.Hq + hq) * a.n_chunks;
-  float M = -INFINITY;
-  for (int c = lane; c < a.n_chunks; c += 64) M = fmaxf(M, a.ws_ml[(p0 + c) * 2]);
-  M = wave_max(M);
-  const float Mu = M == -INFINITY ? 0.0f : M;
   const int d = slice * 64 + lane;
-  float L = 0.0f, acc = 0.0f;
-#pragma unroll 16
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const float mc = a.ws_ml[(p0 + c) * 2];
-    const float lc = a.ws_ml[(p0 + c) * 2 + 1];
-    const float oc = a.ws_o[(p0 + c) * kDecD + d];
-    const bool dead = mc == -INFINITY;
-    const float w = dead ? 0.0f : fast_exp2(mc - Mu);
-    L += dead ? 0.0f : lc * w;
-    acc += dead ? 0.0f : oc * w;
+  float M = -INFINITY, L = 0.0f, acc = 0.0f;
+  for (int c0 = 0; c0 < a.n_chunks; c0 += 64) {
+    const int nc = min(64, a.n_chunks - c0);
+    const int64_t pc = p0 + c0 + (lane < nc ? lane : 0);
+    const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.ws_ml + pc * 2);
+    const float mc = lane < nc ? ml[0] : -INFINITY;
+    float oc[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) oc[i] = a.ws_o[(p0 + c0 + (i < nc ? i : 0)) * kDecD + d];
+    const float Mb = fmaxf(M, wave_max(mc));
+    const float Mu = Mb == -INFINITY ? 0.0f : Mb;
+    const float w = mc == -INFINITY ? 0.0f : fast_exp2(mc - Mu);
+    const float rs = M == -INFINITY ? 0.0f : fast_exp2(M - Mu);  // rescale of the running sums
+    L = L * rs + wave_sum(w > 0.0f ? ml[1] * w : 0.0f);
+    acc *= rs;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), i));
+      acc += wi > 0.0f ? oc[i] * wi : 0.0f;
+    }
+    M = Mb;
   }
   const float r = L > 0.0f ? acc / L : 0.0f;
   a.out[((int64_t)b * a.Hq + hq) * kDecD + d] = (__bf16)r;
