@@ -109,6 +109,46 @@ def cpu_baseline(pre, n_rows: int):
                       f"(fp64 C oracle incl. KV decode), {dt:.1f} s wall"}
 
 
+def time_next_workloads(taa, dev, reps: int = 20):
+    """Encoder workload variants beyond the step (reported, not part of
+    `value`): the 64-frame V-JEPA 2 clip (8192 tokens) and a gte-base batch
+    right-padded to 512 tokens with ragged real lengths (additive key mask).
+    Back-to-back launches between two HIP events, after 3 warm-up calls."""
+    out = {}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    c = W.encoder_custom(803, 1, 16, 8192)
+    q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+    o = torch.empty_like(q)
+    ms = timed(lambda: taa.attn_encoder_fwd(q, k, v, c.scale, None, out=o, want_ln=False))
+    f = acc.encoder_flops(1, 16, 8192, 8192, 64)
+    out["vjepa2_clip64_s8192_attention"] = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12,
+                                            "frac_bf16_peak": f / (ms * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS}
+    g = torch.Generator().manual_seed(900)
+    lens = torch.randint(6, 513, (8,), generator=g).tolist()
+    c = W.encoder_custom(900, 8, 12, 512, masked_lens=lens)
+    q, k, v, m = c.q.to(dev), c.k.to(dev), c.v.to(dev), c.mask.to(dev)
+    res, gam, bet = c.residual.to(dev), c.gamma.to(dev), c.beta.to(dev)
+    ms = timed(lambda: taa.attn_encoder_fwd(q, k, v, c.scale, m, residual=res, gamma=gam, beta=bet, eps=c.eps))
+    dense = acc.encoder_flops(8, 12, 512, 512, 64)
+    live = 4 * 512 * sum(lens) * 12 * 64
+    out["gte_base_padded_L512_b8_block"] = {"ms": ms, "lens": lens, "dense_equiv_tflops": dense / (ms * 1e-3) / 1e12,
+                                            "live_key_tflops": live / (ms * 1e-3) / 1e12,
+                                            "kernels": "attention+mask+residual, res_ln"}
+    return out
+
+
 def _short(name: str) -> str:
     """Kernel family name from a demangled rocprofv3 kernel name."""
     for k in ("prefill_paged_kernel", "encoder_fwd_kernel", "res_ln_kernel", "decode_split_kernel",
@@ -188,7 +228,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=4, help="query tokens in the CPU-baseline sample (0: skip)")
-    ap.add_argument("--only", choices=["all", "encoder", "decode", "prefill"], default="all",
+    ap.add_argument("--only", choices=["all", "encoder", "decode", "prefill", "next"], default="all",
                     help="run a single kernel family (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (scales the rocprofv3 "
@@ -246,6 +286,8 @@ def main():
     run_enc = args.only in ("all", "encoder")
     run_dec = args.only in ("all", "decode")
     run_pre = args.only in ("all", "prefill")
+    if args.only == "next":
+        args.steps = args.warmup = 0
 
     def step(timed: bool):
         if run_enc:
@@ -277,7 +319,7 @@ def main():
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    ms_step = wall * 1e3 / args.steps if args.steps else 0.0
 
     f_enc = acc.encoder_flops(enc.B, enc.H, enc.S, enc.S, enc.D)
     lens = dec.lens.tolist()
@@ -325,6 +367,9 @@ def main():
         roofline = {"bound": "hbm", "achieved": p["gbps"], "peak": acc.PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": p["frac_hbm_peak"], "traffic": None, "kernel": "decode_split_kernel+decode_combine_kernel"}
 
+    if args.only in ("all", "next"):
+        parts["next"] = time_next_workloads(taa, dev)
+
     cpu = None
     if args.cpu_rows > 0 and run_pre:
         _log(f"[bench] cpu baseline: oracle on {args.cpu_rows} prefill tokens")
@@ -332,7 +377,7 @@ def main():
 
     line = {
         "metric": "attn TFLOP/s & % MFMA peak (encoder/prefill); decode GB/s & % HBM peak",
-        "value": total_flops / (ms_step * 1e-3) / 1e12,
+        "value": total_flops / (ms_step * 1e-3) / 1e12 if ms_step else 0.0,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,

@@ -1,0 +1,96 @@
+"""Encoder workload variants against the fp64 oracle (through the C ABI).
+
+- gte-style right-padded batches: the fused attention block of the GTE encoder
+  page ("Constraints": head_dim 64, right padding with a 0/1 attention mask;
+  its supported L in {128, ..., 1024}), here as an additive -inf key mask;
+- padding exactness: the rows of a sequence do not change when the batch is
+  padded to a longer length or the padding holds other values;
+- the long V-JEPA 2 clip (64 frames, 8192 tokens) of the ViT page's
+  "Attention shapes", checked on sampled query rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import assert_close, assert_ln_stats
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run_block(taa, case, with_ln=True):
+    d = lambda t: None if t is None else t.to(DEV)
+    r = taa.attn_encoder_fwd(d(case.q), d(case.k), d(case.v), case.scale, d(case.mask), residual=d(case.residual),
+                             gamma=d(case.gamma), beta=d(case.beta), eps=case.eps, want_ln=with_ln)
+    torch.cuda.synchronize()
+    return r
+
+
+def _ragged_lengths(seed: int, B: int, L: int):
+    """Per-sequence real lengths from 6 tokens up to L (the page's ragged inputs)."""
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.randint(6, L + 1, (B,), generator=g).tolist()
+    lens[0], lens[-1] = 6, L  # shortest and unpadded sequences always present
+    return lens
+
+
+@pytest.mark.parametrize("L", [128, 384, 1024])
+def test_gte_right_padded_batch(gpu_lib, L):
+    lens = _ragged_lengths(700 + L, 4, L)
+    case = W.encoder_custom(700 + L, 4, 12, L, masked_lens=lens)  # gte-base: 12 heads x 64 = 768
+    _say(f"[encoder-variant] gte padded L={L} lens={lens}")
+    r = _run_block(gpu_lib, case)
+    ref = oracle.encoder_block(case.q, case.k, case.v, case.scale, case.residual, case.gamma, case.beta, case.eps,
+                               case.mask)
+    assert_close(r["out"], ref["attn"], f"gte L={L} attention")
+    assert_close(r["residual_out"], ref["res_out"], f"gte L={L} residual_out")
+    assert_close(r["ln_out"], ref["ln_out"], f"gte L={L} ln_out")
+    assert_ln_stats(r["residual_out"], r["ln_mean"], r["ln_rstd"], case.gamma, case.beta, case.eps, f"gte L={L}")
+
+
+def test_padding_exactness(gpu_lib):
+    """The rows of a sequence of n real tokens are bit-identical whether the
+    batch is padded to 128 or 256 and whatever the padding holds."""
+    n, H, D = 77, 12, 64
+    short = W.encoder_custom(801, 1, H, 128, masked_lens=[n])
+    long = W.encoder_custom(802, 1, H, 256, masked_lens=[n])  # different padding contents
+    for name in ("q", "k", "v"):
+        getattr(long, name)[:, :, :n] = getattr(short, name)[:, :, :n]
+    long.residual[:, :n] = short.residual[:, :n]
+    long.gamma.copy_(short.gamma)
+    long.beta.copy_(short.beta)
+    _say(f"[encoder-variant] padding exactness n={n}: L=128 vs L=256")
+    a = _run_block(gpu_lib, short)
+    b = _run_block(gpu_lib, long)
+    for key in ("out", "residual_out", "ln_out"):
+        x, y = a[key], b[key]
+        x = x[:, :, :n] if key == "out" else x[:, :n]
+        y = y[:, :, :n] if key == "out" else y[:, :n]
+        assert torch.equal(x, y), f"{key}: rows of the real tokens depend on the padding"
+    assert torch.equal(a["ln_mean"][:n], b["ln_mean"][:n]) and torch.equal(a["ln_rstd"][:n], b["ln_rstd"][:n])
+    ref = oracle.encoder_block(short.q, short.k, short.v, short.scale, short.residual, short.gamma, short.beta,
+                               short.eps, short.mask)
+    assert_close(a["out"][:, :, :n], ref["attn"][:, :, :n], "padding exactness: attention vs oracle")
+
+
+def test_vjepa2_long_clip_8192(gpu_lib):
+    case = W.encoder_custom(803, 1, 16, 8192)
+    _say(f"[encoder-variant] V-JEPA2 64-frame clip: B=1 H=16 S=8192 D=64")
+    d = lambda t: t.to(DEV)
+    r = gpu_lib.attn_encoder_fwd(d(case.q), d(case.k), d(case.v), case.scale, None, want_ln=False)
+    torch.cuda.synchronize()
+    rows = torch.randperm(8192, generator=torch.Generator().manual_seed(803))[:48].sort().values
+    rows = torch.cat([rows, torch.tensor([0, 8191])])
+    ref = oracle.sdpa(case.q[:, :, rows], case.k, case.v, case.scale)
+    assert_close(r["out"][:, :, rows.to(DEV)], ref, "V-JEPA2 8192 sampled rows")
+    assert np.isfinite(r["out"].float().cpu().numpy()).all()
