@@ -109,12 +109,28 @@ def cpu_baseline(pre, n_rows: int):
                       f"(fp64 C oracle incl. KV decode), {dt:.1f} s wall"}
 
 
-def time_next_workloads(taa, dev, reps: int = 20):
-    """Encoder workload variants beyond the step (reported, not part of
-    `value`): the 64-frame V-JEPA 2 clip (8192 tokens) and a gte-base batch
-    right-padded to 512 tokens with ragged real lengths (additive key mask).
-    Back-to-back launches between two HIP events, after 3 warm-up calls."""
+def time_next_workloads(taa, dev, flush, reps: int = 20):
+    """Workload variants beyond the step (reported, not part of `value`):
+    the 64-frame V-JEPA 2 clip (8192 tokens), a gte-base batch right-padded to
+    512 tokens with ragged real lengths (additive key mask), both timed as
+    back-to-back launches between two HIP events after 3 warm-up calls; and
+    the decode at head_dim 512 (global layers) and over a 1024-key sliding
+    window at head_dim 256, each call timed alone after the cache flush."""
     out = {}
+
+    def timed_flushed(fn):
+        for _ in range(3):
+            fn()
+        ms = []
+        for _ in range(reps):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return statistics.median(ms)
 
     def timed(fn):
         for _ in range(3):
@@ -146,6 +162,32 @@ def time_next_workloads(taa, dev, reps: int = 20):
     out["gte_base_padded_L512_b8_block"] = {"ms": ms, "lens": lens, "dense_equiv_tflops": dense / (ms * 1e-3) / 1e12,
                                             "live_key_tflops": live / (ms * 1e-3) / 1e12,
                                             "kernels": "attention+mask+residual, res_ln"}
+
+    c = W.decode_gemma(1005, D=512)
+    q, k, v, m = c.q.to(dev), c.k.to(dev), c.v.to(dev), c.mask.to(dev)
+    o = torch.empty_like(q)
+    ws = torch.empty(taa.attn_decode_gqa_workspace_size(c.B, c.Hq, c.S_ctx, c.D), dtype=torch.uint8, device=dev)
+    ms = timed_flushed(lambda: taa.attn_decode_gqa(q, k, v, m, c.scale, c.G, out=o, workspace=ws))
+    b = acc.decode_bytes(c.lens.tolist(), c.Hkv, c.Hq, c.S_ctx, c.D)
+    out["gemma_gqa_decode_d512_b8_ctx4096"] = {"median_ms": ms, "lens": c.lens.tolist(), "bytes": b,
+                                              "gbps": b / (ms * 1e-3) / 1e9,
+                                              "frac_hbm_peak": b / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBPS}
+    del k, v
+    c = W.decode_gemma(1006)
+    win = 1024
+    lens = c.lens.tolist()
+    beg = torch.tensor([max(n - win, 0) for n in lens], dtype=torch.int32, device=dev)
+    end = torch.tensor(lens, dtype=torch.int32, device=dev)
+    q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+    o = torch.empty_like(q)
+    ws = torch.empty(taa.attn_decode_gqa_window_workspace_size(c.B, c.Hq, c.S_ctx, win, c.D), dtype=torch.uint8,
+                     device=dev)
+    ms = timed_flushed(lambda: taa.attn_decode_gqa_window(q, k, v, None, beg, end, win, c.scale, c.G, out=o,
+                                                          workspace=ws))
+    b = acc.decode_window_bytes([min(n, win) for n in lens], c.Hkv, c.Hq, c.D)
+    out["gemma_sliding_window1024_decode_d256_b8_ctx4096"] = {
+        "median_ms": ms, "lens": lens, "window": win, "bytes": b, "gbps": b / (ms * 1e-3) / 1e9,
+        "frac_hbm_peak": b / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBPS}
     return out
 
 
@@ -368,7 +410,7 @@ def main():
                     "frac": p["frac_hbm_peak"], "traffic": None, "kernel": "decode_split_kernel+decode_combine_kernel"}
 
     if args.only in ("all", "next"):
-        parts["next"] = time_next_workloads(taa, dev)
+        parts["next"] = time_next_workloads(taa, dev, flush)
 
     cpu = None
     if args.cpu_rows > 0 and run_pre:

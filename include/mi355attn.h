@@ -123,8 +123,10 @@ ATTN_API int attn_encoder_fwd(const attn_encoder_args_t *args, hipStream_t strea
  *   q [B,Hq,1,D] bf16, k/v [B,Hkv,S_ctx,D] bf16, attn_mask [B,1,1,S_ctx] fp32
  *   (nullable = no mask), out [B,Hq,1,D] bf16, all contiguous and 16-byte
  *   aligned.  Query head h reads KV head h / num_kv_groups; Hq must equal
- *   Hkv * num_kv_groups, num_kv_groups in {1, 2, 4, 8}, D == 256.  Key chunks whose
- *   mask entries are all -inf are skipped without reading K/V.
+ *   Hkv * num_kv_groups, num_kv_groups in {1, 2, 4, 8}, D in {256, 512} (the
+ *   page's introduction: 256 on sliding-window layers, 512 on global ones).
+ *   Key chunks whose mask entries are all -inf are skipped without reading K/V.
+ *   A query row whose keys are all masked gets o = 0.
  *   workspace: device scratch of at least attn_decode_gqa_workspace_size()
  *   bytes, 256-byte aligned, owned by the caller; its contents on entry are
  *   ignored.
@@ -133,6 +135,34 @@ ATTN_API size_t attn_decode_gqa_workspace_size(int B, int Hq, int S_ctx, int D);
 ATTN_API int attn_decode_gqa(const void *q, const void *k, const void *v, const float *attn_mask,
                     float softmax_scale, int num_kv_groups, int B, int Hq, int Hkv, int S_ctx, int D,
                     void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * GQA single-token decode over a per-sequence key range (sliding-window
+ * layers).
+ *
+ * Follows: the same page, "Future performance follow-on" (a windowed-KV
+ * gather for sliding-window layers: only the most recent window of keys is
+ * needed).  Sequence b attends the keys j with
+ *     e_b = clamp(key_end[b], 0, S_ctx)              (S_ctx if key_end is null)
+ *     s_b = max(clamp(key_begin[b], 0, e_b), e_b - max_keys)   (0 if key_begin is null)
+ *     s_b <= j < e_b  and  attn_mask[b, j] != -inf,
+ * i.e. the range is cut to its last max_keys keys (the window).  The other
+ * operands, their layouts and the requirements are those of attn_decode_gqa;
+ * key_begin/key_end are device int32 [B] (each nullable, 4-byte aligned),
+ * read by the kernels, so the range may change between calls without a host
+ * round trip.  The grid covers only min(ceil(min(max_keys, S_ctx)/64) + 1,
+ * ceil(S_ctx/64)) chunks of 64 keys per sequence, counted from s_b rounded
+ * down to a multiple of 64: keys before the window are neither fetched nor
+ * given work.  A sequence with an empty range gets o = 0.
+ *   workspace: at least attn_decode_gqa_window_workspace_size(B, Hq, S_ctx,
+ *   max_keys, D) bytes, 256-byte aligned, owned by the caller; contents on
+ *   entry ignored.  max_keys >= 1, else ATTN_ERR_INVALID_ARG.
+ */
+ATTN_API size_t attn_decode_gqa_window_workspace_size(int B, int Hq, int S_ctx, int max_keys, int D);
+ATTN_API int attn_decode_gqa_window(const void *q, const void *k, const void *v, const float *attn_mask,
+                           const int32_t *key_begin, const int32_t *key_end, int max_keys,
+                           float softmax_scale, int num_kv_groups, int B, int Hq, int Hkv, int S_ctx,
+                           int D, void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * History-only GQA prefill over a paged FP8 KV cache.

@@ -115,6 +115,45 @@ def sdpa(q, k, v, scale: float, mask=None, return_lse: bool = False):
     return (out, lse) if return_lse else out
 
 
+def window_range(S_ctx: int, B: int, key_begin=None, key_end=None, max_keys=None):
+    """Per-sequence key range [s_b, e_b) of a windowed decode.
+
+    head_dim>128 (256/512) GQA Flash-Decode NKI Kernel for AWS Trainium,
+    "Future performance follow-on": a sliding-window layer needs only the
+    most recent window of keys.  Reading taken here: the caller's range is
+    clamped to the cache, e_b = clamp(end_b, 0, S_ctx), s_b = clamp(begin_b,
+    0, e_b), and then cut to its last max_keys keys, s_b = max(s_b, e_b -
+    max_keys).  Missing bounds mean 0 and S_ctx.
+    """
+    W = S_ctx if max_keys is None else int(max_keys)
+    beg = [0] * B if key_begin is None else [int(x) for x in np.asarray(key_begin).reshape(-1)]
+    end = [S_ctx] * B if key_end is None else [int(x) for x in np.asarray(key_end).reshape(-1)]
+    out = []
+    for b in range(B):
+        e = min(max(end[b], 0), S_ctx)
+        s = min(max(beg[b], 0), e)
+        out.append((max(s, e - W), e))
+    return out
+
+
+def decode_window(q, k, v, scale: float, mask=None, key_begin=None, key_end=None, max_keys=None):
+    """Single-token GQA decode over per-sequence key ranges (``window_range``).
+
+    The range is one more additive mask: keys outside [s_b, e_b) get -inf,
+    added to the caller's mask; then plain attention (``sdpa``).  A sequence
+    with no key left gets o = 0, as every fully masked row does.
+    """
+    import torch
+
+    B, Skv = q.shape[0], k.shape[2]
+    add = np.full((B, Skv), -np.inf)
+    for b, (s, e) in enumerate(window_range(Skv, B, key_begin, key_end, max_keys)):
+        add[b, s:e] = 0.0
+    if mask is not None:
+        add = add + _f64(mask).reshape(B, Skv)
+    return sdpa(q, k, v, scale, torch.from_numpy(add))
+
+
 def layernorm(x, gamma=None, beta=None, eps: float = 1e-6):
     """LayerNorm over the last dim; returns (y, mean, rstd) in fp64."""
     xs = _f64(x)

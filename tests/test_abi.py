@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_the_four_entry_points():
     names = _declared_functions()
     for n in ("attn_encoder_fwd", "attn_decode_gqa", "attn_prefill_paged", "res_ln",
-              "attn_decode_gqa_workspace_size", "attn_status_string", "attn_version"):
+              "attn_decode_gqa_workspace_size", "attn_decode_gqa_window", "attn_decode_gqa_window_workspace_size",
+              "attn_status_string", "attn_version"):
         assert n in names
 
 
@@ -114,6 +115,7 @@ def test_decode_workspace_size(lib):
     (dict(q=None), taa.ATTN_ERR_INVALID_ARG),
     (dict(Hq=15), taa.ATTN_ERR_INVALID_ARG),                   # Hq != Hkv * G
     (dict(D=128), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(D=512), taa.ATTN_ERR_WORKSPACE),                     # head_dim 512 passes the shape checks
     (dict(G=16, Hq=128), taa.ATTN_ERR_UNSUPPORTED),
     (dict(G=3, Hq=24), taa.ATTN_ERR_UNSUPPORTED),
     (dict(k=BAD), taa.ATTN_ERR_INVALID_ARG),
@@ -125,6 +127,46 @@ def test_decode_workspace_size(lib):
 ])
 def test_decode_validation(lib, kw, expect):
     assert lib.attn_decode_gqa(*_dec(**kw)) == expect
+
+
+def _win(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, mask=None, kb=FAKE, ke=FAKE, W=1024, scale=1.0, G=2, B=8, Hq=16, Hkv=8, S=4096,
+             D=256, out=FAKE, ws=None, wsb=0)
+    a.update(kw)
+    return (a["q"], a["k"], a["v"], a["mask"], a["kb"], a["ke"], a["W"], a["scale"], a["G"], a["B"], a["Hq"],
+            a["Hkv"], a["S"], a["D"], a["out"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("S,W,chunks", [
+    (4096, 1024, 17),   # a 1024-key window starting anywhere touches at most 17 chunks of 64
+    (4096, 64, 2),
+    (4096, 1, 2),
+    (4096, 4096, 64),   # never more chunks than the cache holds
+    (4096, 100000, 64),
+    (100, 50, 2),
+    (100, 64, 2),
+])
+def test_window_workspace_size(S, W, chunks):
+    n = taa.attn_decode_gqa_window_workspace_size(2, 4, S, W, 512)
+    parts = 2 * 4 * chunks
+    assert n == (parts * 512 * 4 + 255) // 256 * 256 + parts * 2 * 4
+    assert taa.attn_decode_gqa_window_workspace_size(2, 4, S, 0, 512) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(W=0), taa.ATTN_ERR_INVALID_ARG),
+    (dict(W=-5), taa.ATTN_ERR_INVALID_ARG),
+    (dict(kb=FAKE + 2), taa.ATTN_ERR_INVALID_ARG),             # int32 arrays need 4-byte alignment
+    (dict(ke=FAKE + 1), taa.ATTN_ERR_INVALID_ARG),
+    (dict(D=128), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=15), taa.ATTN_ERR_INVALID_ARG),
+    (dict(), taa.ATTN_ERR_WORKSPACE),
+    (dict(kb=None, ke=None, D=512), taa.ATTN_ERR_WORKSPACE),  # both ranges optional
+    (dict(ws=FAKE, wsb=100), taa.ATTN_ERR_WORKSPACE),
+    (dict(scale=float("nan")), taa.ATTN_ERR_INVALID_ARG),
+])
+def test_window_validation(lib, kw, expect):
+    assert lib.attn_decode_gqa_window(*_win(**kw)) == expect
 
 
 def _pre(**kw):

@@ -48,3 +48,9 @@ def test_pcp_full_machine():
 def test_decode_bytes():
     # one KV head, one row of 3 keys, D=4: K+V 3*4*2*2, mask 8*4, q+out 2*1*4*2
     assert acc.decode_bytes([3], 1, 1, 8, 4) == 48 + 32 + 16
+
+
+def test_decode_window_bytes():
+    # two sequences of 3 and 5 in-range keys, 2 KV / 4 query heads, D=8:
+    # K+V 8*2*8*2*2, q+out 2*2*4*8*2, no mask
+    assert acc.decode_window_bytes([3, 5], 2, 4, 8) == 512 + 256

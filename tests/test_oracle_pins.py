@@ -286,3 +286,58 @@ def test_paged_prefill_equals_dense_on_logical_kv():
         vc2[int(bt[i])] = torch.tensor(-448.0).to(torch.float8_e4m3fn)
     out2 = oracle.prefill_paged(q, kc2, vc2, ks, vs, bt, L_act, 0.2, rows)
     assert np.array_equal(out, out2)
+
+
+# ----------------------------------------------------------------------------- windowed decode
+
+
+@pytest.mark.parametrize("beg,end,W,expect", [
+    (5, 70, 1000, (5, 70)),      # range inside the cache, wider window: unchanged
+    (0, 100, 16, (84, 100)),     # cut to its last 16 keys
+    (-3, 50, 1000, (0, 50)),     # begin clamped to 0
+    (10, 500, 1000, (10, 128)),  # end clamped to S_ctx = 128
+    (90, 40, 1000, (40, 40)),    # begin past end: empty
+    (0, -7, 8, (0, 0)),          # end before the cache: empty
+    (120, 128, 1, (127, 128)),   # one-key window
+])
+def test_window_range_worked_cases(beg, end, W, expect):
+    """Worked by hand from the reading: clamp to [0, S_ctx], keep the last W."""
+    assert oracle.window_range(128, 1, [beg], [end], W) == [expect]
+
+
+def test_window_range_defaults():
+    assert oracle.window_range(77, 2) == [(0, 77), (0, 77)]
+    assert oracle.window_range(77, 1, None, [60], 16) == [(44, 60)]
+    assert oracle.window_range(77, 1, [70], None, None) == [(70, 77)]
+
+
+def test_decode_window_equals_attention_over_the_slice():
+    """Windowed decode of each sequence equals torch fp64 SDPA over K/V sliced
+    to that sequence's range, with the caller's mask sliced alongside."""
+    g = torch.Generator().manual_seed(16)
+    B, Hq, Hkv, S, D = 3, 4, 2, 90, 8
+    q, k, v = _rand(g, B, Hq, 1, D), _rand(g, B, Hkv, S, D), _rand(g, B, Hkv, S, D)
+    mask = torch.zeros(B, 1, 1, S, dtype=torch.float64)
+    mask[1, ..., 60:64] = -math.inf
+    mask[2, ..., 7] = 0.75  # a finite additive bias inside the window
+    beg, end, W = [10, 0, 3], [50, 90, 40], 32
+    out = oracle.decode_window(q, k, v, 0.4, mask, beg, end, W)
+    slices = [(18, 50), (58, 90), (8, 40)]  # the last 32 keys of [10,50), [0,90), [3,40)
+    for b, (s, e) in enumerate(slices):
+        ref = _torch_sdpa64(q[b:b + 1], k[b:b + 1, :, s:e], v[b:b + 1, :, s:e], 0.4, mask[b:b + 1, ..., s:e])
+        assert _relmax(out[b:b + 1], ref) < 1e-12
+    # keys outside every window may hold anything
+    k2, v2 = k.clone(), v.clone()
+    k2[0, :, :18] = 1e6
+    v2[0, :, 50:] = -1e6
+    k2[2, :, 40:] = -3e5
+    assert np.array_equal(oracle.decode_window(q, k2, v2, 0.4, mask, beg, end, W), out)
+
+
+def test_decode_window_empty_range_is_zero():
+    g = torch.Generator().manual_seed(17)
+    q, k, v = _rand(g, 2, 2, 1, 4), _rand(g, 2, 1, 10, 4), _rand(g, 2, 1, 10, 4)
+    out = oracle.decode_window(q, k, v, 1.0, None, [6, 0], [6, 10], 4)
+    assert np.all(out[0] == 0.0)
+    ref = _torch_sdpa64(q[1:], k[1:, :, 6:], v[1:, :, 6:], 1.0)
+    assert _relmax(out[1:], ref) < 1e-12

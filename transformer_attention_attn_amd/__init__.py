@@ -8,6 +8,7 @@ is raised.
 
 Entry points (same names as the C ABI in include/mi355attn.h):
   attn_encoder_fwd, attn_decode_gqa, attn_decode_gqa_workspace_size,
+  attn_decode_gqa_window, attn_decode_gqa_window_workspace_size,
   attn_prefill_paged, res_ln, attn_status_string, attn_version.
 """
 from __future__ import annotations
@@ -71,6 +72,10 @@ def load(path: str | None = None):
     L.attn_decode_gqa_workspace_size.restype = Z
     L.attn_decode_gqa.argtypes = [P, P, P, P, F, I, I, I, I, I, I, P, P, Z, P]
     L.attn_decode_gqa.restype = I
+    L.attn_decode_gqa_window_workspace_size.argtypes = [I, I, I, I, I]
+    L.attn_decode_gqa_window_workspace_size.restype = Z
+    L.attn_decode_gqa_window.argtypes = [P, P, P, P, P, P, I, F, I, I, I, I, I, I, P, P, Z, P]
+    L.attn_decode_gqa_window.restype = I
     L.attn_prefill_paged.argtypes = [P, P, P, F, F, P, I, I, I, I, F, I, I, I, I, I, P, P, P]
     L.attn_prefill_paged.restype = I
     L.res_ln.argtypes = [P, P, I, P, P, F, I, I, P, P, I, P, P, P]
@@ -202,6 +207,38 @@ def attn_decode_gqa(q, k, v, attn_mask, softmax_scale: float, num_kv_groups: int
     rc = load().attn_decode_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(attn_mask), float(softmax_scale), int(num_kv_groups),
                                 B, Hq, Hkv, S_ctx, D, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "attn_decode_gqa")
+    return out
+
+
+def attn_decode_gqa_window_workspace_size(B: int, Hq: int, S_ctx: int, max_keys: int, D: int) -> int:
+    return int(load().attn_decode_gqa_window_workspace_size(B, Hq, S_ctx, max_keys, D))
+
+
+def attn_decode_gqa_window(q, k, v, attn_mask, key_begin, key_end, max_keys: int, softmax_scale: float,
+                           num_kv_groups: int, *, out=None, workspace=None, stream=None):
+    """GQA single-token decode over per-sequence key ranges: as attn_decode_gqa,
+    plus key_begin/key_end int32 [B] device tensors (or None) and the window
+    bound max_keys.  Returns out [B,Hq,1,D] bf16."""
+    _need_cuda(q, k, v, attn_mask, key_begin, key_end)
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    if attn_mask is not None and not attn_mask.is_contiguous():
+        raise ValueError("attn_mask must be contiguous")
+    B, Hq, _, D = q.shape
+    Hkv, S_ctx = k.shape[1], k.shape[2]
+    for name, t in (("key_begin", key_begin), ("key_end", key_end)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B):
+            raise ValueError(f"{name} must be a contiguous int32 tensor of B entries")
+    if out is None:
+        out = torch.empty(B, Hq, 1, D, dtype=torch.bfloat16, device=q.device)
+    need = attn_decode_gqa_window_workspace_size(B, Hq, S_ctx, max_keys, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = load().attn_decode_gqa_window(_ptr(q), _ptr(k), _ptr(v), _ptr(attn_mask), _ptr(key_begin), _ptr(key_end),
+                                       int(max_keys), float(softmax_scale), int(num_kv_groups), B, Hq, Hkv, S_ctx,
+                                       D, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "attn_decode_gqa_window")
     return out
 
 

@@ -32,6 +32,63 @@ void exp2_scale(float scale, float *c, int *q_neg) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+// Chunks of keys per sequence the decode grid spans.  Without a range: the
+// whole cache.  With one: a range of at most w = min(max_keys, S_ctx) keys
+// starting anywhere touches at most ceil(w / chunk) + 1 chunks, and never
+// more than the cache holds.
+int64_t decode_chunks(int S_ctx, int max_keys, bool ranged) {
+  const int64_t C = decode_chunk_keys();
+  const int64_t all = (S_ctx + C - 1) / C;
+  if (!ranged) return all;
+  const int64_t w = max_keys < S_ctx ? max_keys : S_ctx;
+  const int64_t n = (w + C - 1) / C + 1;
+  return n < all ? n : all;
+}
+
+int decode_common(const void *q, const void *k, const void *v, const float *attn_mask, const int32_t *key_begin,
+                  const int32_t *key_end, int max_keys, bool ranged, float softmax_scale, int num_kv_groups, int B,
+                  int Hq, int Hkv, int S_ctx, int D, void *out, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_ctx <= 0 || D <= 0 || num_kv_groups <= 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)Hkv * num_kv_groups != Hq) return ATTN_ERR_INVALID_ARG;
+  if (D != 256 && D != 512) return ATTN_ERR_UNSUPPORTED;
+  if (num_kv_groups > decode_max_groups() || (num_kv_groups & (num_kv_groups - 1)))
+    return ATTN_ERR_UNSUPPORTED;
+  if (!finite(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
+  if (attn_mask && !aligned16(attn_mask)) return ATTN_ERR_INVALID_ARG;
+  const int64_t n_chunks = decode_chunks(S_ctx, max_keys, ranged);
+  const size_t need = ranged ? attn_decode_gqa_window_workspace_size(B, Hq, S_ctx, max_keys, D)
+                             : attn_decode_gqa_workspace_size(B, Hq, S_ctx, D);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_INVALID_ARG;
+  if (n_chunks > 0x7fffffffLL || Hkv > 65535 || B > 65535 || Hq > 65535) return ATTN_ERR_UNSUPPORTED;
+
+  DecodeLaunch L;
+  memset(&L, 0, sizeof L);
+  L.q = static_cast<const __bf16 *>(q);
+  L.k = static_cast<const __bf16 *>(k);
+  L.v = static_cast<const __bf16 *>(v);
+  L.mask = attn_mask;
+  L.key_begin = key_begin;
+  L.key_end = key_end;
+  L.max_keys = max_keys;
+  L.B = B;
+  L.Hq = Hq;
+  L.Hkv = Hkv;
+  L.G = num_kv_groups;
+  L.S_ctx = S_ctx;
+  L.D = D;
+  L.n_chunks = (int)n_chunks;
+  L.c = softmax_scale * 1.4426950408889634f;
+  const int64_t parts = (int64_t)B * Hq * n_chunks;
+  L.ws_o = static_cast<float *>(workspace);
+  L.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + ((parts * D * 4) + 255) / 256 * 256);
+  L.out = static_cast<__bf16 *>(out);
+  return hip_status(launch_decode(L, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,9 +187,17 @@ int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
   return hip_status(launch_res_ln(R, stream));
 }
 
+size_t attn_decode_gqa_window_workspace_size(int B, int Hq, int S_ctx, int max_keys, int D) {
+  if (B <= 0 || Hq <= 0 || S_ctx <= 0 || max_keys <= 0 || D <= 0) return 0;
+  const int64_t n_chunks = decode_chunks(S_ctx, max_keys, true);
+  const int64_t parts = (int64_t)B * Hq * n_chunks;
+  const int64_t o_bytes = ((parts * D * 4) + 255) / 256 * 256;
+  return (size_t)(o_bytes + parts * 2 * 4);
+}
+
 size_t attn_decode_gqa_workspace_size(int B, int Hq, int S_ctx, int D) {
   if (B <= 0 || Hq <= 0 || S_ctx <= 0 || D <= 0) return 0;
-  const int64_t n_chunks = (S_ctx + decode_chunk_keys() - 1) / decode_chunk_keys();
+  const int64_t n_chunks = decode_chunks(S_ctx, S_ctx, false);
   const int64_t parts = (int64_t)B * Hq * n_chunks;
   const int64_t o_bytes = ((parts * D * 4) + 255) / 256 * 256;
   return (size_t)(o_bytes + parts * 2 * 4);
@@ -141,39 +206,20 @@ size_t attn_decode_gqa_workspace_size(int B, int Hq, int S_ctx, int D) {
 int attn_decode_gqa(const void *q, const void *k, const void *v, const float *attn_mask, float softmax_scale,
                     int num_kv_groups, int B, int Hq, int Hkv, int S_ctx, int D, void *out, void *workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_ctx <= 0 || D <= 0 || num_kv_groups <= 0) return ATTN_ERR_INVALID_ARG;
-  if ((int64_t)Hkv * num_kv_groups != Hq) return ATTN_ERR_INVALID_ARG;
-  if (D != 256) return ATTN_ERR_UNSUPPORTED;
-  if (num_kv_groups > decode_max_groups() || (num_kv_groups & (num_kv_groups - 1)))
-    return ATTN_ERR_UNSUPPORTED;
-  if (!finite(softmax_scale)) return ATTN_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
-  if (attn_mask && !aligned16(attn_mask)) return ATTN_ERR_INVALID_ARG;
-  const size_t need = attn_decode_gqa_workspace_size(B, Hq, S_ctx, D);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_INVALID_ARG;
-  const int n_chunks = (S_ctx + decode_chunk_keys() - 1) / decode_chunk_keys();
-  if (n_chunks > 65535 || Hkv > 65535 || B > 65535 || Hq > 65535) return ATTN_ERR_UNSUPPORTED;
+  return decode_common(q, k, v, attn_mask, nullptr, nullptr, S_ctx, false, softmax_scale, num_kv_groups, B, Hq,
+                       Hkv, S_ctx, D, out, workspace, workspace_bytes, stream);
+}
 
-  DecodeLaunch L;
-  memset(&L, 0, sizeof L);
-  L.q = static_cast<const __bf16 *>(q);
-  L.k = static_cast<const __bf16 *>(k);
-  L.v = static_cast<const __bf16 *>(v);
-  L.mask = attn_mask;
-  L.B = B;
-  L.Hq = Hq;
-  L.Hkv = Hkv;
-  L.G = num_kv_groups;
-  L.S_ctx = S_ctx;
-  L.n_chunks = n_chunks;
-  L.c = softmax_scale * 1.4426950408889634f;
-  const int64_t parts = (int64_t)B * Hq * n_chunks;
-  L.ws_o = static_cast<float *>(workspace);
-  L.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + ((parts * D * 4) + 255) / 256 * 256);
-  L.out = static_cast<__bf16 *>(out);
-  return hip_status(launch_decode(L, stream));
+int attn_decode_gqa_window(const void *q, const void *k, const void *v, const float *attn_mask,
+                           const int32_t *key_begin, const int32_t *key_end, int max_keys, float softmax_scale,
+                           int num_kv_groups, int B, int Hq, int Hkv, int S_ctx, int D, void *out, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (max_keys <= 0) return ATTN_ERR_INVALID_ARG;
+  if ((key_begin && (reinterpret_cast<uintptr_t>(key_begin) & 3u)) ||
+      (key_end && (reinterpret_cast<uintptr_t>(key_end) & 3u)))
+    return ATTN_ERR_INVALID_ARG;
+  return decode_common(q, k, v, attn_mask, key_begin, key_end, max_keys, true, softmax_scale, num_kv_groups, B,
+                       Hq, Hkv, S_ctx, D, out, workspace, workspace_bytes, stream);
 }
 
 int attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache, float k_scale, float v_scale,

@@ -1,13 +1,20 @@
-// GQA single-token decode, head_dim 256, split-K ("flash-decode") + combine.
+// GQA single-token decode, head_dim 256 or 512, split-K ("flash-decode") +
+// combine, over the whole cache or over a per-sequence key range.
 //
 // head_dim>128 (256/512) GQA Flash-Decode NKI Kernel for AWS Trainium,
 // "Input contract" fixes the operands (q [B,Hq,1,D], k/v [B,Hkv,S_ctx,D],
 // additive 0/-inf mask [B,1,1,S_ctx], softmax_scale, num_kv_groups); its
 // "Perf caveat" and "Future performance follow-on" note that one program
 // re-streaming the whole cache is bandwidth-starved and that the KV stream
-// should be sharded over many programs.  Here every (batch, KV head, chunk of
+// should be sharded over many programs, and that sliding-window layers need
+// only the most recent window of keys.  Here every (batch, KV head, chunk of
 // 64 keys) is its own workgroup, the G query heads of a KV head share the
-// one pass over its K/V, and a second kernel merges the chunk partials.
+// one pass over its K/V, and a second kernel merges the chunk partials.  With
+// a key range the grid spans only the chunks the widest range can touch,
+// counted from each sequence's own first key (a windowed gather: keys before
+// the window are never fetched and get no workgroup).  The introduction of
+// the same page names the two head sizes: 256 on sliding-window layers, 512
+// on global ones.
 //
 // Split kernel, per workgroup (4 waves of kDecNG groups of 16 keys; with more
 // than one group the loads of group g+1 are in flight while group g is
@@ -18,8 +25,8 @@
 //   mask : additive, in log2 units; keys it removes are never fetched (their
 //          buffer offsets fall out of range), a wave with no live key skips
 //          the loads;
-//   PV   : on the VALU, each lane owning 4 of the 256 output columns, V read
-//          with 512 contiguous bytes per key per wave;
+//   PV   : on the VALU, each lane owning D/64 of the D output columns, V read
+//          with 2D contiguous bytes per key per wave;
 //   merge: the 4 wave partials combine through LDS; the chunk partial
 //          (m, l in log2 units, unnormalised o) goes to the workspace.
 // Combine kernel, per (b, query head): M = max m_c, L = sum 2^(m_c-M) l_c,
@@ -29,7 +36,6 @@
 
 namespace mi355 {
 
-constexpr int kDecD = 256;
 constexpr int kDecKW = 16;                      // keys per group (one 16-key MFMA block)
 constexpr int kDecNG = 1;                       // groups per wave
 constexpr int kDecWaves = 4;                    // waves per workgroup
@@ -49,56 +55,105 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dec_rsrc(const void *base, uin
                                            (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-// One group of 16 keys in registers: K as the A operand of the QK MFMA
-// (lane l: key l%16, d = 32s + 8(l/16) .. +7) and V as 16 rows of the lane's
-// 4 output columns.
-struct DecStage {
-  u32x4_t k[kDecD / 32];
-  u32x2_t v[kDecKW];
+// Per-lane V slice: D/64 bf16 columns of one key (4 -> 8 bytes, 8 -> 16).
+template <int D> struct DecV;
+template <> struct DecV<256> {
+  typedef u32x2_t type;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNT));
+  }
+};
+template <> struct DecV<512> {
+  typedef u32x4_t type;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT));
+  }
 };
 
-// Issue the loads of group g (keys g*16 .. g*16+15 of the wave); keys the
-// mask removes get an out-of-range offset and are never fetched.
-__device__ __forceinline__ void dec_load(DecStage &st, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+// One group of 16 keys in registers: K as the A operand of the QK MFMA
+// (lane l: key l%16, d = 32s + 8(l/16) .. +7) and V as 16 rows of the lane's
+// D/64 output columns.
+template <int D>
+struct DecStage {
+  u32x4_t k[D / 32];
+  typename DecV<D>::type v[kDecKW];
+};
+
+// Issue the loads of group g (keys g*16 .. g*16+15 of the wave); keys that
+// are not live get an out-of-range offset and are never fetched.
+template <int D>
+__device__ __forceinline__ void dec_load(DecStage<D> &st, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                          uint64_t live, int g, int lane) {
   const int gq = lane & 15, quad = lane >> 4;
   const int kk = g * kDecKW + gq;
-  const uint32_t koff = ((live >> kk) & 1) ? kk * (kDecD * 2) + 16 * quad : kOOB;
+  const uint32_t koff = ((live >> kk) & 1) ? kk * (D * 2) + 16 * quad : kOOB;
 #pragma unroll
-  for (int s = 0; s < kDecD / 32; ++s)
+  for (int s = 0; s < D / 32; ++s)
     st.k[s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 64 * s, 0, kNT));
 #pragma unroll
   for (int j = 0; j < kDecKW; ++j) {
     const int kj = g * kDecKW + j;
-    const uint32_t voff = ((live >> kj) & 1) ? kj * (kDecD * 2) + 8 * lane : kOOB;
-    st.v[j] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 0, kNT));
+    const uint32_t voff = ((live >> kj) & 1) ? kj * (D * 2) + (D / 32) * lane : kOOB;
+    st.v[j] = DecV<D>::load(rv, voff);
   }
 }
 
-template <int G>
-__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(5))) void decode_split_kernel(DecodeLaunch a) {
+// Key range of sequence b: [beg, end) clamped to [0, S_ctx], then cut to its
+// last max_keys keys; chunk 0 of the sequence starts at beg rounded down to
+// a chunk boundary.
+struct DecRange {
+  int beg, end, base;
+};
+__device__ __forceinline__ DecRange dec_range(const DecodeLaunch &a, int b) {
+  int end = a.S_ctx, beg = 0;
+  if (a.key_end) end = min(max(a.key_end[b], 0), a.S_ctx);
+  if (a.key_begin) beg = min(max(a.key_begin[b], 0), end);
+  beg = max(beg, end - a.max_keys);
+  return DecRange{beg, end, beg - beg % kDecChunk};
+}
+
+// The accumulator of one query head: the lane's D/64 output columns.
+template <int D> struct DecAcc { float x[D / 64]; };
+
+template <int D> constexpr int dec_waves_per_eu() { return D == 256 ? 5 : 2; }
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<D>())))
+void decode_split_kernel(DecodeLaunch a) {
   constexpr int KW = kDecKW, NW = kDecWaves, NG = kDecNG, WK = NG * KW;  // WK: keys per wave
+  constexpr int CPL = D / 64;                                             // output columns per lane
   static_assert(WK <= 64, "one liveness bit per lane");
-  __shared__ __attribute__((aligned(16))) float sc[NW][G][KW];
-  __shared__ __attribute__((aligned(16))) float red_o[NW][G][kDecD];
+  // LDS: each wave's copy of the G query rows and its score tile (used in
+  // the key loop), then the wave partials of the merge.  When the three
+  // together would cap occupancy the merge buffer reuses the first two,
+  // behind one more barrier.
+  constexpr int QS_B = NW * G * D * 2, SC_B = NW * G * KW * 4, RO_B = NW * G * D * 4;
+  constexpr bool ALIAS = QS_B + SC_B + RO_B > 48 * 1024;
+  constexpr int SMEM_B = ALIAS ? (QS_B + SC_B > RO_B ? QS_B + SC_B : RO_B) : QS_B + SC_B + RO_B;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_B];
   __shared__ float red_ml[NW][G][2];
-  __shared__ __attribute__((aligned(16))) __bf16 qs[NW][G][kDecD];  // each wave's copy of the G query rows
+  auto qs = reinterpret_cast<__bf16(*)[G][D]>(smem);
+  auto sc = reinterpret_cast<float(*)[G][KW]>(smem + QS_B);
+  auto red_o = reinterpret_cast<float(*)[G][D]>(smem + (ALIAS ? 0 : QS_B + SC_B));
 
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const DecRange R = dec_range(a, b);
   const float *mrow = a.mask ? a.mask + (int64_t)b * a.S_ctx : nullptr;
   const int64_t part0 = ((int64_t)b * a.Hq + (int64_t)kvh * G) * a.n_chunks + chunk;  // head g adds g*n_chunks
-  const int key0 = chunk * kDecChunk + wave * WK;
+  const int ckey0 = R.base + chunk * kDecChunk;  // first key of the chunk
+  const int key0 = ckey0 + wave * WK;
 
   // Every wave reads the mask of the whole chunk (lane l: key l of the chunk,
-  // log2 units, -inf where removed) and votes: a chunk with no live key
-  // writes its empty statistics and exits without touching K/V or the LDS
-  // (every wave takes the same branch, no barrier needed).
+  // log2 units, -inf where removed or outside the range) and votes: a chunk
+  // with no live key writes its empty statistics and exits without touching
+  // K/V or the LDS (every wave takes the same branch, no barrier needed).
+  // Keys outside the range never read the mask.
   static_assert(kDecChunk <= 64, "one chunk key per lane");
   float mk_lane = -INFINITY;
   if (lane < kDecChunk) {
-    const int key = chunk * kDecChunk + lane;
-    const float mv = key < a.S_ctx ? (mrow ? mrow[key] : 0.0f) : -INFINITY;
+    const int key = ckey0 + lane;
+    const float mv = (key >= R.beg && key < R.end) ? (mrow ? mrow[key] : 0.0f) : -INFINITY;
     mk_lane = mv == -INFINITY ? -INFINITY : mv * kLog2e;
   }
   const uint64_t live_chunk = __ballot(mk_lane != -INFINITY);
@@ -112,37 +167,37 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   }
   const uint64_t live = (live_chunk >> (wave * WK)) & ((WK == 64) ? ~0ull : ((1ull << WK) - 1));
 
-  // The G query rows (G * 512 B) are copied into this wave's LDS slice: the
-  // q^T B-operand fragments are read from there right before their MFMAs,
-  // which keeps them out of the registers.  Issued before the liveness vote
-  // is used, so the load latency overlaps the mask read.
+  // The G query rows (G * 2D bytes) are copied into this wave's LDS slice:
+  // the q^T B-operand fragments are read from there right before their
+  // MFMAs, which keeps them out of the registers.
   const int gq = lane & 15, quad = lane >> 4;
   {
-    const auto rq = dec_rsrc(a.q + ((int64_t)b * a.Hq + (int64_t)kvh * G) * kDecD, G * kDecD * 2);
+    const auto rq = dec_rsrc(a.q + ((int64_t)b * a.Hq + (int64_t)kvh * G) * D, G * D * 2);
 #pragma unroll
-    for (int i = 0; i < (G * kDecD * 2 + 1023) / 1024; ++i) {
+    for (int i = 0; i < (G * D * 2 + 1023) / 1024; ++i) {
       const uint32_t off = (lane + 64 * i) * 16;
-      if (off < G * kDecD * 2)
+      if (off < G * D * 2)
         *reinterpret_cast<u32x4_t *>(reinterpret_cast<char *>(&qs[wave][0][0]) + off) =
             __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
   }
 
   float m[G], l[G];
-  f32x4_t o[G];
+  DecAcc<D> o[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.0f;
-    o[g] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[g].x[c] = 0.0f;
   }
 
   if (live != 0) {
     const int64_t row0 = ((int64_t)b * a.Hkv + kvh) * a.S_ctx + key0;
-    const uint32_t span = (uint32_t)max(min(WK, a.S_ctx - key0), 0) * (kDecD * 2);
-    const auto rk = dec_rsrc(a.k + row0 * kDecD, span), rv = dec_rsrc(a.v + row0 * kDecD, span);
-    DecStage st[NG < 2 ? 1 : 2];
-    dec_load(st[0], rk, rv, live, 0, lane);
+    const uint32_t span = (uint32_t)max(min(WK, R.end - key0), 0) * (D * 2);
+    const auto rk = dec_rsrc(a.k + row0 * D, span), rv = dec_rsrc(a.v + row0 * D, span);
+    DecStage<D> st[NG < 2 ? 1 : 2];
+    dec_load<D>(st[0], rk, rv, live, 0, lane);
 
 #pragma unroll
     for (int grp = 0; grp < NG; ++grp) {
@@ -151,16 +206,16 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
         // mask keeps the compiler from hoisting every group's loads to the top
         uint64_t live_n = live;
         asm volatile("" : "+s"(live_n));
-        dec_load(st[(grp + 1) & 1], rk, rv, live_n, grp + 1, lane);
+        dec_load<D>(st[(grp + 1) & 1], rk, rv, live_n, grp + 1, lane);
       }
-      const DecStage &cs = st[NG < 2 ? 0 : grp & 1];
+      const DecStage<D> &cs = st[NG < 2 ? 0 : grp & 1];
       // q^T fragment: lane l holds q[g = l%16][32s + 8(l/16) .. +7], zero for g >= G
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's copy of q is in LDS
       __builtin_amdgcn_wave_barrier();
       const char *qrow = reinterpret_cast<const char *>(&qs[wave][gq < G ? gq : 0][0]) + 16 * quad;
       f32x4_t s4 = {0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < kDecD / 32; ++s) {
+      for (int s = 0; s < D / 32; ++s) {
         const u32x4_t qv = *reinterpret_cast<const u32x4_t *>(qrow + 64 * s);
         s4 = mfma16(as_bf16x8(cs.k[s]), as_bf16x8(gq < G ? qv : u32x4_t{0, 0, 0, 0}), s4);
       }
@@ -188,15 +243,18 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
         m[g] = m_new;
         float ls = l[g] * alpha;
-        f32x4_t acc = o[g] * alpha;
+        DecAcc<D> acc;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc.x[c] = o[g].x[c] * alpha;
 #pragma unroll
         for (int j = 0; j < KW; ++j) {
           const float pj = fast_exp2(sc[wave][g][j] - m_use);
           ls += pj;
-          acc[0] += pj * bf16_lo(cs.v[j][0]);
-          acc[1] += pj * bf16_hi(cs.v[j][0]);
-          acc[2] += pj * bf16_lo(cs.v[j][1]);
-          acc[3] += pj * bf16_hi(cs.v[j][1]);
+#pragma unroll
+          for (int w = 0; w < CPL / 2; ++w) {
+            acc.x[2 * w] += pj * bf16_lo(cs.v[j][w]);
+            acc.x[2 * w + 1] += pj * bf16_hi(cs.v[j][w]);
+          }
         }
         l[g] = ls;
         o[g] = acc;
@@ -206,20 +264,24 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   }
 
   // Merge the wave partials (fixed order) and write the chunk partial.
+  if (ALIAS) __syncthreads();  // every wave is done with its q copy and scores
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    *reinterpret_cast<f32x4_t *>(&red_o[wave][g][4 * lane]) = o[g];
+#pragma unroll
+    for (int c = 0; c < CPL; c += 4)
+      *reinterpret_cast<f32x4_t *>(&red_o[wave][g][CPL * lane + c]) =
+          f32x4_t{o[g].x[c], o[g].x[c + 1], o[g].x[c + 2], o[g].x[c + 3]};
     if (lane == 0) {
       red_ml[wave][g][0] = m[g];
       red_ml[wave][g][1] = l[g];
     }
   }
   __syncthreads();
-  // thread t handles column t % D of heads t / D, t / D + NW*64/D, ...
+  // thread t handles (head, column) pairs t, t + 256, ... of the G x D partial
+  static_assert((G * D) % (64 * NW) == 0, "whole rounds of the merge");
 #pragma unroll
-  for (int g0 = 0; g0 < G; g0 += 64 * NW / kDecD) {
-    const int g = g0 + tid / kDecD, col = tid % kDecD;
-    if (g >= G) break;
+  for (int i0 = 0; i0 < G * D; i0 += 64 * NW) {
+    const int g = (i0 + tid) / D, col = (i0 + tid) % D;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, red_ml[w][g][0]);
@@ -232,7 +294,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       acc += red_o[w][g][col] * sw;
     }
     const int64_t part = part0 + (int64_t)g * a.n_chunks;
-    if (M != -INFINITY) a.ws_o[part * kDecD + col] = acc;
+    if (M != -INFINITY) a.ws_o[part * D + col] = acc;
     if (col == 0) {
       a.ws_ml[part * 2 + 0] = M;
       a.ws_ml[part * 2 + 1] = L;
@@ -247,6 +309,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 // from lane c.  Dead chunks (m_c = -inf, partial never written) and chunks
 // whose weight underflows are selected away, not branched around.  The chunk
 // order is fixed, so the result is deterministic.
+template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeLaunch a) {
   const int slice = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int64_t p0 = ((int64_t)b * a.Hq + hq) * a.n_chunks;
@@ -259,7 +322,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeLaunch a) {
     const float mc = lane < nc ? ml[0] : -INFINITY;
     float oc[64];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) oc[i] = a.ws_o[(p0 + c0 + (i < nc ? i : 0)) * kDecD + d];
+    for (int i = 0; i < 64; ++i) oc[i] = a.ws_o[(p0 + c0 + (i < nc ? i : 0)) * D + d];
     const float Mb = fmaxf(M, wave_max(mc));
     const float Mu = Mb == -INFINITY ? 0.0f : Mb;
     const float w = mc == -INFINITY ? 0.0f : fast_exp2(mc - Mu);
@@ -274,22 +337,31 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeLaunch a) {
     M = Mb;
   }
   const float r = L > 0.0f ? acc / L : 0.0f;
-  a.out[((int64_t)b * a.Hq + hq) * kDecD + d] = (__bf16)r;
+  a.out[((int64_t)b * a.Hq + hq) * D + d] = (__bf16)r;
 }
 
-hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
+template <int D>
+static hipError_t launch_decode_d(const DecodeLaunch &a, hipStream_t stream) {
   const dim3 grid(a.n_chunks, a.Hkv, a.B), block(64 * kDecWaves);
   switch (a.G) {
-    case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(decode_split_kernel<4>, grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(decode_split_kernel<8>, grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<D, 4>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_split_kernel<D, 8>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(kDecD / 64, a.Hq, a.B), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(D / 64, a.Hq, a.B), dim3(64), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
+  switch (a.D) {
+    case 256: return launch_decode_d<256>(a, stream);
+    case 512: return launch_decode_d<512>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 int decode_chunk_keys() { return kDecChunk; }

@@ -38,7 +38,9 @@ struct PrefillLaunch {
 struct DecodeLaunch {
   const __bf16 *q, *k, *v;
   const float *mask;  // nullable [B, S_ctx]
-  int B, Hq, Hkv, G, S_ctx, n_chunks;
+  const int32_t *key_begin, *key_end;  // nullable [B]: per-sequence key range
+  int max_keys;       // keys per sequence the grid covers (S_ctx without a range)
+  int B, Hq, Hkv, G, S_ctx, D, n_chunks;
   float c;            // softmax_scale * log2(e)
   float *ws_o;        // [B*Hq*n_chunks, D]
   float *ws_ml;       // [B*Hq*n_chunks, 2]

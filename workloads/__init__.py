@@ -162,8 +162,9 @@ def length_mask(lens: torch.Tensor, S_ctx: int) -> torch.Tensor:
 
 def decode_gemma(seed: int = 1004, B: int = 8, Hq: int = 16, Hkv: int = 8, S_ctx: int = 4096,
                  D: int = 256, lens=None) -> DecodeCase:
-    """Gemma-style GQA single-token decode at head_dim 256: bf16 entries
-    N(0, 0.25^2), softmax_scale 1.0, len_b ~ U{1..S_ctx}."""
+    """Gemma-style GQA single-token decode at head_dim D (256: sliding-window
+    layers, 512: global layers): bf16 entries N(0, 0.25^2), softmax_scale 1.0,
+    len_b ~ U{1..S_ctx}."""
     g = _gen(seed)
     q = to_bf16(torch.randn(B, Hq, 1, D, generator=g) * 0.25)
     k = to_bf16(torch.randn(B, Hkv, S_ctx, D, generator=g) * 0.25)

@@ -35,6 +35,12 @@ def decode_bytes(lens, Hkv: int, Hq: int, S_ctx: int, D: int, elem: int = 2, mas
     return kv + B * S_ctx * mask_elem + 2 * B * Hq * D * elem
 
 
+def decode_window_bytes(n_keys, Hkv: int, Hq: int, D: int, elem: int = 2) -> int:
+    """K+V rows inside each sequence's key range (no mask read), q and out."""
+    B = len(n_keys)
+    return sum(int(n) for n in n_keys) * Hkv * D * elem * 2 + 2 * B * Hq * D * elem
+
+
 def decode_dense_bytes(B: int, Hkv: int, Hq: int, S_ctx: int, D: int, elem: int = 2) -> int:
     return B * Hkv * S_ctx * D * elem * 2 + B * S_ctx * 4 + 2 * B * Hq * D * elem
 
