@@ -44,6 +44,7 @@ def lib():
         L.oracle_layernorm.argtypes = [P, I64, I, P, P, D, P, P, P]
         L.oracle_encoder_block.argtypes = [P, P, P, I, P, I, I, I, I, D, P, P, P, D, P, P, P, P, P]
         L.oracle_prefill_paged.argtypes = [P, I, P, P, D, D, P, I, I, I, I, D, I, I, I, I, P, I, P, P]
+        L.oracle_prefill_causal.argtypes = [P, I, P, P, D, D, P, I, I, I, I, P, P, I, D, I, I, I, I, P, I, P, P]
         L.oracle_decode.argtypes = [P, I, I64, P]
         L.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_f64.restype = D
@@ -223,4 +224,34 @@ def prefill_paged(q, k_cache, v_cache, k_scale, v_scale, block_table, L_act, sca
                                     _ptr(out), _ptr(lse))
     if rc:
         raise ValueError(f"oracle_prefill_paged rc={rc}")
+    return (out, lse) if return_lse else out
+
+
+def prefill_causal(q, k_cache, v_cache, k_scale, v_scale, block_table, L_act, k_cur, v_cur, scale, rows,
+                   return_lse: bool = False):
+    """Paged history plus causal current-token prefill for token indices
+    ``rows`` and all query heads: token t attends history keys 0..L_act-1 and
+    current keys 0..t.  q [Hq,Lq,D]; caches [num_blocks,Hkv,bs,D] e4m3fn;
+    k_cur/v_cur [Hkv,Lq,D]; returns out [Hq,len(rows),D] fp64 (and lse)."""
+    import torch
+
+    qr, qt = _raw(q)
+    kr, kt = _raw(k_cur)
+    vr, vt = _raw(v_cur)
+    if kt != vt:
+        raise TypeError("prefill_causal: k_cur and v_cur must share a dtype")
+    kc = k_cache.detach().cpu().contiguous().view(torch.uint8).numpy()
+    vc = v_cache.detach().cpu().contiguous().view(torch.uint8).numpy()
+    bt = np.ascontiguousarray(np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table),
+                              dtype=np.int32)
+    r = np.ascontiguousarray(np.asarray(rows.cpu() if hasattr(rows, "cpu") else rows), dtype=np.int64)
+    Hq, Lq, D = qr.shape
+    nb, Hkv, bs, _ = kc.shape
+    out = np.empty((Hq, r.size, D))
+    lse = np.empty((Hq, r.size))
+    rc = lib().oracle_prefill_causal(_ptr(qr), qt, _ptr(kc), _ptr(vc), float(k_scale), float(v_scale), _ptr(bt),
+                                     bt.size, nb, bs, int(L_act), _ptr(kr), _ptr(vr), kt, float(scale), Hq, Hkv, Lq,
+                                     D, _ptr(r), r.size, _ptr(out), _ptr(lse))
+    if rc:
+        raise ValueError(f"oracle_prefill_causal rc={rc}")
     return (out, lse) if return_lse else out

@@ -34,6 +34,8 @@
  * Context-Parallel Attention POC, "Layout" and "Benchmark": runtime additive
  * score bias derived from actual_history_len; the final partial block is
  * padded and biased).  Keys are e4m3fn codes times one fp32 scale per tensor.
+ * The prefill with current-token attention (oracle_prefill_causal) is the
+ * one causal computation here: token t also attends current tokens 0..t.
  */
 #include <math.h>
 #include <stdint.h>
@@ -255,4 +257,69 @@ int oracle_prefill_paged(const void *q, int q_dtype, const uint8_t *k_cache, con
     free(kd);
     free(vd);
     return 0;
+}
+
+/*
+ * Prefill with current-token attention: query token t of head h attends the
+ * L_act history keys of the paged cache (gathered and biased as above),
+ * followed by the keys of the current tokens 0..t of its own KV head
+ * (causal).  Prefill Context-Parallel Attention POC, introduction: its first
+ * version leaves out attention among the current tokens; this adds it.  The
+ * current tokens' K/V are k_cur/v_cur [Hkv, Lq, D] in cur_dtype, with no
+ * scale.  L_act may be 0 (no history).  The softmax runs over the joined key
+ * list in that order: history keys 0..L_act-1, then current keys 0..t.
+ * out [Hq, n_rows, D] fp64, lse nullable [Hq, n_rows].
+ */
+int oracle_prefill_causal(const void *q, int q_dtype, const uint8_t *k_cache, const uint8_t *v_cache,
+                          double k_scale, double v_scale, const int32_t *block_table, int max_blocks,
+                          int num_blocks, int bs, int L_act, const void *k_cur, const void *v_cur, int cur_dtype,
+                          double scale, int Hq, int Hkv, int Lq, int D, const int64_t *rows, int n_rows,
+                          double *out, double *lse) {
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || bs <= 0 || D <= 0 || Lq <= 0 || L_act < 0 ||
+        L_act > (int64_t)max_blocks * bs)
+        return -1;
+    const int G = Hq / Hkv;
+    const int64_t n = (int64_t)L_act + Lq; /* keys per KV head in the joined list */
+    double *kd = (double *)malloc(sizeof(double) * (size_t)Hkv * n * D);
+    double *vd = (double *)malloc(sizeof(double) * (size_t)Hkv * n * D);
+    if (!kd || !vd) { free(kd); free(vd); return -2; }
+    for (int h = 0; h < Hkv; ++h) {
+        for (int64_t j = 0; j < L_act; ++j) {
+            int32_t phys = block_table[j / bs];
+            if (phys < 0 || phys >= num_blocks) { free(kd); free(vd); return -3; }
+            int64_t src = (((int64_t)phys * Hkv + h) * bs + j % bs) * D;
+            for (int d = 0; d < D; ++d) {
+                kd[((int64_t)h * n + j) * D + d] = oracle_e4m3_to_f64(k_cache[src + d]) * k_scale;
+                vd[((int64_t)h * n + j) * D + d] = oracle_e4m3_to_f64(v_cache[src + d]) * v_scale;
+            }
+        }
+        for (int64_t j = 0; j < Lq; ++j)
+            for (int d = 0; d < D; ++d) {
+                int64_t src = ((int64_t)h * Lq + j) * D + d;
+                kd[((int64_t)h * n + L_act + j) * D + d] = load_elem(k_cur, cur_dtype, src);
+                vd[((int64_t)h * n + L_act + j) * D + d] = load_elem(v_cur, cur_dtype, src);
+            }
+    }
+    const int64_t total = (int64_t)Hq * n_rows;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * n);
+        double *qr = (double *)malloc(sizeof(double) * D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < total; ++r) {
+            int h = (int)(r / n_rows);
+            int64_t t = rows[r % n_rows];
+            if (t < 0 || t >= Lq) { bad = 1; continue; }
+            for (int d = 0; d < D; ++d) qr[d] = load_elem(q, q_dtype, ((int64_t)h * Lq + t) * D + d);
+            const int64_t kv0 = (int64_t)(h / G) * n * D;
+            /* the first L_act + t + 1 keys of the joined list: history, then current 0..t */
+            attend_row(qr, kd + kv0, vd + kv0, NULL, L_act + t + 1, D, scale, s, out + r * D, lse ? lse + r : NULL);
+        }
+        free(s);
+        free(qr);
+    }
+    free(kd);
+    free(vd);
+    return bad ? -4 : 0;
 }

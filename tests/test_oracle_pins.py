@@ -341,3 +341,87 @@ def test_decode_window_empty_range_is_zero():
     assert np.all(out[0] == 0.0)
     ref = _torch_sdpa64(q[1:], k[1:, :, 6:], v[1:, :, 6:], 1.0)
     assert _relmax(out[1:], ref) < 1e-12
+
+
+# ----------------------------------------------------------------------------- prefill with current tokens
+
+
+def _paged_case(seed, Hq=8, Hkv=2, Lq=12, D=16, bs=8, nb=5, L_act=29):
+    g = torch.Generator().manual_seed(seed)
+    q = _rand(g, Hq, Lq, D).to(torch.bfloat16)
+    logical_k = (torch.randn(nb * bs, Hkv, D, generator=g) * 2).to(torch.float8_e4m3fn)
+    logical_v = (torch.randn(nb * bs, Hkv, D, generator=g) * 2).to(torch.float8_e4m3fn)
+    bt = torch.randperm(nb, generator=g).to(torch.int32)
+    kc = torch.empty(nb, Hkv, bs, D, dtype=torch.float8_e4m3fn)
+    vc = torch.empty_like(kc)
+    for i in range(nb):
+        kc[bt[i]] = logical_k[i * bs:(i + 1) * bs].transpose(0, 1)
+        vc[bt[i]] = logical_v[i * bs:(i + 1) * bs].transpose(0, 1)
+    k_cur = _rand(g, Hkv, Lq, D).to(torch.bfloat16)
+    v_cur = _rand(g, Hkv, Lq, D).to(torch.bfloat16)
+    return q, logical_k, logical_v, bt, kc, vc, k_cur, v_cur
+
+
+def test_prefill_causal_without_history_is_causal_sdpa():
+    """L_act = 0: plain causal self-attention of the current tokens (torch
+    fp64 SDPA with is_causal, GQA heads contiguous)."""
+    q, _, _, bt, kc, vc, k_cur, v_cur = _paged_case(18)
+    rows = torch.tensor([0, 1, 7, 11])
+    out = oracle.prefill_causal(q, kc, vc, 0.5, 0.25, bt, 0, k_cur, v_cur, 0.3, rows)
+    G = q.shape[0] // k_cur.shape[0]
+    kq = k_cur.to(torch.float64).repeat_interleave(G, dim=0)[None]
+    vq = v_cur.to(torch.float64).repeat_interleave(G, dim=0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(q.to(torch.float64)[None], kq, vq, is_causal=True,
+                                                           scale=0.3)[0]
+    assert _relmax(out, ref[:, rows].numpy()) < 1e-12
+    # token 0 sees exactly one key: its own value row
+    assert _relmax(out[:, 0], v_cur.to(torch.float64).repeat_interleave(G, dim=0)[:, 0].numpy()) < 1e-15
+
+
+def test_prefill_causal_equals_dense_masked_sdpa_over_joined_keys():
+    """History keys (dequantised, first L_act logical keys) joined with the
+    current keys, with an explicit -inf on current keys after the query's own
+    token; torch fp64 SDPA on that."""
+    q, lk, lv, bt, kc, vc, k_cur, v_cur = _paged_case(19)
+    L_act, Lq, ks, vs = 29, q.shape[1], 0.5, 0.125
+    rows = torch.tensor([11, 0, 4, 5])
+    out, lse = oracle.prefill_causal(q, kc, vc, ks, vs, bt, L_act, k_cur, v_cur, 0.2, rows, return_lse=True)
+    kd = torch.cat([(lk[:L_act].to(torch.float64) * ks).transpose(0, 1), k_cur.to(torch.float64)], dim=1)
+    vd = torch.cat([(lv[:L_act].to(torch.float64) * vs).transpose(0, 1), v_cur.to(torch.float64)], dim=1)
+    mask = torch.zeros(Lq, L_act + Lq, dtype=torch.float64)
+    for t in range(Lq):
+        mask[t, L_act + t + 1:] = -math.inf
+    G = q.shape[0] // kd.shape[0]
+    qs = q.to(torch.float64)[:, rows]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qs[None], kd.repeat_interleave(G, dim=0)[None], vd.repeat_interleave(G, dim=0)[None],
+        attn_mask=mask[rows][None, None], scale=0.2)[0]
+    assert _relmax(out, ref.numpy()) < 1e-12
+    s = 0.2 * torch.einsum("hrd,hkd->hrk", qs, kd.repeat_interleave(G, dim=0)) + mask[rows][None]
+    assert np.max(np.abs(lse - torch.logsumexp(s, dim=-1).numpy())) < 1e-12
+
+
+def test_prefill_causal_is_the_lse_merge_of_history_and_current():
+    """The joined softmax equals the log-sum-exp merge of the history-only
+    result (oracle.prefill_paged) and causal attention over the current
+    tokens alone: o = (e^{lse_h} o_h + e^{lse_c} o_c) / (e^{lse_h} + e^{lse_c})."""
+    q, _, _, bt, kc, vc, k_cur, v_cur = _paged_case(20)
+    rows = torch.tensor([0, 6, 11])
+    o, lse = oracle.prefill_causal(q, kc, vc, 0.5, 0.125, bt, 29, k_cur, v_cur, 0.2, rows, return_lse=True)
+    oh, lh = oracle.prefill_paged(q, kc, vc, 0.5, 0.125, bt, 29, 0.2, rows, return_lse=True)
+    oc, lc = oracle.prefill_causal(q, kc, vc, 0.5, 0.125, bt, 0, k_cur, v_cur, 0.2, rows, return_lse=True)
+    M = np.maximum(lh, lc)
+    wh, wc = np.exp(lh - M), np.exp(lc - M)
+    merged = (wh[..., None] * oh + wc[..., None] * oc) / (wh + wc)[..., None]
+    assert _relmax(o, merged) < 1e-12
+    assert np.max(np.abs(lse - (M + np.log(wh + wc)))) < 1e-12
+
+
+def test_prefill_causal_ignores_future_tokens_bitwise():
+    q, _, _, bt, kc, vc, k_cur, v_cur = _paged_case(21)
+    rows = torch.tensor([0, 3, 5])
+    o1 = oracle.prefill_causal(q, kc, vc, 0.5, 0.125, bt, 29, k_cur, v_cur, 0.2, rows)
+    k2, v2 = k_cur.clone(), v_cur.clone()
+    k2[:, 6:] = 3e4
+    v2[:, 6:] = -3e4
+    assert np.array_equal(oracle.prefill_causal(q, kc, vc, 0.5, 0.125, bt, 29, k2, v2, 0.2, rows), o1)
