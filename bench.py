@@ -109,13 +109,15 @@ def cpu_baseline(pre, n_rows: int):
                       f"(fp64 C oracle incl. KV decode), {dt:.1f} s wall"}
 
 
-def time_next_workloads(taa, dev, flush, reps: int = 20):
+def time_next_workloads(taa, dev, flush, pre_dev, reps: int = 20):
     """Workload variants beyond the step (reported, not part of `value`):
     the 64-frame V-JEPA 2 clip (8192 tokens), a gte-base batch right-padded to
     512 tokens with ragged real lengths (additive key mask), both timed as
     back-to-back launches between two HIP events after 3 warm-up calls; and
     the decode at head_dim 512 (global layers) and over a 1024-key sliding
-    window at head_dim 256, each call timed alone after the cache flush."""
+    window at head_dim 256, each call timed alone after the cache flush; and
+    the paged prefill with causal attention among the 4096 current tokens
+    (the history inputs of the step, already on the device)."""
     out = {}
 
     def timed_flushed(fn):
@@ -188,6 +190,34 @@ def time_next_workloads(taa, dev, flush, reps: int = 20):
     out["gemma_sliding_window1024_decode_d256_b8_ctx4096"] = {
         "median_ms": ms, "lens": lens, "window": win, "bytes": b, "gbps": b / (ms * 1e-3) / 1e9,
         "frac_hbm_peak": b / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBPS}
+    del q, k, v
+
+    pre, p_q, p_k, p_v, p_bt = pre_dev
+    kc, vc = (t.to(dev) for t in W.prefill_current_kv(1105, pre.Hkv, pre.Lq, pre.D))
+    o = torch.empty_like(p_q)
+    r3 = max(3, reps // 5)
+
+    def timed_b2b(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    pws = torch.empty(taa.attn_prefill_paged_causal_workspace_size(pre.Hq, pre.Hkv, pre.Lq, pre.D),
+                      dtype=torch.uint8, device=dev)
+    ms = timed_b2b(lambda: taa.attn_prefill_paged_causal(p_q, p_k, p_v, pre.k_scale, pre.v_scale, p_bt, pre.L_act,
+                                                         kc, vc, pre.scale, pre.G, out=o, workspace=pws), r3)
+    f_hist = acc.prefill_flops(pre.Lq, pre.Hq, pre.L_act, pre.D)
+    f_cur = acc.causal_flops(pre.Lq, pre.Hq, pre.D)
+    tf = (f_hist + f_cur) / (ms * 1e-3) / 1e12
+    out["paged_fp8_prefill_q4096_hist120000_plus_causal_current"] = {
+        "ms": ms, "tflops": tf, "frac_bf16_peak": tf / acc.PEAK_BF16_TFLOPS, "flops_history": f_hist,
+        "flops_current": f_cur}
     return out
 
 
@@ -410,7 +440,7 @@ def main():
                     "frac": p["frac_hbm_peak"], "traffic": None, "kernel": "decode_split_kernel+decode_combine_kernel"}
 
     if args.only in ("all", "next"):
-        parts["next"] = time_next_workloads(taa, dev, flush)
+        parts["next"] = time_next_workloads(taa, dev, flush, (pre, p_q, p_k, p_v, p_bt))
 
     cpu = None
     if args.cpu_rows > 0 and run_pre:

@@ -14,7 +14,8 @@
  *  - Device DATA is not inspected on the host: a block-table entry outside
  *    [0, num_blocks) is undefined behaviour.
  *  - Results are bitwise deterministic: the same inputs give the same bits,
- *    and a query row's output does not depend on any other batch entry.
+ *    and a query row's output does not depend on any other query row, head
+ *    or batch entry (every online-softmax decision is taken per row).
  *  - Softmax runs in fp32 (row max and row sum in fp32 registers), the
  *    contractions run on bf16 MFMA with fp32 accumulation.  Inference only:
  *    there is no backward pass.
@@ -188,6 +189,43 @@ ATTN_API int attn_prefill_paged(const void *q, const void *k_cache, const void *
                        float v_scale, const int32_t *block_table, int max_blocks, int num_blocks,
                        int block_size, int actual_history_len, float softmax_scale, int num_kv_groups,
                        int Hq, int Hkv, int Lq, int D, void *out, float *lse, hipStream_t stream);
+
+/*
+ * Paged history plus causal current-token GQA prefill.
+ *
+ * Follows: Prefill Context-Parallel Attention POC for Trainium2, introduction
+ * (its first version leaves attention among the current tokens out) and
+ * "Layout".  Query token t of head h attends the history keys
+ * 0..actual_history_len-1 of the paged cache exactly as attn_prefill_paged,
+ * and then the current tokens' keys 0..t of KV head h / num_kv_groups: one
+ * softmax over the joined key list, which is the log-sum-exp merge of the
+ * history result and the current-token result.  Two kernels on the stream:
+ * the history one hands its fp32 result and lse to the current-token one,
+ * which continues the same online softmax (the merge is exact up to fp32
+ * rounding).
+ *
+ *   Arguments as attn_prefill_paged, plus k_cur/v_cur [Hkv,Lq,D] bf16
+ *   (contiguous, 16-byte aligned, non-null; no scale: the current tokens'
+ *   K/V in model units).  actual_history_len may be 0 (no history; the block
+ *   table is then not read).  lse (nullable) is the joined log-sum-exp.
+ *   workspace: device scratch of at least
+ *   attn_prefill_paged_causal_workspace_size(Hq, Hkv, Lq, D) bytes (about
+ *   Hq*Lq*(4D+4) bytes), 256-byte aligned, owned by the caller, contents on
+ *   entry ignored: the history kernel leaves its normalised output in fp32
+ *   and its lse there, and the current-token kernel continues the softmax
+ *   from that state (running max = lse, sum = 1).
+ *   Current V rows after a query's token contribute p = 0 exactly, which
+ *   keeps every finite value out; a non-finite current V value also reaches
+ *   the earlier rows of its 32-key tile (0 * inf), so current K/V must be
+ *   finite, as they are for real tokens.
+ */
+ATTN_API int attn_prefill_paged_causal(const void *q, const void *k_cache, const void *v_cache, float k_scale,
+                              float v_scale, const int32_t *block_table, int max_blocks, int num_blocks,
+                              int block_size, int actual_history_len, const void *k_cur, const void *v_cur,
+                              float softmax_scale, int num_kv_groups, int Hq, int Hkv, int Lq, int D,
+                              void *out, float *lse, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+ATTN_API size_t attn_prefill_paged_causal_workspace_size(int Hq, int Hkv, int Lq, int D);
 
 /*
  * (Residual +) LayerNorm over the last dimension.

@@ -33,7 +33,7 @@ def test_header_declares_the_four_entry_points():
     names = _declared_functions()
     for n in ("attn_encoder_fwd", "attn_decode_gqa", "attn_prefill_paged", "res_ln",
               "attn_decode_gqa_workspace_size", "attn_decode_gqa_window", "attn_decode_gqa_window_workspace_size",
-              "attn_status_string", "attn_version"):
+              "attn_prefill_paged_causal", "attn_prefill_paged_causal_workspace_size", "attn_status_string", "attn_version"):
         assert n in names
 
 
@@ -193,6 +193,32 @@ def test_prefill_validation(lib, kw, expect):
     assert lib.attn_prefill_paged(*_pre(**kw)) == expect
 
 
+def _prc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=1.0, vs=1.0, bt=FAKE, maxb=256, nb=256, bs=512, L=120000, kc=FAKE, vc=FAKE,
+             scale=0.0625, G=16, Hq=32, Hkv=2, Lq=4096, D=256, out=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return (a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["maxb"], a["nb"], a["bs"], a["L"], a["kc"],
+            a["vc"], a["scale"], a["G"], a["Hq"], a["Hkv"], a["Lq"], a["D"], a["out"], a["lse"], a["ws"], a["wsb"],
+            None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(kc=None), taa.ATTN_ERR_INVALID_ARG),
+    (dict(vc=None), taa.ATTN_ERR_INVALID_ARG),
+    (dict(kc=BAD), taa.ATTN_ERR_INVALID_ARG),
+    (dict(L=-1), taa.ATTN_ERR_INVALID_ARG),
+    (dict(L=256 * 512 + 1), taa.ATTN_ERR_INVALID_ARG),
+    (dict(D=128), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=31), taa.ATTN_ERR_INVALID_ARG),
+    (dict(vs=float("inf")), taa.ATTN_ERR_INVALID_ARG),
+    (dict(ws=None), taa.ATTN_ERR_WORKSPACE),
+    (dict(wsb=1000), taa.ATTN_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), taa.ATTN_ERR_INVALID_ARG),             # workspace must be 256-byte aligned
+])
+def test_prefill_causal_validation(lib, kw, expect):
+    assert lib.attn_prefill_paged_causal(*_prc(**kw)) == expect
+
+
 @pytest.mark.parametrize("args,expect", [
     ((None, None, 0, None, None, 1e-6, 4, 64, None, FAKE, 1, None, None, None), taa.ATTN_ERR_INVALID_ARG),
     ((FAKE, None, 0, None, None, 1e-6, 4, 60, None, FAKE, 1, None, None, None), taa.ATTN_ERR_INVALID_ARG),
@@ -210,3 +236,12 @@ def test_binding_raises_instead_of_falling_back():
     with pytest.raises(ValueError):
         taa.attn_decode_gqa(torch.zeros(1, 2, 1, 256), torch.zeros(1, 1, 8, 256), torch.zeros(1, 1, 8, 256), None,
                             1.0, 2)
+
+
+def test_prefill_causal_workspace_size():
+    # fp32 history output [Hq*Lq, D] (rounded up to 256 bytes), then its lse per row
+    n = taa.attn_prefill_paged_causal_workspace_size(32, 2, 4096, 256)
+    assert n == 32 * 4096 * 256 * 4 + 32 * 4096 * 4
+    assert taa.attn_prefill_paged_causal_workspace_size(6, 2, 100, 256) == 6 * 100 * 256 * 4 + 6 * 100 * 4
+    assert taa.attn_prefill_paged_causal_workspace_size(1, 1, 3, 256) == 3 * 256 * 4 + 3 * 4
+    assert taa.attn_prefill_paged_causal_workspace_size(6, 4, 100, 256) == 0  # Hq not a multiple of Hkv

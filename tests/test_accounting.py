@@ -54,3 +54,8 @@ def test_decode_window_bytes():
     # two sequences of 3 and 5 in-range keys, 2 KV / 4 query heads, D=8:
     # K+V 8*2*8*2*2, q+out 2*2*4*8*2, no mask
     assert acc.decode_window_bytes([3, 5], 2, 4, 8) == 512 + 256
+
+
+def test_causal_flops():
+    # 3 tokens see 1, 2, 3 keys: 6 (query, key) pairs, 4*D FLOPs each, 2 heads
+    assert acc.causal_flops(3, 2, 8) == 6 * 4 * 8 * 2

@@ -90,6 +90,79 @@ int decode_common(const void *q, const void *k, const void *v, const float *attn
 }
 
 }  // namespace
+extern "C" size_t attn_prefill_paged_causal_workspace_size(int Hq, int Hkv, int Lq, int D);
+namespace {
+
+// Bytes of the history -> current-token handoff's O part: the normalised
+// history output [Hq*Lq, D] in fp32, rounded up to 256 bytes (the lse
+// [Hq*Lq] follows).
+int64_t prefill_handoff_o_bytes(int Hq, int, int Lq, int D) {
+  return ((int64_t)Hq * Lq * D * 4 + 255) / 256 * 256;
+}
+
+// Shared validation and launch of the paged prefill; k_cur/v_cur non-null
+// adds the causal current-token part (then an empty history is allowed and
+// the workspace carries the history's state).
+int prefill_common(const void *q, const void *k_cache, const void *v_cache, float k_scale, float v_scale,
+                   const int32_t *block_table, int max_blocks, int num_blocks, int block_size, int actual_history_len,
+                   const void *k_cur, const void *v_cur, float softmax_scale, int num_kv_groups, int Hq, int Hkv,
+                   int Lq, int D, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  const bool cur = k_cur != nullptr;
+  if (!q || !k_cache || !v_cache || !block_table || !out) return ATTN_ERR_INVALID_ARG;
+  if (max_blocks <= 0 || num_blocks <= 0 || block_size <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || D <= 0 ||
+      num_kv_groups <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)Hkv * num_kv_groups != Hq) return ATTN_ERR_INVALID_ARG;
+  if (actual_history_len < (cur ? 0 : 1) || (int64_t)actual_history_len > (int64_t)max_blocks * block_size)
+    return ATTN_ERR_INVALID_ARG;
+  if (D != 256) return ATTN_ERR_UNSUPPORTED;
+  if (block_size % 64 != 0 || block_size % prefill_key_tile() != 0) return ATTN_ERR_UNSUPPORTED;
+  if (!finite(k_scale) || !finite(v_scale) || !(k_scale > 0.0f) || !(v_scale > 0.0f)) return ATTN_ERR_INVALID_ARG;
+  if (!finite(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
+  if (cur && (!aligned16(k_cur) || !aligned16(v_cur))) return ATTN_ERR_INVALID_ARG;
+  if (cur) {
+    if (!workspace || workspace_bytes < attn_prefill_paged_causal_workspace_size(Hq, Hkv, Lq, D))
+      return ATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_INVALID_ARG;
+  }
+  if (((int64_t)num_blocks * Hkv * block_size * D) > ((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)num_kv_groups * Lq > 0x7fffffffLL - 256) return ATTN_ERR_UNSUPPORTED;
+  // a 32-key tile of current K/V is addressed with 32-bit offsets from its own base
+  if (cur && (int64_t)Lq * D * 2 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+
+  PrefillLaunch L;
+  memset(&L, 0, sizeof L);
+  L.q = static_cast<const __bf16 *>(q);
+  L.kc = static_cast<const uint8_t *>(k_cache);
+  L.vc = static_cast<const uint8_t *>(v_cache);
+  L.bt = block_table;
+  L.bs = block_size;
+  L.L_act = actual_history_len;
+  L.Hkv = Hkv;
+  L.G = num_kv_groups;
+  L.Lq = Lq;
+  exp2_scale(softmax_scale * k_scale, &L.c, &L.q_neg);
+  L.v_scale = v_scale;
+  if (cur) {
+    int neg;
+    L.kcur = static_cast<const __bf16 *>(k_cur);
+    L.vcur = static_cast<const __bf16 *>(v_cur);
+    exp2_scale(softmax_scale, &L.c_cur, &neg);
+    // One q sign for both loops: the sign of softmax_scale (k_scale > 0; if
+    // softmax_scale * k_scale underflowed to zero the history part is
+    // sign-blind anyway).
+    L.q_neg = neg;
+    L.ws_o = static_cast<float *>(workspace);
+    L.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + prefill_handoff_o_bytes(Hq, Hkv, Lq, D));
+  }
+  L.out = static_cast<__bf16 *>(out);
+  L.lse = lse;
+  return hip_status(launch_prefill(L, stream));
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -226,37 +299,25 @@ int attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache, 
                        const int32_t *block_table, int max_blocks, int num_blocks, int block_size,
                        int actual_history_len, float softmax_scale, int num_kv_groups, int Hq, int Hkv, int Lq,
                        int D, void *out, float *lse, hipStream_t stream) {
-  if (!q || !k_cache || !v_cache || !block_table || !out) return ATTN_ERR_INVALID_ARG;
-  if (max_blocks <= 0 || num_blocks <= 0 || block_size <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || D <= 0 ||
-      num_kv_groups <= 0)
-    return ATTN_ERR_INVALID_ARG;
-  if ((int64_t)Hkv * num_kv_groups != Hq) return ATTN_ERR_INVALID_ARG;
-  if (actual_history_len < 1 || (int64_t)actual_history_len > (int64_t)max_blocks * block_size)
-    return ATTN_ERR_INVALID_ARG;
-  if (D != 256) return ATTN_ERR_UNSUPPORTED;
-  if (block_size % 64 != 0 || block_size % prefill_key_tile() != 0) return ATTN_ERR_UNSUPPORTED;
-  if (!finite(k_scale) || !finite(v_scale) || !(k_scale > 0.0f) || !(v_scale > 0.0f)) return ATTN_ERR_INVALID_ARG;
-  if (!finite(softmax_scale)) return ATTN_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
-  if (((int64_t)num_blocks * Hkv * block_size * D) > ((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
-  if ((int64_t)num_kv_groups * Lq > 0x7fffffffLL - 256) return ATTN_ERR_UNSUPPORTED;
+  return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
+                        actual_history_len, nullptr, nullptr, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out, lse,
+                        nullptr, 0, stream);
+}
 
-  PrefillLaunch L;
-  memset(&L, 0, sizeof L);
-  L.q = static_cast<const __bf16 *>(q);
-  L.kc = static_cast<const uint8_t *>(k_cache);
-  L.vc = static_cast<const uint8_t *>(v_cache);
-  L.bt = block_table;
-  L.bs = block_size;
-  L.L_act = actual_history_len;
-  L.Hkv = Hkv;
-  L.G = num_kv_groups;
-  L.Lq = Lq;
-  exp2_scale(softmax_scale * k_scale, &L.c, &L.q_neg);
-  L.v_scale = v_scale;
-  L.out = static_cast<__bf16 *>(out);
-  L.lse = lse;
-  return hip_status(launch_prefill(L, stream));
+size_t attn_prefill_paged_causal_workspace_size(int Hq, int Hkv, int Lq, int D) {
+  if (Hq <= 0 || Hkv <= 0 || Lq <= 0 || D <= 0 || Hq % Hkv) return 0;
+  return (size_t)prefill_handoff_o_bytes(Hq, Hkv, Lq, D) + (size_t)Hq * Lq * 4;
+}
+
+int attn_prefill_paged_causal(const void *q, const void *k_cache, const void *v_cache, float k_scale, float v_scale,
+                              const int32_t *block_table, int max_blocks, int num_blocks, int block_size,
+                              int actual_history_len, const void *k_cur, const void *v_cur, float softmax_scale,
+                              int num_kv_groups, int Hq, int Hkv, int Lq, int D, void *out, float *lse,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!k_cur || !v_cur) return ATTN_ERR_INVALID_ARG;
+  return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
+                        actual_history_len, k_cur, v_cur, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out, lse,
+                        workspace, workspace_bytes, stream);
 }
 
 int res_ln(const float *residual, const void *x, attn_dtype_t x_dtype, const float *gamma, const float *beta,

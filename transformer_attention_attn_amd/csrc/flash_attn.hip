@@ -1,11 +1,15 @@
 // Tiled online-softmax ("flash") attention forward for gfx950.
 //
-// One kernel template serves two callers:
+// One kernel template serves three callers:
 //   * the non-causal encoder (q/k/v [B,H,S,D] bf16 or fp32, optional additive
 //     key mask, fused residual-add epilogue);
 //   * the history-only GQA prefill over a paged FP8 (e4m3fn) KV cache, whose
 //     G query heads per KV head are packed into the M dimension (rows r of a KV
-//     head are (head g, token t) with r = g*Lq + t).
+//     head are (head g, token t) with r = g*Lq + t);
+//   * the same prefill followed, in the same workgroup, by causal attention
+//     over the current tokens' bf16 K/V: the online softmax state of the
+//     history loop carries into a second loop, which is the log-sum-exp merge
+//     of the two parts done in registers.
 //
 // Prefill Context-Parallel Attention POC for Trainium2, "Layout": Q heads that
 // share a KV head are packed together, online max/sum stay fp32 while the
@@ -332,23 +336,59 @@ __device__ __forceinline__ void qk_tile(f32x16_t (&s)[G::NT][G::KB], const u32x4
   }
 }
 
-// Remove keys >= n_keys from a tile whose keys start at key0 (no-mask kernels;
-// rare uniform branch: only the ragged last tile and padding tiles).
-template <class G>
-__device__ __forceinline__ void mask_tail(f32x16_t (&s)[G::NT][G::KB], int key0, int n_keys, int lane) {
-  if (key0 + G::BN > n_keys) {
-    const int h = lane >> 5;
+// Score masks of the kernels without an additive mask, applied to S of each
+// tile (keys key0 ..) right after its QK^T.  Lane l holds keys
+// key0 + kb*32 + (v/4)*8 + 4*(l/32) + v%4 of its row in s[nt][kb][v].
+//
+// TailMask removes keys >= n_keys (rare uniform branch: only the ragged last
+// tile and padding tiles).
+struct TailMask {
+  int n_keys;
+  template <class G>
+  __device__ __forceinline__ void apply(f32x16_t (&s)[G::NT][G::KB], int key0, int lane) const {
+    if (key0 + G::BN > n_keys) {
+      const int h = lane >> 5;
 #pragma unroll
-    for (int kb = 0; kb < G::KB; ++kb)
+      for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = key0 + kb * 32 + (v >> 2) * 8 + 4 * h + (v & 3);
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + kb * 32 + (v >> 2) * 8 + 4 * h + (v & 3);
 #pragma unroll
-        for (int nt = 0; nt < G::NT; ++nt)
-          if (key >= n_keys) s[nt][kb][v] = -INFINITY;
-      }
+          for (int nt = 0; nt < G::NT; ++nt)
+            if (key >= n_keys) s[nt][kb][v] = -INFINITY;
+        }
+    }
   }
-}
+};
+
+// CausalMask: the row of token t sees keys <= t.  The uniform branch is taken
+// only by tiles that reach past the smallest token of the wave (the diagonal
+// tiles, the ragged last tile and padding tiles; the source's n_keys is one
+// past the largest token of the workgroup, so keys >= n_keys are removed too).
+// The mask replaces scores, it does not add to them: a key after the token
+// leaves no trace whatever its K holds.
+template <int NT>
+struct CausalMask {
+  int t[NT];  // token of the lane's row in row block nt (huge for padding rows)
+  int t_min;  // wave-uniform minimum of t
+  template <class G>
+  __device__ __forceinline__ void apply(f32x16_t (&s)[G::NT][G::KB], int key0, int lane) const {
+    if (key0 + G::BN - 1 > t_min) {
+      const int h = lane >> 5;
+      int lim[G::NT];  // keys with offset > lim are after the token
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt) lim[nt] = t[nt] - key0 - 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int off = kb * 32 + (v >> 2) * 8 + (v & 3);
+#pragma unroll
+          for (int nt = 0; nt < G::NT; ++nt) s[nt][kb][v] = off > lim[nt] ? -INFINITY : s[nt][kb][v];
+        }
+    }
+  }
+};
 
 // Empty asm statements are ordered side effects: pin_in redefines a value at
 // a point (nothing that uses it can move above), pin_out consumes it (its
@@ -427,9 +467,10 @@ __device__ __forceinline__ u32x4_t p_frag(const PCarry<G> &pc, int nt, int kb, i
 // under its own VALU work; the second half of P is left to phase B, which
 // balances the VALU load of the two phases.
 //
-// Lazy rescale: the reference max m of a row only moves when the tile max
-// exceeds it by more than kTau, so p = 2^(s - m) <= 2^kTau and the O rescale
-// (a VALU pass over every accumulator) is rare.  Exact: the final O/l uses one
+// Lazy rescale: the reference max m of a row only moves when the row's tile
+// max exceeds it by more than kTau, so p = 2^(s - m) <= 2^kTau and the O
+// rescale (a VALU pass over every accumulator, skipped unless some row of the
+// wave moved) is rare.  Exact: the final O/l uses one
 // consistent reference per row.  The row sum is taken on the packed bf16 P
 // (v_dot2_f32_bf16), so it normalises exactly the values multiplied into V.
 template <class G, bool HAS_MASK>
@@ -500,17 +541,21 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
         pin_out(mx[nt]);
       }
     } else if (f == 1) {
-      bool grow = false;
+      bool grow = false, grow_row[G::NT];
 #pragma unroll
       for (int nt = 0; nt < G::NT; ++nt) {
         const float m2 = pair_max(mx[nt]);
         mx[nt] = HAS_MASK ? m2 : m2 * c;  // -inf * c = -inf (c > 0)
-        grow |= mx[nt] > ws.m[nt] + kTau;
+        grow_row[nt] = mx[nt] > ws.m[nt] + kTau;
+        grow |= grow_row[nt];
       }
       any = __ballot(grow) != 0;
 #pragma unroll
       for (int nt = 0; nt < G::NT; ++nt) {
-        const float m_new = any ? fmaxf(ws.m[nt], mx[nt]) : ws.m[nt];
+        // per row: a row's reference moves only on its own scores, so its
+        // result never depends on the other rows of the wave (alpha = 1
+        // leaves the rows that keep theirs bit-identical)
+        const float m_new = grow_row[nt] ? fmaxf(ws.m[nt], mx[nt]) : ws.m[nt];
         alpha[nt] = m_new == -INFINITY ? 1.0f : fast_exp2(ws.m[nt] - m_new);
         ws.m[nt] = m_new;
         pc.m_use[nt] = m_new == -INFINITY ? 0.0f : m_new;
@@ -592,21 +637,28 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
 // other V buffer, and issues the global loads of K(it+3) and V(it+2) into the
 // register stage.  Tiles past the last one read as zeros and are fully
 // masked (p = 0), including the padding step of an odd iteration count.
-// Returns with the LDS free (barrier passed).
-template <class G, bool HAS_MASK, class Src>
+// Without an additive mask, `mk` masks the scores of each tile (TailMask,
+// CausalMask).  `fresh` starts a new softmax state; otherwise the loop
+// continues the one in `ws` (same log2 units: c must give true scores times
+// log2(e)).  `tid` is threadIdx.x (a caller running two loops passes the
+// second one a pinned copy, so that no per-lane offset of the second loop is
+// computed early and kept live through the first).  Returns with the LDS
+// free (barrier passed).
+template <class G, bool HAS_MASK, class Src, class Mask>
 __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, const u32x4_t (&qf)[G::NT][G::SD],
-                                           char *smem, float c) {
-  const unsigned tid = threadIdx.x;
+                                           char *smem, float c, const Mask &mk, bool fresh, unsigned tid) {
   const int lane = tid & 63;
   const int sp = __builtin_amdgcn_readfirstlane((int)(tid >> 6)) / G::RG;
   const int n_tiles = (src.n_keys + G::BN - 1) / G::BN;
   const int n_iter = (n_tiles + G::NSPLIT - 1) / G::NSPLIT;
+  if (fresh) {
 #pragma unroll
-  for (int nt = 0; nt < G::NT; ++nt) {
-    ws.m[nt] = -INFINITY;
-    ws.l[nt] = 0.0f;
+    for (int nt = 0; nt < G::NT; ++nt) {
+      ws.m[nt] = -INFINITY;
+      ws.l[nt] = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] = f32x16_t{};
+      for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] = f32x16_t{};
+    }
   }
   if (n_iter <= 0) return;
 
@@ -629,7 +681,7 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
 
   f32x16_t s[G::NT][G::KB];
   qk_tile<G>(s, qf, kbuf + sp * G::KTILE, lane);
-  if constexpr (!HAS_MASK) mask_tail<G>(s, sp * G::BN, src.n_keys, lane);
+  if constexpr (!HAS_MASK) mk.template apply<G>(s, sp * G::BN, lane);
 
   // One tile step: S holds S(it) on entry, SN receives S(it+1).  The loop
   // below alternates the two register sets instead of copying S each step;
@@ -664,7 +716,7 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
     });
     __syncthreads();
 
-    if constexpr (!HAS_MASK) mask_tail<G>(SN, ((it + 1) * G::NSPLIT + sp) * G::BN, src.n_keys, lane);
+    if constexpr (!HAS_MASK) mk.template apply<G>(SN, ((it + 1) * G::NSPLIT + sp) * G::BN, lane);
   };
 
   f32x16_t s2[G::NT][G::KB];
@@ -787,7 +839,7 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   src.mask = HAS_MASK ? a.mask + b * a.mask_sb : nullptr;
 
   WaveState<G> ws;
-  flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c);
+  flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c, TailMask{a.Skv}, true, threadIdx.x);
 
   // The residual rows are read before the split merge, so their latency
   // overlaps it.
@@ -843,7 +895,42 @@ void encoder_fwd_kernel(EncoderLaunch a) {
 
 // ------------------------------------------------------------------ prefill kernel
 
-template <class G>
+// O * o_scale / l and the lse for the rows of one prefill row tile: to the
+// bf16 output and the caller's lse, or (HANDOFF) in fp32 to the handoff
+// buffers [Hkv*rows, D] and [Hkv*rows], from where the current-token kernel
+// continues the softmax.  Both forms share every instruction but the store,
+// which keeps the register allocation of the key loop ahead of them alike.
+template <class G, bool HANDOFF>
+__device__ __forceinline__ void prefill_epilogue(const WaveState<G> &ws, const PrefillLaunch &a, int rt, int kvh,
+                                                 int rg, int lane, float o_scale) {
+  const int rows = a.G * a.Lq;
+  const int64_t row_base = (int64_t)kvh * rows;
+  const int l32 = lane & 31, hh = lane >> 5;
+  float *const lse = HANDOFF ? a.ws_ml : a.lse;
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
+    const float lt = pair_sum(ws.l[nt]);
+    if (r >= rows) continue;
+    const float inv = lt > 0.0f ? o_scale / lt : 0.0f;
+    if (lse && hh == 0) lse[row_base + r] = lt > 0.0f ? (ws.m[nt] + __log2f(lt)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = mt * 32 + r4 * 8 + 4 * hh;
+        const float o0 = ws.o[nt][mt][4 * r4 + 0] * inv, o1 = ws.o[nt][mt][4 * r4 + 1] * inv;
+        const float o2 = ws.o[nt][mt][4 * r4 + 2] * inv, o3 = ws.o[nt][mt][4 * r4 + 3] * inv;
+        if constexpr (HANDOFF)
+          *reinterpret_cast<f32x4_t *>(a.ws_o + (row_base + r) * G::D + d0) = f32x4_t{o0, o1, o2, o3};
+        else
+          *reinterpret_cast<u32x2_t *>(a.out + (row_base + r) * G::D + d0) =
+              u32x2_t{pack_bf16(o0, o1), pack_bf16(o2, o3)};
+      }
+  }
+}
+
+template <class G, bool HANDOFF>
 __global__ __launch_bounds__(G::THREADS) __attribute__((amdgpu_waves_per_eu(G::WPE, G::WPE)))
 void prefill_paged_kernel(PrefillLaunch a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];  // G::LDS bytes
@@ -877,25 +964,97 @@ void prefill_paged_kernel(PrefillLaunch a) {
   src.n_keys = a.L_act;
 
   WaveState<G> ws;
-  flash_loop<G, false>(ws, src, qf, smem, a.c);
+  flash_loop<G, false>(ws, src, qf, smem, a.c, TailMask{a.L_act}, true, threadIdx.x);
 
+  prefill_epilogue<G, HANDOFF>(ws, a, rt, kvh, rg, lane, a.v_scale);
+}
+
+// Causal attention among the current tokens (bf16 K/V [Hkv, Lq, D]): the row
+// of token t sees current keys 0..t.  With a history the online softmax
+// continues the history kernel's handed-off state (the log-sum-exp merge of
+// the two parts, exact: the state passes in fp32); without one it starts
+// fresh.  A row tile's last token bounds the keys it reads, so the tiles of
+// the latest token blocks carry the most work and are dispatched first.
+template <class G>
+__global__ __launch_bounds__(G::THREADS) __attribute__((amdgpu_waves_per_eu(G::WPE, G::WPE)))
+void prefill_current_kernel(PrefillLaunch a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // G::LDS bytes
+  const int rows = a.G * a.Lq;
+  const int n_rt = (rows + G::BM - 1) / G::BM;
+  const int total = n_rt * a.Hkv, i = blockIdx.x;
+  int rt, kvh;
+  if (a.Lq % G::BM == 0) {  // whole row tiles per head: latest token block first
+    const int nb = a.Lq / G::BM, per = a.G * a.Hkv;
+    const int tb = nb - 1 - i / per, g = (i % per) / a.Hkv;
+    kvh = i % a.Hkv;
+    rt = g * nb + tb;
+  } else {
+    kvh = (total - 1 - i) / n_rt;
+    rt = (total - 1 - i) % n_rt;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave % G::RG;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int64_t row_base = (int64_t)kvh * rows;
+  const uint32_t qsign = a.q_neg ? 0x80008000u : 0u;
+
+  u32x4_t qf[G::NT][G::SD];
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
     const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
-    const float lt = pair_sum(ws.l[nt]);
-    if (r >= rows) continue;
-    const float inv = lt > 0.0f ? a.v_scale / lt : 0.0f;
-    if (a.lse && hh == 0) a.lse[row_base + r] = lt > 0.0f ? (ws.m[nt] + __log2f(lt)) * kLn2 : -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = mt * 32 + r4 * 8 + 4 * hh;
-        *reinterpret_cast<u32x2_t *>(a.out + (row_base + r) * G::D + d0) =
-            u32x2_t{pack_bf16(ws.o[nt][mt][4 * r4 + 0] * inv, ws.o[nt][mt][4 * r4 + 1] * inv),
-                    pack_bf16(ws.o[nt][mt][4 * r4 + 2] * inv, ws.o[nt][mt][4 * r4 + 3] * inv)};
-      }
+    for (int sd = 0; sd < G::SD; ++sd)
+      qf[nt][sd] = neg_bf16x8(
+          r < rows ? ldg<u32x4_t>(a.q + (row_base + r) * G::D + 16 * sd + 8 * hh) : u32x4_t{0, 0, 0, 0}, qsign);
   }
+
+  // With a history: its normalised output O_h (fp32) and lse_h, i.e. the
+  // state m = lse_h (log2 units), l = 1, O = O_h, which the loop continues.
+  WaveState<G> ws;
+  const bool fresh = a.L_act == 0;
+  if (!fresh) {
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) {
+      const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
+      const bool ok = r < rows;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t x = ok ? ldg<f32x4_t>(a.ws_o + (row_base + r) * G::D + mt * 32 + r4 * 8 + 4 * hh)
+                               : f32x4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ws.o[nt][mt][4 * r4 + c] = x[c];
+        }
+      ws.m[nt] = ok ? a.ws_ml[row_base + r] * kLog2e : -INFINITY;
+      ws.l[nt] = ok && hh == 0 ? 1.0f : 0.0f;  // the pair sum of the two halves gives l = 1
+    }
+  }
+
+  CausalMask<G::NT> cm;
+  int tmin = 0x3fffffff;
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
+    cm.t[nt] = r < rows ? r % a.Lq : 0x3fffffff;  // padding rows: see everything, never written
+    tmin = min(tmin, cm.t[nt]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tmin = min(tmin, __shfl_xor(tmin, o, 64));
+  cm.t_min = __builtin_amdgcn_readfirstlane(tmin);
+  // keys this tile needs: one past its largest token (all of them when its
+  // rows span two heads)
+  const int first = rt * G::BM, last = min(first + G::BM, rows) - 1;
+  EncSrc<G, false, false> cs;
+  cs.kb = reinterpret_cast<const char *>(a.kcur + (int64_t)kvh * a.Lq * G::D);
+  cs.vb = reinterpret_cast<const char *>(a.vcur + (int64_t)kvh * a.Lq * G::D);
+  cs.krow = cs.vrow = G::D * 2;
+  cs.kstep = cs.vstep = (int64_t)G::NSPLIT * G::BN * G::D * 2;
+  cs.n_keys = first / a.Lq == last / a.Lq ? last % a.Lq + 1 : a.Lq;
+  cs.mask = nullptr;
+  flash_loop<G, false>(ws, cs, qf, smem, a.c_cur, cm, fresh, threadIdx.x);
+
+  prefill_epilogue<G, false>(ws, a, rt, kvh, rg, lane, 1.0f);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -935,9 +1094,15 @@ int encoder_rows_per_block() { return EncGeo::BM; }
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream) {
   const int rows = a.G * a.Lq;
   const int n_rt = (rows + PrefGeo::BM - 1) / PrefGeo::BM;
-  return launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo>, dim3(n_rt * a.Hkv), a, stream);
+  if (!a.kcur) return launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo, false>, dim3(n_rt * a.Hkv), a, stream);
+  if (a.L_act > 0) {
+    const hipError_t e = launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo, true>, dim3(n_rt * a.Hkv), a, stream);
+    if (e != hipSuccess) return e;
+  }
+  return launch_lds<PrefGeo>(prefill_current_kernel<PrefGeo>, dim3(n_rt * a.Hkv), a, stream);
 }
 
 int prefill_key_tile() { return PrefGeo::BN; }
+int prefill_rows_per_block() { return PrefGeo::BM; }
 
 }  // namespace mi355

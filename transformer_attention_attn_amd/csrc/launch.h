@@ -31,6 +31,9 @@ struct PrefillLaunch {
   float c;        // |softmax_scale| * k_scale * log2(e), > 0
   int q_neg;      // 1: the scale was negative, q is negated on load
   float v_scale;
+  const __bf16 *kcur, *vcur;  // nullable: current tokens' K/V [Hkv, Lq, D] (causal part)
+  float c_cur;                // |softmax_scale| * log2(e), > 0
+  float *ws_o, *ws_ml;        // history -> current-token handoff (causal part with a history)
   __bf16 *out;
   float *lse;     // nullable
 };
@@ -64,6 +67,7 @@ hipError_t launch_encoder(const EncoderLaunch &a, bool f32_in, hipStream_t strea
 int encoder_rows_per_block();
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream);
 int prefill_key_tile();
+int prefill_rows_per_block();
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
 int decode_chunk_keys();
 int decode_max_groups();

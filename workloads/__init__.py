@@ -222,6 +222,15 @@ def prefill_paged(seed: int = 1005, Hq: int = 32, Hkv: int = 2, Lq: int = 4096, 
                        num_blocks, block_size, L_act, scale, q, k8, v8, ks, vs, bt, rows)
 
 
+def prefill_current_kv(seed: int, Hkv: int, Lq: int, D: int = 256):
+    """The current tokens' K/V [Hkv, Lq, D] for causal prefill: bf16 entries
+    N(0, 1), the magnitude of the dequantised history K/V."""
+    g = _gen(seed)
+    k = to_bf16(torch.randn(Hkv, Lq, D, generator=g))
+    v = to_bf16(torch.randn(Hkv, Lq, D, generator=g))
+    return k, v
+
+
 CONFIGS = {
     1: encoder_tiny,
     2: encoder_vjepa2,

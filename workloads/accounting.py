@@ -35,6 +35,11 @@ def decode_bytes(lens, Hkv: int, Hq: int, S_ctx: int, D: int, elem: int = 2, mas
     return kv + B * S_ctx * mask_elem + 2 * B * Hq * D * elem
 
 
+def causal_flops(Lq: int, Hq: int, D: int) -> int:
+    """QK^T + PV FLOPs of causal attention among Lq tokens: token t sees t+1 keys."""
+    return 4 * Hq * D * (Lq * (Lq + 1) // 2)
+
+
 def decode_window_bytes(n_keys, Hkv: int, Hq: int, D: int, elem: int = 2) -> int:
     """K+V rows inside each sequence's key range (no mask read), q and out."""
     B = len(n_keys)
