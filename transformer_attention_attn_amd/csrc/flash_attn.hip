@@ -71,7 +71,7 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int OCC_, bool VFIRST_ = false>
+template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int OCC_, bool VFIRST_ = false, int QL_ = 0>
 struct Geo {
   static constexpr int D = D_, BN = BN_, NT = NT_, RG = RG_, NSPLIT = NSPLIT_;
   static constexpr int GRP = GRP_;  // LDS fragments read ahead of the MFMAs that use them
@@ -97,10 +97,18 @@ struct Geo {
   static constexpr int MT = D / 32;   // d tiles of O^T
   static constexpr int NFQ = SD * KB, NFV = 2 * KB * MT;  // LDS fragments per tile: QK, PV
   static constexpr int MERGE = (NSPLIT - 1) * RG * NT * (MT * 16 + 2) * 64 * 4;  // split partials (merge_splits)
-  static constexpr int LDS = 2 * (KSLOT + VSLOT) > MERGE ? 2 * (KSLOT + VSLOT) : MERGE;  // K/V double buffers
+  // The first QL Q fragments of every lane live in LDS, not in registers: one
+  // 16-byte slot per (fragment, row block, thread) after the K/V buffers.
+  // Read with ds_read they wait on the LDS counter only; a register spilled
+  // instead would be reloaded from scratch, and that wait (the vector memory
+  // counter, in order) also drains the K/V tile loads in flight.
+  static constexpr int QL = QL_;
+  static constexpr int QOFF = 2 * (KSLOT + VSLOT) > MERGE ? 2 * (KSLOT + VSLOT) : MERGE;
+  static constexpr int LDS = QOFF + QL * NT * THREADS * 16;  // K/V double buffers (or merge space), Q slots
   // softmax VALU instructions issued between consecutive QK MFMA groups
   static constexpr int VPM = (NT * (7 * BN / 4 + 8) + NFQ - 1) / NFQ;
   static_assert(D % 64 == 0 && BN % 32 == 0 && (VSH == 0 || D == 64), "tile shape");
+  static_assert(QL >= 0 && QL <= SD, "Q fragments in LDS");
   static_assert(LDS <= 160 * 1024, "LDS budget (gfx950: 160 KiB per workgroup)");
 
   static __device__ __forceinline__ int k_row(int key) { return key * KROW; }
@@ -317,9 +325,25 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // S^T of one tile: s[nt][kb] = K-block kb . Q^T.  K fragment (kb, sd) is the
 // 16 bytes at d = 16*sd + 8*(lane/32) of row kb*32 + lane%32.
+// Q fragment (nt, sd): from LDS for sd < QL (qa: this thread's first slot),
+// else from the registers.
+template <class G>
+__device__ __forceinline__ u32x4_t q_lds(const char *qa, int nt, int sd) {
+  return *reinterpret_cast<const u32x4_t *>(qa + (sd * G::NT + nt) * G::THREADS * 16);
+}
+// Store the LDS-resident Q fragments of this thread (before the key loop).
+template <class G>
+__device__ __forceinline__ void q_to_lds(const u32x4_t (&qf)[G::NT][G::SD], char *smem, unsigned tid) {
+#pragma unroll
+  for (int sd = 0; sd < G::QL; ++sd)
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt)
+      *reinterpret_cast<u32x4_t *>(smem + G::QOFF + ((sd * G::NT + nt) * G::THREADS + tid) * 16) = qf[nt][sd];
+}
+
 template <class G>
 __device__ __forceinline__ void qk_tile(f32x16_t (&s)[G::NT][G::KB], const u32x4_t (&qf)[G::NT][G::SD],
-                                        const char *kt, int lane) {
+                                        const char *qa, const char *kt, int lane) {
   const char *base = kt + (lane & 31) * G::KROW + 16 * (lane >> 5);
   u32x4_t fb[G::NFQ];
 #pragma unroll
@@ -332,7 +356,8 @@ __device__ __forceinline__ void qk_tile(f32x16_t (&s)[G::NT][G::KB], const u32x4
     const int kb = f % G::KB, sd = f / G::KB;
 #pragma unroll
     for (int nt = 0; nt < G::NT; ++nt)
-      s[nt][kb] = mfma32(as_bf16x8(fb[f]), as_bf16x8(qf[nt][sd]), sd == 0 ? f32x16_t{} : s[nt][kb]);
+      s[nt][kb] = mfma32(as_bf16x8(fb[f]), as_bf16x8(sd < G::QL ? q_lds<G>(qa, nt, sd) : qf[nt][sd]),
+                         sd == 0 ? f32x16_t{} : s[nt][kb]);
   }
 }
 
@@ -476,8 +501,8 @@ __device__ __forceinline__ u32x4_t p_frag(const PCarry<G> &pc, int nt, int kb, i
 template <class G, bool HAS_MASK>
 __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_t (&sn)[G::NT][G::KB],
                                         f32x16_t (&s)[G::NT][G::KB], float (&alpha)[G::NT],
-                                        const u32x4_t (&qf)[G::NT][G::SD], const char *kt, const float *mk, float c,
-                                        int lane) {
+                                        const u32x4_t (&qf)[G::NT][G::SD], const char *qa, const char *kt,
+                                        const float *mk, float c, int lane) {
   constexpr int RA = G::GRP < G::NFQ ? G::GRP : G::NFQ;
   constexpr int NP = G::NT * G::KB * 4;  // P pairs of the first half
   constexpr int SLOTS = G::NFQ - 2;
@@ -487,11 +512,16 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
   const char *kbase = kt + (lane & 31) * G::KROW + 16 * h;
 
   u32x4_t fb[G::NFQ];
+  u32x4_t ql[G::QL > 0 ? G::QL : 1][G::NT];
   f32x4_t m4[G::KB][4];
   float mx[G::NT];
   bool any = false;
 
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int sd = 0; sd < G::QL; ++sd)
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) ql[sd][nt] = q_lds<G>(qa, nt, sd);
 #pragma unroll
   for (int f = 0; f < RA; ++f)
     fb[f] = *reinterpret_cast<const u32x4_t *>(kbase + (f % G::KB) * 32 * G::KROW + 32 * (f / G::KB));
@@ -507,8 +537,11 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
     const int kb = f % G::KB, sd = f / G::KB;
     pin_in(fb[f]);
 #pragma unroll
-    for (int nt = 0; nt < G::NT; ++nt)
-      sn[nt][kb] = mfma32(as_bf16x8(fb[f]), as_bf16x8(qf[nt][sd]), sd == 0 ? f32x16_t{} : sn[nt][kb]);
+    for (int nt = 0; nt < G::NT; ++nt) {
+      if (sd < G::QL) pin_in(ql[sd < G::QL ? sd : 0][nt]);
+      sn[nt][kb] = mfma32(as_bf16x8(fb[f]), as_bf16x8(sd < G::QL ? ql[sd < G::QL ? sd : 0][nt] : qf[nt][sd]),
+                          sd == 0 ? f32x16_t{} : sn[nt][kb]);
+    }
     if (f + RA < G::NFQ) {
       const int g = f + RA;
       fb[g] = *reinterpret_cast<const u32x4_t *>(kbase + (g % G::KB) * 32 * G::KROW + 32 * (g / G::KB));
@@ -663,6 +696,7 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
   if (n_iter <= 0) return;
 
   char *const kbuf = smem, *const vbuf = smem + 2 * G::KSLOT;
+  const char *const qa = smem + G::QOFF + tid * 16;  // this thread's LDS Q slots (G::QL > 0)
   // Prologue: K(0), V(0) and K(1) in one round trip (a second register stage
   // that is only live here), then K(2), V(1) in flight.
   typename Src::Stage st, st1;
@@ -680,7 +714,7 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
   __syncthreads();
 
   f32x16_t s[G::NT][G::KB];
-  qk_tile<G>(s, qf, kbuf + sp * G::KTILE, lane);
+  qk_tile<G>(s, qf, qa, kbuf + sp * G::KTILE, lane);
   if constexpr (!HAS_MASK) mk.template apply<G>(s, sp * G::BN, lane);
 
   // One tile step: S holds S(it) on entry, SN receives S(it+1).  The loop
@@ -694,7 +728,7 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
     PCarry<G> pc;
     float alpha[G::NT];
     const bool any =
-        phase_a<G, HAS_MASK>(ws, pc, SN, S, alpha, qf, knext + sp * G::KTILE,
+        phase_a<G, HAS_MASK>(ws, pc, SN, S, alpha, qf, qa, knext + sp * G::KTILE,
                              reinterpret_cast<const float *>(vcur + G::NSPLIT * G::VTILE) + sp * G::BN, c, lane);
     if (any) {
 #pragma unroll
@@ -838,6 +872,7 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   src.n_keys = a.Skv;
   src.mask = HAS_MASK ? a.mask + b * a.mask_sb : nullptr;
 
+  q_to_lds<G>(qf, smem, threadIdx.x);
   WaveState<G> ws;
   flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c, TailMask{a.Skv}, true, threadIdx.x);
 
@@ -963,6 +998,7 @@ void prefill_paged_kernel(PrefillLaunch a) {
   src.bs = a.bs;
   src.n_keys = a.L_act;
 
+  q_to_lds<G>(qf, smem, threadIdx.x);
   WaveState<G> ws;
   flash_loop<G, false>(ws, src, qf, smem, a.c, TailMask{a.L_act}, true, threadIdx.x);
 
@@ -1008,6 +1044,7 @@ void prefill_current_kernel(PrefillLaunch a) {
           r < rows ? ldg<u32x4_t>(a.q + (row_base + r) * G::D + 16 * sd + 8 * hh) : u32x4_t{0, 0, 0, 0}, qsign);
   }
 
+  q_to_lds<G>(qf, smem, threadIdx.x);
   // With a history: its normalised output O_h (fp32) and lse_h, i.e. the
   // state m = lse_h (log2 units), l = 1, O = O_h, which the loop continues.
   WaveState<G> ws;
@@ -1062,7 +1099,7 @@ void prefill_current_kernel(PrefillLaunch a) {
 using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true>;      // BM 128, 8 waves: 4 row groups x 2 key splits, 32-key tiles, 4 waves/SIMD
 using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: mask values held in registers, 2 waves/SIMD
 using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: twice the staging registers per tile
-using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2>;    // BM 256, 8 waves of 32 rows, 2 waves per SIMD
+using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 3>;  // BM 256, 8 waves of 32 rows, 2 waves per SIMD, 3 Q fragments in LDS
 
 // Launch with G::LDS bytes of dynamic LDS; kernels above 64 KiB are opted in
 // once per process (hipFuncSetAttribute is per function, not per device).
