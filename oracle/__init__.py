@@ -155,6 +155,44 @@ def decode_window(q, k, v, scale: float, mask=None, key_begin=None, key_end=None
     return sdpa(q, k, v, scale, torch.from_numpy(add))
 
 
+def rope(x, cos, sin, pairing: str):
+    """Rotary position embedding of x [..., S, D] with per-token tables
+    cos/sin [S, D/2] (pair k of token s turns by the angle whose cosine and
+    sine are cos[s, k], sin[s, k]).  Returns fp64.
+
+    vit-encoder-neuron-kernels, "Kernels": the two pairings of lanes,
+    "half" (lane k with lane k + D/2, rotate-half) and "interleaved" (lane 2k
+    with lane 2k + 1).  For a pair (a, b) the rotation is
+    a' = a cos - b sin,  b' = b cos + a sin.
+    """
+    x = _f64(x).copy()
+    c = _f64(cos)
+    s_ = _f64(sin)
+    D = x.shape[-1]
+    if pairing == "half":
+        a, b = x[..., : D // 2].copy(), x[..., D // 2:].copy()
+        x[..., : D // 2] = a * c - b * s_
+        x[..., D // 2:] = b * c + a * s_
+    elif pairing == "interleaved":
+        a, b = x[..., 0::2].copy(), x[..., 1::2].copy()
+        x[..., 0::2] = a * c - b * s_
+        x[..., 1::2] = b * c + a * s_
+    else:
+        raise ValueError(f"rope: unknown pairing {pairing!r}")
+    return x
+
+
+def encoder_block_rope(q, k, v, scale, residual, gamma, beta, eps, mask, cos, sin, pairing: str):
+    """The encoder block with RoPE applied to q and k first (token i of the
+    queries and token j of the keys use table rows i and j)."""
+    import torch
+
+    Sq, Skv = q.shape[2], k.shape[2]
+    qr = torch.from_numpy(rope(q, _f64(cos)[:Sq], _f64(sin)[:Sq], pairing))
+    kr = torch.from_numpy(rope(k, _f64(cos)[:Skv], _f64(sin)[:Skv], pairing))
+    return encoder_block(qr, kr, torch.from_numpy(_f64(v)), scale, residual, gamma, beta, eps, mask)
+
+
 def layernorm(x, gamma=None, beta=None, eps: float = 1e-6):
     """LayerNorm over the last dim; returns (y, mean, rstd) in fp64."""
     xs = _f64(x)

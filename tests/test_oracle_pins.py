@@ -425,3 +425,80 @@ def test_prefill_causal_ignores_future_tokens_bitwise():
     k2[:, 6:] = 3e4
     v2[:, 6:] = -3e4
     assert np.array_equal(oracle.prefill_causal(q, kc, vc, 0.5, 0.125, bt, 29, k2, v2, 0.2, rows), o1)
+
+
+# ----------------------------------------------------------------------------- rotary embedding
+
+
+def _angles(S, P, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.rand(S, P, generator=g, dtype=torch.float64) * 6.0 - 3.0
+
+
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+def test_rope_identity_tables_leave_x(pairing):
+    g = torch.Generator().manual_seed(22)
+    x = _rand(g, 2, 3, 5, 8)
+    out = oracle.rope(x, np.ones((5, 4)), np.zeros((5, 4)), pairing)
+    assert np.array_equal(out, x.numpy())
+
+
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+def test_rope_is_complex_multiplication(pairing):
+    """Pair k as the complex number a + ib turns by e^{i theta}: (a + ib) e^{i theta}."""
+    g = torch.Generator().manual_seed(23)
+    S, D = 7, 16
+    x = _rand(g, 2, S, D).numpy()
+    th = _angles(S, D // 2, 24).numpy()
+    out = oracle.rope(x, np.cos(th), np.sin(th), pairing)
+    if pairing == "half":
+        z = x[..., : D // 2] + 1j * x[..., D // 2:]
+        r = z * np.exp(1j * th)
+        want = np.concatenate([r.real, r.imag], axis=-1)
+    else:
+        z = x[..., 0::2] + 1j * x[..., 1::2]
+        r = z * np.exp(1j * th)
+        want = np.stack([r.real, r.imag], axis=-1).reshape(x.shape)
+    assert _relmax(out, want) < 1e-14
+
+
+def test_rope_pairings_differ_by_a_lane_permutation():
+    """Interleaved RoPE equals rotate-half RoPE conjugated by the lane
+    permutation (k, k + D/2) <-> (2k, 2k + 1)."""
+    g = torch.Generator().manual_seed(25)
+    S, D = 6, 12
+    x = _rand(g, 3, S, D).numpy()
+    th = _angles(S, D // 2, 26).numpy()
+    perm = np.empty(D, dtype=np.int64)  # interleaved lane -> half lane
+    perm[0::2] = np.arange(D // 2)
+    perm[1::2] = np.arange(D // 2) + D // 2
+    xi = x[..., perm]  # half layout -> interleaved layout
+    out_i = oracle.rope(xi, np.cos(th), np.sin(th), "interleaved")
+    out_h = oracle.rope(x, np.cos(th), np.sin(th), "half")
+    assert np.array_equal(out_i, out_h[..., perm])
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    """With angles pos * omega_k (1D RoPE), q_m . k_n depends on m - n only."""
+    g = torch.Generator().manual_seed(27)
+    D, S = 16, 40
+    omega = 10000.0 ** (-np.arange(D // 2) / (D // 2))
+    th = np.arange(S)[:, None] * omega[None, :]
+    q, k = _rand(g, D).numpy(), _rand(g, D).numpy()
+    for pairing in ("half", "interleaved"):
+        qr = oracle.rope(np.broadcast_to(q, (S, D)), np.cos(th), np.sin(th), pairing)
+        kr = oracle.rope(np.broadcast_to(k, (S, D)), np.cos(th), np.sin(th), pairing)
+        s1 = qr[12] @ kr[5]
+        s2 = qr[30] @ kr[23]
+        assert abs(s1 - s2) < 1e-12 * max(1.0, abs(s1))
+        assert abs(qr[12] @ kr[12] - q @ k) < 1e-12 * max(1.0, abs(q @ k))  # same position: no rotation left
+
+
+def test_rope_rotation_keeps_pair_norms():
+    g = torch.Generator().manual_seed(28)
+    x = _rand(g, 4, 9, 10).numpy()
+    th = _angles(9, 5, 29).numpy()
+    out = oracle.rope(x, np.cos(th), np.sin(th), "half")
+    n0 = x[..., :5] ** 2 + x[..., 5:] ** 2
+    n1 = out[..., :5] ** 2 + out[..., 5:] ** 2
+    assert _relmax(n1, n0) < 1e-14
