@@ -192,6 +192,26 @@ def time_next_workloads(taa, dev, flush, pre_dev, reps: int = 20):
         "frac_hbm_peak": b / (ms * 1e-3) / 1e9 / acc.PEAK_HBM_GBPS}
     del q, k, v
 
+    # the encoder attention with RoPE (K rotated by its pass, q rows as the
+    # attention kernel loads them; the step's V-JEPA2 inputs and the DINOv3
+    # shape; attention alone, back to back, both kernels timed)
+    from transformer_attention_attn_amd.rope import grid_positions, rope_tables
+    for name, case, grid, prefix, pairing in (("vjepa2_s2048_rope3d_interleaved", W.encoder_vjepa2(), (8, 16, 16), 0,
+                                               "interleaved"),
+                                              ("dinov3_s789_rope2d_half", W.encoder_dinov3(), (28, 28), 5, "half")):
+        pos, rot = grid_positions(*grid, prefix_tokens=prefix)
+        c, s_ = (torch.from_numpy(t).to(dev) for t in rope_tables(pos, case.D, rotate=rot))
+        q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+        o = torch.empty_like(q)
+        rws = torch.empty(taa.attn_encoder_rope_workspace_size(case.B, case.H, case.S, case.D), dtype=torch.uint8,
+                          device=dev)
+        ms_r = timed(lambda: taa.attn_encoder_fwd(q, k, v, case.scale, None, out=o, want_ln=False, rope=pairing,
+                                                  rope_cos=c, rope_sin=s_, rope_workspace=rws))
+        ms_0 = timed(lambda: taa.attn_encoder_fwd(q, k, v, case.scale, None, out=o, want_ln=False))
+        f = acc.encoder_flops(case.B, case.H, case.S, case.S, case.D)
+        out[f"{name}_attention"] = {"ms": ms_r, "ms_without_rope": ms_0, "tflops": f / (ms_r * 1e-3) / 1e12,
+                                    "frac_bf16_peak": f / (ms_r * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS}
+
     pre, p_q, p_k, p_v, p_bt = pre_dev
     kc, vc = (t.to(dev) for t in W.prefill_current_kv(1105, pre.Hkv, pre.Lq, pre.D))
     o = torch.empty_like(p_q)

@@ -50,6 +50,13 @@ typedef enum {
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_FP8_E4M3FN = 2 } attn_dtype_t;
 
+/* Rotary position embedding pairing of the encoder's fused RoPE prologue. */
+typedef enum {
+  ATTN_ROPE_NONE = 0,
+  ATTN_ROPE_HALF = 1,        /* lane k pairs with lane k + D/2 (rotate-half) */
+  ATTN_ROPE_INTERLEAVED = 2  /* lane 2k pairs with lane 2k + 1 */
+} attn_rope_t;
+
 /* Static, human-readable text for a status code (never NULL). */
 ATTN_API const char *attn_status_string(int status);
 
@@ -88,6 +95,24 @@ ATTN_API int attn_version(void);
  *   ln_mean/ln_rstd  fp32 [B*S_q] statistics of that LayerNorm (nullable).
  * gamma/beta are fp32 [H*D] and nullable (affine-free LayerNorm).
  * mask is nullable fp32 [B,1,1,S_kv] with batch stride mask_stride_b.
+ *
+ * Fused RoPE prologue (rope != ATTN_ROPE_NONE; vit-encoder-neuron-kernels,
+ * "Kernels": the rotate-half and interleaved pairings; V-JEPA2 ViT-L Encoder
+ * NKI Kernels, "Repository layout": host-side RoPE tables).  q and k are
+ * rotated before the contraction, in fp32, then rounded to bf16: for each
+ * pair (a, b) of lanes of token s (q row s, key s), with k the pair index,
+ *     a' = a cos[s,k] - b sin[s,k],   b' = b cos[s,k] + a sin[s,k].
+ * rope_cos/rope_sin are fp32 [rows, D/2] contiguous (rows >= max(S_q, S_kv)),
+ * 16-byte aligned, the tables of batch entry b at + b * rope_stride_b floats
+ * (0: one table for the whole batch; otherwise a multiple of 4).  Any
+ * positional layout (1D, 2D or 3D grids, extra unrotated tokens with
+ * cos = 1, sin = 0, scaled frequencies) is a matter of the tables.
+ * q rows are rotated as the attention kernel loads them; K is rotated once,
+ * by a pass on the same stream before it, into rope_workspace (at least
+ * attn_encoder_rope_workspace_size() bytes, 256-byte aligned, owned by the
+ * caller, contents on entry ignored): every query tile streams all keys, so
+ * rotating K inside the key loop would repeat the rotation per query tile.
+ * Without rope the workspace fields are ignored.
  */
 typedef struct {
   const void *q, *k, *v;
@@ -108,9 +133,17 @@ typedef struct {
   void *ln_out;
   attn_dtype_t ln_dtype;
   float *ln_mean, *ln_rstd;
+  const float *rope_cos, *rope_sin;
+  int64_t rope_stride_b;
+  attn_rope_t rope;
+  void *rope_workspace;
+  size_t rope_workspace_bytes;
 } attn_encoder_args_t;
 
 ATTN_API int attn_encoder_fwd(const attn_encoder_args_t *args, hipStream_t stream);
+/* Bytes of the rotated-K workspace: B * H * S_kv * D elements of in_dtype
+ * (0 for invalid arguments). */
+ATTN_API size_t attn_encoder_rope_workspace_size(int B, int H, int S_kv, int D, attn_dtype_t in_dtype);
 
 /*
  * GQA single-token decode (split-K "flash-decode" plus a combine pass).

@@ -33,7 +33,8 @@ def test_header_declares_the_four_entry_points():
     names = _declared_functions()
     for n in ("attn_encoder_fwd", "attn_decode_gqa", "attn_prefill_paged", "res_ln",
               "attn_decode_gqa_workspace_size", "attn_decode_gqa_window", "attn_decode_gqa_window_workspace_size",
-              "attn_prefill_paged_causal", "attn_prefill_paged_causal_workspace_size", "attn_status_string", "attn_version"):
+              "attn_prefill_paged_causal", "attn_prefill_paged_causal_workspace_size",
+              "attn_encoder_rope_workspace_size", "attn_status_string", "attn_version"):
         assert n in names
 
 
@@ -53,7 +54,7 @@ def test_status_strings(lib):
     for s in range(5):
         assert taa.attn_status_string(s).startswith(("ATTN_OK", "ATTN_ERR"))
     assert taa.attn_status_string(99) == "unknown attn status"
-    assert taa.attn_version() == 10000
+    assert taa.attn_version() == 10100
 
 
 def _enc(**kw):
@@ -87,6 +88,17 @@ def _enc(**kw):
     (dict(out=None), taa.ATTN_ERR_INVALID_ARG),
     (dict(residual=FAKE), taa.ATTN_ERR_INVALID_ARG),           # residual without residual_out
     (dict(ln_out=FAKE), taa.ATTN_ERR_INVALID_ARG),             # LayerNorm needs the residual stream
+    (dict(rope=3), taa.ATTN_ERR_UNSUPPORTED),                  # no such pairing
+    (dict(rope=1), taa.ATTN_ERR_INVALID_ARG),                  # pairing without tables
+    (dict(rope=2, rope_cos=FAKE), taa.ATTN_ERR_INVALID_ARG),   # sin table missing
+    (dict(rope=1, rope_cos=FAKE, rope_sin=BAD), taa.ATTN_ERR_INVALID_ARG),
+    (dict(rope=1, rope_cos=FAKE, rope_sin=FAKE, rope_stride_b=-4), taa.ATTN_ERR_INVALID_ARG),
+    (dict(rope=2, rope_cos=FAKE, rope_sin=FAKE, rope_stride_b=6), taa.ATTN_ERR_INVALID_ARG),  # 16-byte rows
+    (dict(rope=1, rope_cos=FAKE, rope_sin=FAKE), taa.ATTN_ERR_WORKSPACE),                    # no K workspace
+    (dict(rope=2, rope_cos=FAKE, rope_sin=FAKE, rope_workspace=FAKE, rope_workspace_bytes=100),
+     taa.ATTN_ERR_WORKSPACE),
+    (dict(rope=2, rope_cos=FAKE, rope_sin=FAKE, rope_workspace=FAKE + 16, rope_workspace_bytes=1 << 30),
+     taa.ATTN_ERR_INVALID_ARG),                                                             # 256-byte alignment
     (dict(softmax_scale=float("nan")), taa.ATTN_ERR_INVALID_ARG),
     (dict(out_dtype=taa.ATTN_FP8_E4M3FN), taa.ATTN_ERR_UNSUPPORTED),
 ])
@@ -245,3 +257,9 @@ def test_prefill_causal_workspace_size():
     assert taa.attn_prefill_paged_causal_workspace_size(6, 2, 100, 256) == 6 * 100 * 256 * 4 + 6 * 100 * 4
     assert taa.attn_prefill_paged_causal_workspace_size(1, 1, 3, 256) == 3 * 256 * 4 + 3 * 4
     assert taa.attn_prefill_paged_causal_workspace_size(6, 4, 100, 256) == 0  # Hq not a multiple of Hkv
+
+
+def test_encoder_rope_workspace_size():
+    assert taa.attn_encoder_rope_workspace_size(1, 16, 2048, 64) == 16 * 2048 * 64 * 2
+    assert taa.attn_encoder_rope_workspace_size(2, 3, 100, 64, torch.float32) == 2 * 3 * 100 * 64 * 4
+    assert taa.attn_encoder_rope_workspace_size(0, 3, 100, 64) == 0

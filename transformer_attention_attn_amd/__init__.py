@@ -23,6 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libmi355attn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3FN = 0, 1, 2
+ATTN_ROPE_NONE, ATTN_ROPE_HALF, ATTN_ROPE_INTERLEAVED = 0, 1, 2
+_ROPE = {None: ATTN_ROPE_NONE, "half": ATTN_ROPE_HALF, "interleaved": ATTN_ROPE_INTERLEAVED}
 
 _lib = None
 
@@ -49,6 +51,9 @@ class EncoderArgs(ctypes.Structure):
         ("gamma", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("eps", ctypes.c_float),
         ("ln_out", ctypes.c_void_p), ("ln_dtype", ctypes.c_int),
         ("ln_mean", ctypes.c_void_p), ("ln_rstd", ctypes.c_void_p),
+        ("rope_cos", ctypes.c_void_p), ("rope_sin", ctypes.c_void_p), ("rope_stride_b", ctypes.c_int64),
+        ("rope", ctypes.c_int),
+        ("rope_workspace", ctypes.c_void_p), ("rope_workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -68,6 +73,8 @@ def load(path: str | None = None):
     L.attn_version.restype = I
     L.attn_encoder_fwd.argtypes = [ctypes.POINTER(EncoderArgs), P]
     L.attn_encoder_fwd.restype = I
+    L.attn_encoder_rope_workspace_size.argtypes = [I, I, I, I, I]
+    L.attn_encoder_rope_workspace_size.restype = Z
     L.attn_decode_gqa_workspace_size.argtypes = [I, I, I, I]
     L.attn_decode_gqa_workspace_size.restype = Z
     L.attn_decode_gqa.argtypes = [P, P, P, P, F, I, I, I, I, I, I, P, P, Z, P]
@@ -124,13 +131,21 @@ def _need_cuda(*ts):
 # ----------------------------------------------------------------------------- entry points
 
 
+def attn_encoder_rope_workspace_size(B: int, H: int, S_kv: int, D: int, dtype=torch.bfloat16) -> int:
+    return int(load().attn_encoder_rope_workspace_size(B, H, S_kv, D, _DT.get(dtype, -1)))
+
+
 def attn_encoder_fwd(q, k, v, softmax_scale: float, mask=None, *, out=None, out_dtype=torch.bfloat16,
                      want_out: bool = True, lse=None, residual=None, residual_out=None, gamma=None, beta=None,
                      eps: float = 1e-6, ln_out=None, ln_dtype=torch.bfloat16, want_ln: bool | None = None,
-                     ln_mean=None, ln_rstd=None, stream=None):
+                     ln_mean=None, ln_rstd=None, rope=None, rope_cos=None, rope_sin=None, rope_workspace=None,
+                     stream=None):
     """Non-causal SDPA over q/k/v [B,H,S,D] (bf16 or fp32, any strides with a
     unit d stride), optional additive key mask [B,1,1,S_kv] fp32, optional
     fused residual add (+ LayerNorm) into the fp32 residual stream [B,S,H*D].
+    rope: None, "half" or "interleaved", with fp32 tables rope_cos/rope_sin
+    [rows, D/2] (shared by the batch) or [B, rows, D/2]; rope_workspace
+    (uint8, allocated here when None) receives the rotated keys.
 
     Returns a dict of the produced tensors (out, lse, residual_out, ln_out,
     ln_mean, ln_rstd as requested).
@@ -179,6 +194,24 @@ def attn_encoder_fwd(q, k, v, softmax_scale: float, mask=None, *, out=None, out_
         a.ln_dtype = _DT.get(ln_out.dtype, -1)
     a.ln_mean = None if ln_mean is None else ln_mean.data_ptr()
     a.ln_rstd = None if ln_rstd is None else ln_rstd.data_ptr()
+    if rope not in _ROPE:
+        raise ValueError(f"rope must be one of {list(_ROPE)}")
+    a.rope = _ROPE[rope]
+    if rope is not None:
+        _need_cuda(rope_cos, rope_sin)
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            if t is None or t.dtype != torch.float32 or not t.is_contiguous() or t.shape[-1] != D // 2:
+                raise ValueError(f"{name} must be a contiguous fp32 [rows, D/2] or [B, rows, D/2] tensor")
+            if t.shape[-2] < max(Sq, Skv):
+                raise ValueError(f"{name} needs at least max(S_q, S_kv) rows")
+        if rope_cos.shape != rope_sin.shape:
+            raise ValueError("rope_cos and rope_sin must have one shape")
+        a.rope_cos, a.rope_sin = rope_cos.data_ptr(), rope_sin.data_ptr()
+        a.rope_stride_b = rope_cos.stride(0) if rope_cos.dim() == 3 else 0
+        if rope_workspace is None:
+            need = attn_encoder_rope_workspace_size(B, H, Skv, D, q.dtype)
+            rope_workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        a.rope_workspace, a.rope_workspace_bytes = rope_workspace.data_ptr(), rope_workspace.numel()
     _check(load().attn_encoder_fwd(ctypes.byref(a), _stream(stream)), "attn_encoder_fwd")
     for name, t in (("out", out), ("lse", lse), ("residual_out", residual_out), ("ln_out", ln_out),
                     ("ln_mean", ln_mean), ("ln_rstd", ln_rstd)):

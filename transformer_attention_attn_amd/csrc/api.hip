@@ -177,7 +177,13 @@ const char *attn_status_string(int status) {
   }
 }
 
-int attn_version(void) { return 10000; }
+int attn_version(void) { return 10100; }
+
+size_t attn_encoder_rope_workspace_size(int B, int H, int S_kv, int D, attn_dtype_t in_dtype) {
+  if (B <= 0 || H <= 0 || S_kv <= 0 || D <= 0) return 0;
+  if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F32) return 0;
+  return (size_t)B * H * S_kv * D * (in_dtype == ATTN_F32 ? 4 : 2);
+}
 
 int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
   if (!a) return ATTN_ERR_INVALID_ARG;
@@ -216,6 +222,15 @@ int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
   }
   if ((int64_t)a->B * a->H * ((a->S_q + encoder_rows_per_block() - 1) / encoder_rows_per_block()) > 0x7fffffffLL)
     return ATTN_ERR_UNSUPPORTED;
+  if (a->rope != ATTN_ROPE_NONE) {
+    if (a->rope != ATTN_ROPE_HALF && a->rope != ATTN_ROPE_INTERLEAVED) return ATTN_ERR_UNSUPPORTED;
+    if (!a->rope_cos || !a->rope_sin || !aligned16(a->rope_cos) || !aligned16(a->rope_sin)) return ATTN_ERR_INVALID_ARG;
+    if (a->rope_stride_b < 0 || a->rope_stride_b % 4) return ATTN_ERR_INVALID_ARG;
+    if (!a->rope_workspace ||
+        a->rope_workspace_bytes < attn_encoder_rope_workspace_size(a->B, a->H, a->S_kv, a->D, a->in_dtype))
+      return ATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(a->rope_workspace) & 255u) != 0) return ATTN_ERR_INVALID_ARG;
+  }
 
   EncoderLaunch L;
   memset(&L, 0, sizeof L);
@@ -240,6 +255,34 @@ int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
   L.lse = a->lse;
   L.res = a->residual;
   L.res_out = a->residual_out;
+  L.rope = (int)a->rope;
+  L.rope_cos = a->rope_cos;
+  L.rope_sin = a->rope_sin;
+  L.rope_sb = a->rope_stride_b;
+  if (a->rope != ATTN_ROPE_NONE) {
+    // K rotated once into the workspace (contiguous [B,H,S_kv,D]), read from there
+    RopeLaunch R;
+    memset(&R, 0, sizeof R);
+    R.k = a->k;
+    for (int i = 0; i < 4; ++i) R.ks[i] = a->k_stride[i];
+    R.out = a->rope_workspace;
+    R.B = a->B;
+    R.H = a->H;
+    R.S = a->S_kv;
+    R.D = a->D;
+    R.f32 = a->in_dtype == ATTN_F32;
+    R.rope = (int)a->rope;
+    R.cos = a->rope_cos;
+    R.sin = a->rope_sin;
+    R.sb = a->rope_stride_b;
+    const int rc0 = hip_status(launch_rope_k(R, stream));
+    if (rc0 != ATTN_OK) return rc0;
+    L.k = a->rope_workspace;
+    L.ks[0] = (int64_t)a->H * a->S_kv * a->D;
+    L.ks[1] = (int64_t)a->S_kv * a->D;
+    L.ks[2] = a->D;
+    L.ks[3] = 1;
+  }
   int rc = hip_status(launch_encoder(L, a->in_dtype == ATTN_F32, stream));
   if (rc != ATTN_OK || !a->ln_out) return rc;
 

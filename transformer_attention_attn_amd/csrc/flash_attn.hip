@@ -121,6 +121,35 @@ struct Geo {
 // keys it*NSPLIT*BN ...) into a register stage and writes them to an LDS
 // buffer.  Keys past n_keys read as zeros (buffer range check).
 
+// Rotary position embedding (vit-encoder-neuron-kernels, "Kernels"): pair k
+// of token s turns by the angle of the tables' (cos[s,k], sin[s,k]); pairing
+// 1 ("half") pairs lane k with lane k + D/2, pairing 2 ("interleaved") lane
+// 2k with lane 2k + 1.  For a pair (a, b): a' = a cos - b sin,
+// b' = b cos + a sin, in fp32, rounded to bf16 afterwards.
+__device__ __forceinline__ void rot_pair(float &a, float &b, float c, float s) {
+  const float a2 = __builtin_fmaf(-b, s, a * c);
+  b = __builtin_fmaf(a, s, b * c);
+  a = a2;
+}
+
+// 8 raw elements (bf16: one u32x4; fp32: two) <-> fp32
+template <bool F32>
+__device__ __forceinline__ void unpack8(const u32x4_t (&x)[F32 ? 2 : 1], float (&f)[8]) {
+  if constexpr (F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(x[i / 4][i % 4]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(x[0][i]);
+      f[2 * i + 1] = bf16_hi(x[0][i]);
+    }
+  }
+}
+__device__ __forceinline__ u32x4_t pack8(const float (&f)[8]) {
+  return u32x4_t{pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7])};
+}
+
 // Encoder K/V: [B,H,S_kv,D] strided, bf16 or fp32 (fp32 rounded to bf16 on
 // the LDS write).  A unit is 8 elements of one key; unit u of an iteration is
 // key (u / KU)*BN + (u % KU)/(D/8) of the iteration, chunk u % (D/8).
@@ -201,7 +230,8 @@ struct EncSrc {
     for (int j = 0; j < UK; ++j) {
       const unsigned u = tid + j * G::THREADS;
       const unsigned t = (u % KU) / CPR;
-      *reinterpret_cast<u32x4_t *>(slot + (u / KU) * G::KTILE + G::k_row(t) + 16 * chunk_of(u)) = to_bf16(st.k[j]);
+      const u32x4_t x = to_bf16(st.k[j]);
+      *reinterpret_cast<u32x4_t *>(slot + (u / KU) * G::KTILE + G::k_row(t) + 16 * chunk_of(u)) = x;
     }
   }
   // V rows of keys the mask removes are written as zeros (p = 0 there, and a
@@ -823,7 +853,7 @@ __device__ __forceinline__ u32x4_t neg_bf16x8(u32x4_t x, uint32_t sign) {
 
 // ------------------------------------------------------------------ encoder kernel
 
-template <class G, bool F32IN, bool HAS_MASK>
+template <class G, bool F32IN, bool HAS_MASK, int ROPE>
 __global__ __launch_bounds__(G::THREADS) __attribute__((amdgpu_waves_per_eu(G::WPE, G::WPE)))
 void encoder_fwd_kernel(EncoderLaunch a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];  // G::LDS bytes
@@ -838,28 +868,50 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   const uint32_t qsign = a.q_neg ? 0x80008000u : 0u;
 
   // Q fragments (B operand of S^T = K Q^T): row = lane%32, 8 d per lane-half
+  // (fragment sd holds d = 16 sd + 8 hh ..; both RoPE pairings stay inside a
+  // lane: interleaved pairs inside a fragment, rotate-half pairs fragment sd
+  // with sd + SD/2)
   u32x4_t qf[G::NT][G::SD];
   const char *qb = reinterpret_cast<const char *>(a.q) + (b * a.qs[0] + h * a.qs[1]) * ES;
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
     const int row = qt * G::BM + (rg * G::NT + nt) * 32 + l32;
+    float f[G::SD][8];
 #pragma unroll
     for (int sd = 0; sd < G::SD; ++sd) {
       const char *p = qb + (row * a.qs[2] + 16 * sd + 8 * hh) * ES;
-      u32x4_t x = {0, 0, 0, 0};
+      u32x4_t x[F32IN ? 2 : 1] = {};
       if (row < a.Sq) {
-        if constexpr (F32IN) {
-          const u32x4_t x0 = ldg<u32x4_t>(p), x1 = ldg<u32x4_t>(p + 16);
-          x = u32x4_t{pack_bf16(__uint_as_float(x0[0]), __uint_as_float(x0[1])),
-                      pack_bf16(__uint_as_float(x0[2]), __uint_as_float(x0[3])),
-                      pack_bf16(__uint_as_float(x1[0]), __uint_as_float(x1[1])),
-                      pack_bf16(__uint_as_float(x1[2]), __uint_as_float(x1[3]))};
-        } else {
-          x = ldg<u32x4_t>(p);
+        x[0] = ldg<u32x4_t>(p);
+        if constexpr (F32IN) x[1] = ldg<u32x4_t>(p + 16);
+      }
+      unpack8<F32IN>(x, f[sd]);
+    }
+    if (ROPE != 0 && row < a.Sq) {
+      const float *rc = a.rope_cos + b * a.rope_sb + (int64_t)row * (G::D / 2);
+      const float *rs = a.rope_sin + b * a.rope_sb + (int64_t)row * (G::D / 2);
+      if constexpr (ROPE == 1) {
+#pragma unroll
+        for (int sd = 0; sd < G::SD / 2; ++sd) {
+          const int k0 = 16 * sd + 8 * hh;
+          const f32x4_t c0 = ldg<f32x4_t>(rc + k0), c1 = ldg<f32x4_t>(rc + k0 + 4);
+          const f32x4_t s0 = ldg<f32x4_t>(rs + k0), s1 = ldg<f32x4_t>(rs + k0 + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            rot_pair(f[sd][e], f[sd + G::SD / 2][e], e < 4 ? c0[e] : c1[e - 4], e < 4 ? s0[e] : s1[e - 4]);
+        }
+      } else if constexpr (ROPE == 2) {
+#pragma unroll
+        for (int sd = 0; sd < G::SD; ++sd) {
+          const int k0 = 8 * sd + 4 * hh;
+          const f32x4_t c = ldg<f32x4_t>(rc + k0), sn = ldg<f32x4_t>(rs + k0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rot_pair(f[sd][2 * i], f[sd][2 * i + 1], c[i], sn[i]);
         }
       }
-      qf[nt][sd] = neg_bf16x8(x, qsign);
     }
+#pragma unroll
+    for (int sd = 0; sd < G::SD; ++sd) qf[nt][sd] = neg_bf16x8(pack8(f[sd]), qsign);
   }
 
   EncSrc<G, F32IN, HAS_MASK> src;
@@ -1114,16 +1166,28 @@ hipError_t launch_lds(K kernel, dim3 grid, const A &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ROPE here rotates the Q rows as they are loaded; K arrives rotated (the
+// RoPE pass of rope.hip).
+template <int ROPE>
+static hipError_t launch_encoder_r(const EncoderLaunch &a, bool f32_in, dim3 grid, hipStream_t stream) {
+  if (f32_in)
+    return a.mask ? launch_lds<EncGeoF32>(encoder_fwd_kernel<EncGeoF32, true, true, ROPE>, grid, a, stream)
+                  : launch_lds<EncGeoF32>(encoder_fwd_kernel<EncGeoF32, true, false, ROPE>, grid, a, stream);
+  return a.mask ? launch_lds<EncGeoMask>(encoder_fwd_kernel<EncGeoMask, false, true, ROPE>, grid, a, stream)
+                : launch_lds<EncGeo>(encoder_fwd_kernel<EncGeo, false, false, ROPE>, grid, a, stream);
+}
+
 hipError_t launch_encoder(const EncoderLaunch &a, bool f32_in, hipStream_t stream) {
   const int n_qt = (a.Sq + EncGeo::BM - 1) / EncGeo::BM;
   const dim3 grid(n_qt * a.H * a.B);
   static_assert(EncGeo::BM == EncGeoF32::BM && EncGeo::THREADS == EncGeoF32::THREADS, "same launch shape");
   static_assert(EncGeo::BM == EncGeoMask::BM && EncGeo::THREADS == EncGeoMask::THREADS, "same launch shape");
-  if (f32_in)
-    return a.mask ? launch_lds<EncGeoF32>(encoder_fwd_kernel<EncGeoF32, true, true>, grid, a, stream)
-                  : launch_lds<EncGeoF32>(encoder_fwd_kernel<EncGeoF32, true, false>, grid, a, stream);
-  return a.mask ? launch_lds<EncGeoMask>(encoder_fwd_kernel<EncGeoMask, false, true>, grid, a, stream)
-                : launch_lds<EncGeo>(encoder_fwd_kernel<EncGeo, false, false>, grid, a, stream);
+  switch (a.rope) {
+    case 0: return launch_encoder_r<0>(a, f32_in, grid, stream);
+    case 1: return launch_encoder_r<1>(a, f32_in, grid, stream);
+    case 2: return launch_encoder_r<2>(a, f32_in, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 int encoder_rows_per_block() { return EncGeo::BM; }

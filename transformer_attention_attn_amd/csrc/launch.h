@@ -21,6 +21,20 @@ struct EncoderLaunch {
   float *lse;                   // nullable [B,H,Sq]
   const float *res;             // nullable [B,Sq,H*D]
   float *res_out;               // nullable (non-null iff res non-null)
+  const float *rope_cos, *rope_sin;  // RoPE tables [rows, D/2] fp32 (rope != 0; q rows only, K comes rotated)
+  int64_t rope_sb;              // table batch stride in floats (0: shared)
+  int rope;                     // 0 none, 1 rotate-half pairing, 2 interleaved pairing
+};
+
+// K rotation pass of the encoder's RoPE: k [B,H,S,D] strided -> out [B,H,S,D]
+// contiguous, same dtype.
+struct RopeLaunch {
+  const void *k;
+  int64_t ks[4];                 // element strides {b,h,s,d}, d stride 1
+  void *out;
+  int B, H, S, D, f32, rope;     // rope: 1 rotate-half, 2 interleaved
+  const float *cos, *sin;        // [rows, D/2] per batch entry (+ b * sb)
+  int64_t sb;
 };
 
 struct PrefillLaunch {
@@ -72,6 +86,7 @@ hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
 int decode_chunk_keys();
 int decode_max_groups();
 hipError_t launch_res_ln(const ResLnLaunch &a, hipStream_t stream);
+hipError_t launch_rope_k(const RopeLaunch &a, hipStream_t stream);
 int res_ln_max_hidden();
 
 }  // namespace mi355
