@@ -279,6 +279,9 @@ def summarize(prof_dir: str) -> None:
     for r in csv.DictReader(open(one("trace/*kernel_stats.csv"))):
         if not _short(r["Name"]):  # not one of this library's kernels (e.g. the cache flush)
             continue
+        if _short(r["Name"]) in stats:
+            raise SystemExit(f"summarize: two kernels of family {_short(r['Name'])} in the trace; profile the "
+                             "step alone (bench.py --no-next)")
         stats[_short(r["Name"])] = {"kernel": r["Name"], "calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
                                     "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
     cal = {}
@@ -322,6 +325,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4, help="query tokens in the CPU-baseline sample (0: skip)")
     ap.add_argument("--only", choices=["all", "encoder", "decode", "prefill", "next"], default="all",
                     help="run a single kernel family (profiling runs)")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the workload variants reported under parts.next (profiling runs of the step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (scales the rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -459,7 +464,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": p["gbps"], "peak": acc.PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": p["frac_hbm_peak"], "traffic": None, "kernel": "decode_split_kernel+decode_combine_kernel"}
 
-    if args.only in ("all", "next"):
+    if args.only in ("all", "next") and not args.no_next:
         parts["next"] = time_next_workloads(taa, dev, flush, (pre, p_q, p_k, p_v, p_bt))
 
     cpu = None
