@@ -322,7 +322,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=4, help="query tokens in the CPU-baseline sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=160,
+                    help="query tokens in the CPU-baseline sample, about 10 s of oracle work on 16 cores (0: skip)")
     ap.add_argument("--only", choices=["all", "encoder", "decode", "prefill", "next"], default="all",
                     help="run a single kernel family (profiling runs)")
     ap.add_argument("--no-next", action="store_true",
