@@ -9,6 +9,9 @@
  *    allocates or frees memory, never synchronizes, and enqueues all of its work on `stream` (0 = the null
  *    stream).  Calls are asynchronous: a return of ATTN_OK means the work was
  *    enqueued.
+ *  - Calls enqueue kernel launches only (no memset, copy or event), so they
+ *    can be captured into a HIP graph and replayed; every replay recomputes
+ *    from the inputs (workspace contents on entry are never read as state).
  *  - Arguments are validated on the host before anything is launched.  A
  *    failed check returns an error code and leaves every output untouched.
  *  - Device DATA is not inspected on the host: a block-table entry outside
