@@ -43,16 +43,42 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """C/C++/HIP source with comments removed and whitespace runs collapsed to
+    one space: the text the compiler acts on, up to layout.  String and
+    character literals are kept as written."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        ch = src[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and src[j] != ch:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: measured HBM traffic is only reported for the
-    exact kernels it was counted on."""
+    """Hash of the HIP sources' code (comments and layout ignored): measured
+    HBM traffic is only reported for the exact kernels it was counted on."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transformer_attention_attn_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(f.encode() + b"\0" + code_text(open(os.path.join(csrc, f)).read()).encode() + b"\0")
     return h.hexdigest()[:16]
 
 

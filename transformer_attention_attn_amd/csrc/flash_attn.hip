@@ -1,15 +1,15 @@
 // Tiled online-softmax ("flash") attention forward for gfx950.
 //
-// One kernel template serves three callers:
+// One key loop (flash_loop) serves three kernels:
 //   * the non-causal encoder (q/k/v [B,H,S,D] bf16 or fp32, optional additive
-//     key mask, fused residual-add epilogue);
+//     key mask, optional RoPE on the Q rows, fused residual-add epilogue);
 //   * the history-only GQA prefill over a paged FP8 (e4m3fn) KV cache, whose
 //     G query heads per KV head are packed into the M dimension (rows r of a KV
 //     head are (head g, token t) with r = g*Lq + t);
-//   * the same prefill followed, in the same workgroup, by causal attention
-//     over the current tokens' bf16 K/V: the online softmax state of the
-//     history loop carries into a second loop, which is the log-sum-exp merge
-//     of the two parts done in registers.
+//   * causal attention over the current tokens' bf16 K/V, launched after the
+//     history prefill: that kernel hands over its normalised fp32 output and
+//     lse per row, and this one resumes the online softmax from them, which
+//     is the log-sum-exp merge of the two parts.
 //
 // Prefill Context-Parallel Attention POC for Trainium2, "Layout": Q heads that
 // share a KV head are packed together, online max/sum stay fp32 while the
@@ -21,7 +21,8 @@
 // Per workgroup: BM = 32*NT*RG query rows, RG row-group waves times NSPLIT
 // key-split waves.  Split s handles key tiles s, s+NSPLIT, ...; the splits
 // are merged through LDS at the end (log-sum-exp merge).  Each wave owns
-// 32*NT rows; its Q fragments stay in registers for the whole loop.
+// 32*NT rows; its Q fragments stay on chip for the whole loop, in registers
+// except the first Geo::QL, which sit in LDS.
 //
 // Per key tile (BN keys), per wave:
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys on M, query rows on N), so
@@ -694,7 +695,7 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
 
 // ------------------------------------------------------------------ core loop
 
-// The pipelined key loop shared by both kernels.  LDS holds two K buffers and
+// The pipelined key loop of all three kernels.  LDS holds two K buffers and
 // two V buffers; iteration `it` (every split's tile `it`) reads K(it+1) and
 // V(it), writes K(it+2) into the K buffer K(it) used and V(it+1) into the
 // other V buffer, and issues the global loads of K(it+3) and V(it+2) into the
@@ -703,10 +704,8 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
 // Without an additive mask, `mk` masks the scores of each tile (TailMask,
 // CausalMask).  `fresh` starts a new softmax state; otherwise the loop
 // continues the one in `ws` (same log2 units: c must give true scores times
-// log2(e)).  `tid` is threadIdx.x (a caller running two loops passes the
-// second one a pinned copy, so that no per-lane offset of the second loop is
-// computed early and kept live through the first).  Returns with the LDS
-// free (barrier passed).
+// log2(e)).  `tid` is threadIdx.x.  Returns with the LDS free (barrier
+// passed).
 template <class G, bool HAS_MASK, class Src, class Mask>
 __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, const u32x4_t (&qf)[G::NT][G::SD],
                                            char *smem, float c, const Mask &mk, bool fresh, unsigned tid) {
