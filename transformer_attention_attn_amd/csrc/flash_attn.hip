@@ -544,6 +544,10 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
   constexpr int NP = G::NT * G::KB * 4;  // P pairs of the first half
   constexpr int SLOTS = G::NFQ - 2;
   constexpr int PPS = (NP + SLOTS - 1) / SLOTS;
+  // With at least one slot per pair, pairs are spaced evenly over slots
+  // 2 .. NFQ-1 (one every SPA slots) so that no slot's VALU slice outgrows
+  // its MFMA; otherwise PPS consecutive pairs per slot.
+  constexpr int SPA = SLOTS >= NP && NP > 1 ? (SLOTS - 1) / (NP - 1) : 0;
   static_assert(SLOTS >= 1, "QK slots");
   const int h = lane >> 5;
   const char *kbase = kt + (lane & 31) * G::KROW + 16 * h;
@@ -634,6 +638,8 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
         pin_out(pc.lsum[nt]);
         pin_out(alpha[nt]);
       }
+    } else if constexpr (SPA > 0) {
+      if ((f - 2) % SPA == 0 && (f - 2) / SPA < NP) p_pairs<G, HAS_MASK>(pc, s, 0, (f - 2) / SPA, (f - 2) / SPA + 1, c);
     } else {
       const int p0 = (f - 2) * PPS, p1 = (f - 1) * PPS < NP ? (f - 1) * PPS : NP;
       if (p0 < p1) p_pairs<G, HAS_MASK>(pc, s, 0, p0, p1, c);
@@ -644,8 +650,8 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
   return any;
 }
 
-// Phase B: O^T += V^T P^T for one tile.  Its first slots compute the second
-// half of P (needed from PV MFMA MT on), the next ones the staging work of the
+// Phase B: O^T += V^T P^T for one tile.  Slots before MT compute the second
+// half of P (needed from PV MFMA MT on), later ones the staging work of the
 // tile step (`work(k)`, k = 0, 1, 2).  The A fragment (d rows mt*32 + lane%32,
 // k-slots j = 0..7 of lane-half h) must hold the keys P's B fragment holds:
 // kb*32 + 16kk + 8(j/4) + 4h + j%4.  Two transposing reads (t = j/4) fetch
@@ -660,6 +666,11 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
   constexpr int NP = G::NT * G::KB * 4;                 // P pairs of the second half
   constexpr int PPS = (NP + G::MT - 1) / G::MT;          // spread over the first MT slots
   constexpr int PSLOTS = (NP + PPS - 1) / PPS;
+  // With MT >= NP: one pair every SPB slots of the first MT, the three
+  // staging items every WS slots from slot MT on (even VALU per slot).
+  constexpr int SPB = G::MT >= NP ? G::MT / NP : 0;
+  constexpr int WS = (G::NFV - 1 - G::MT) / 2;
+  static_assert(SPB == 0 || (WS >= 1 && G::MT + 2 * WS < G::NFV), "phase B schedule");
   const int h = lane >> 5, j = (lane >> 2) & 3, m = lane & 3, g2 = (lane >> 4) & 1;
   const char *vbase = vt + G::v_row(4 * h) + G::v_row(j) + 32 * g2 + 8 * m;
   u32x4_t fb[G::NFV];
@@ -688,7 +699,10 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
 #pragma unroll
   for (int q = 0; q < G::NFV; ++q) {
     if (!G::VFIRST) pv_slot(q);
-    if (q < PSLOTS) {
+    if constexpr (SPB > 0) {
+      if (q % SPB == 0 && q / SPB < NP) p_pairs<G, HAS_MASK>(pc, s, 1, q / SPB, q / SPB + 1, c);
+      else if (q >= G::MT && (q - G::MT) % WS == 0 && (q - G::MT) / WS <= 2) work((q - G::MT) / WS);
+    } else if (q < PSLOTS) {
       p_pairs<G, HAS_MASK>(pc, s, 1, q * PPS, (q + 1) * PPS < NP ? (q + 1) * PPS : NP, c);
     } else {
       const int k = q - PSLOTS;
