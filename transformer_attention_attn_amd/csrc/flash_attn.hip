@@ -52,6 +52,7 @@
 namespace mi355 {
 
 constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
+constexpr float kFloatMax = __FLT_MAX__;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family: 32-bit data format, no swizzle)
 
 // Raw buffer resource over [base, base + bytes).  Both are uniform at every
@@ -186,10 +187,13 @@ struct EncSrc {
   static __device__ __forceinline__ unsigned chunk_of(unsigned u) { return u % CPR; }
 
   // bytes of the iteration's keys that exist (the key stride is below 2^24
-  // bytes, checked on the host)
+  // bytes, checked on the host).  A select on the uniform iteration index
+  // against loop-invariant bounds keeps this on the scalar unit (a clamp
+  // compiles to a vector med3 and a vector multiply).
   __device__ __forceinline__ uint32_t records(int it, uint32_t row) const {
-    const int rem = min(max(n_keys - it * KEYS, 0), KEYS);
-    return (uint32_t)rem * row;
+    const int full = n_keys / KEYS;  // iterations whose keys all exist
+    const uint32_t n = it < full ? (uint32_t)KEYS : it == full ? (uint32_t)(n_keys % KEYS) : 0u;
+    return n * row;
   }
   __device__ __forceinline__ int64_t tile_base(int) const { return 0; }
 
@@ -293,8 +297,10 @@ struct PagedSrc {
     const int32_t phys = bt[key0 / (unsigned)bs];
     return (int64_t)phys * blk_stride + head_off + (int64_t)(key0 % (unsigned)bs) * G::D;
   }
-  __device__ __forceinline__ uint32_t records(int it) const {
-    return (uint32_t)min(max(n_keys - it * G::BN, 0), G::BN) * G::D;
+  __device__ __forceinline__ uint32_t records(int it) const {  // scalar select, as EncSrc::records
+    const int full = n_keys / G::BN;
+    const uint32_t n = it < full ? (uint32_t)G::BN : it == full ? (uint32_t)(n_keys % G::BN) : 0u;
+    return n * G::D;
   }
   static __device__ __forceinline__ u32x2_t load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
@@ -605,12 +611,17 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
               s[nt][kb][v] = mv == -INFINITY ? -INFINITY : __builtin_fmaf(s[nt][kb][v], c, mv);
             }
         }
-        float mloc = -INFINITY;
+        // one max3 per pair of scores; the pin keeps the chain (left free,
+        // the compiler rebuilds it as a tree of max and max3 that takes 11
+        // instructions for 16 scores instead of 8)
+        float mloc = __builtin_fmaxf(s[nt][0][0], s[nt][0][1]);
 #pragma unroll
         for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
-          for (int v = 0; v < 16; v += 2)
+          for (int v = kb == 0 ? 2 : 0; v < 16; v += 2) {
             mloc = __builtin_fmaxf(mloc, __builtin_fmaxf(s[nt][kb][v], s[nt][kb][v + 1]));
+            pin_in(mloc);
+          }
         mx[nt] = mloc;
         pin_out(mx[nt]);
       }
@@ -628,11 +639,15 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
       for (int nt = 0; nt < G::NT; ++nt) {
         // per row: a row's reference moves only on its own scores, so its
         // result never depends on the other rows of the wave (alpha = 1
-        // leaves the rows that keep theirs bit-identical)
-        const float m_new = grow_row[nt] ? fmaxf(ws.m[nt], mx[nt]) : ws.m[nt];
-        alpha[nt] = m_new == -INFINITY ? 1.0f : fast_exp2(ws.m[nt] - m_new);
+        // leaves the rows that keep theirs bit-identical).  A growing row's
+        // tile max exceeds its old reference, so it is the new one, and is
+        // finite: exp2(m - mx) is 0 for a first live tile (m = -inf).  A row
+        // with no live key yet keeps m = -inf; its exponents use the lowest float
+        // instead (-kFloatMax), which gives p = 0 for its -inf scores without a NaN.
+        const float m_new = grow_row[nt] ? mx[nt] : ws.m[nt];
+        alpha[nt] = grow_row[nt] ? fast_exp2(ws.m[nt] - mx[nt]) : 1.0f;
         ws.m[nt] = m_new;
-        pc.m_use[nt] = m_new == -INFINITY ? 0.0f : m_new;
+        pc.m_use[nt] = fmaxf(m_new, -kFloatMax);
         pc.lsum[nt] = ws.l[nt] * alpha[nt];
         pin_out(pc.m_use[nt]);
         pin_out(pc.lsum[nt]);
