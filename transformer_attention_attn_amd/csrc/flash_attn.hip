@@ -784,6 +784,9 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
   f32x16_t s[G::NT][G::KB];
   qk_tile<G>(s, qf, qa, kbuf + sp * G::KTILE, lane);
   if constexpr (!HAS_MASK) mk.template apply<G>(s, sp * G::BN, lane);
+  // iteration 0 writes K(2) into K(0)'s buffer: every wave must have read
+  // K(0) first
+  __syncthreads();
 
   // One tile step: S holds S(it) on entry, SN receives S(it+1).  The loop
   // below alternates the two register sets instead of copying S each step;
