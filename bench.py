@@ -7,14 +7,16 @@ One step = one pass over every kernel of the path, each on its workload:
   * GQA decode: B=8, 16 query / 8 KV heads, head_dim 256, S_ctx 4096,
     ragged lengths len_b ~ U{1..4096};
   * paged FP8 prefill: 4096 query tokens x 32 heads over 2 KV heads, D=256,
-    512-token blocks under a permuted block table, 120000 live history keys.
+    512-token blocks under a permuted block table, 120000 live history keys,
+    through its workspace (the live history expanded to bf16 tile images,
+    then the key loop; both kernels inside the timed call).
 All inputs are synthetic, seeded, and resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is the step's attention throughput (QK^T + PV
 FLOPs of the three attention calls over the step time); `parts` gives each
 kernel's own metric (TFLOP/s and % of the bf16 MFMA peak, or GB/s and % of
 HBM peak) from HIP events recorded on the stream the kernels run on;
-`roofline` is the dominant kernel's (the prefill).  `cpu_baseline` times the
+`roofline` is the dominant call's (the prefill: its two kernels).  `cpu_baseline` times the
 fp64 oracle on a bounded sample of the prefill workload on the host cores.
 """
 from __future__ import annotations
@@ -264,13 +266,20 @@ def time_next_workloads(taa, dev, flush, pre_dev, reps: int = 20):
     out["paged_fp8_prefill_q4096_hist120000_plus_causal_current"] = {
         "ms": ms, "tflops": tf, "frac_bf16_peak": tf / acc.PEAK_BF16_TFLOPS, "flops_history": f_hist,
         "flops_current": f_cur}
+    # the step's prefill without a workspace: the key loop converts each fp8
+    # tile itself (attn_prefill_paged)
+    ms = timed_b2b(lambda: taa.attn_prefill_paged(p_q, p_k, p_v, pre.k_scale, pre.v_scale, p_bt, pre.L_act,
+                                                  pre.scale, pre.G, out=o), r3)
+    tf = f_hist / (ms * 1e-3) / 1e12
+    out["paged_fp8_prefill_q4096_hist120000_no_workspace"] = {
+        "ms": ms, "tflops": tf, "frac_bf16_peak": tf / acc.PEAK_BF16_TFLOPS, "flops": f_hist}
     return out
 
 
 def _short(name: str) -> str:
     """Kernel family name from a demangled rocprofv3 kernel name."""
-    for k in ("prefill_paged_kernel", "encoder_fwd_kernel", "res_ln_kernel", "decode_split_kernel",
-              "decode_combine_kernel", "copyBuffer"):
+    for k in ("prefill_paged_kernel", "prefill_tile_images_kernel", "encoder_fwd_kernel", "res_ln_kernel",
+              "decode_split_kernel", "decode_combine_kernel", "copyBuffer"):
         if k in name:
             return k
     return None
@@ -401,6 +410,8 @@ def main():
 
     p_q, p_k, p_v, p_bt = (t.to(dev) for t in (pre.q, pre.k_cache, pre.v_cache, pre.block_table))
     p_out = torch.empty_like(p_q)
+    p_ws = torch.empty(taa.attn_prefill_paged_expanded_workspace_size(pre.Hkv, pre.L_act, pre.D), dtype=torch.uint8,
+                       device=dev)
     # 512 MiB written before every decode call (outside its timer), so its
     # ~134 MB of K/V come from HBM and not from the 256 MB Infinity Cache
     flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
@@ -428,8 +439,8 @@ def main():
                 t_dec.stop(s)
         if run_pre:
             s = t_pre.start() if timed else None
-            taa.attn_prefill_paged(p_q, p_k, p_v, pre.k_scale, pre.v_scale, p_bt, pre.L_act, pre.scale, pre.G,
-                                   out=p_out)
+            taa.attn_prefill_paged_expanded(p_q, p_k, p_v, pre.k_scale, pre.v_scale, p_bt, pre.L_act, pre.scale,
+                                            pre.G, out=p_out, workspace=p_ws)
             if timed:
                 t_pre.stop(s)
 
@@ -474,14 +485,20 @@ def main():
         tf = f_pre / (statistics.fmean(ms) * 1e-3) / 1e12
         parts["prefill"] = {**summ(ms), "tflops": tf, "frac_bf16_peak": tf / acc.PEAK_BF16_TFLOPS, "flops": f_pre,
                             "tflops_at_131072_convention": acc.prefill_flops(pre.Lq, pre.Hq, 131072, pre.D)
-                            / (statistics.fmean(ms) * 1e-3) / 1e12}
+                            / (statistics.fmean(ms) * 1e-3) / 1e12,
+                            "kernels": "tile images (fp8 history -> bf16), key loop"}
 
     roofline = None
     if run_pre:
         p = parts["prefill"]
+        # one prefill call = the tile-image pass + the key loop; both count
+        # toward its time (achieved) and its HBM bytes (traffic)
+        t_img, t_loop = measured_traffic("prefill_tile_images_kernel"), measured_traffic("prefill_paged_kernel")
         roofline = {"bound": "mfma", "achieved": p["tflops"], "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": p["tflops"] / acc.PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill_paged_kernel"),
-                    "kernel": "prefill_paged_kernel", "kernel_source_hash": kernel_source_hash()}
+                    "frac": p["tflops"] / acc.PEAK_BF16_TFLOPS,
+                    "traffic": t_img + t_loop if t_img is not None and t_loop is not None else None,
+                    "kernel": "prefill_tile_images_kernel + prefill_paged_kernel",
+                    "kernel_source_hash": kernel_source_hash()}
     elif run_enc:
         p = parts["encoder_block"]
         roofline = {"bound": "mfma", "achieved": p["tflops"], "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

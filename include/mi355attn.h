@@ -227,6 +227,31 @@ ATTN_API int attn_prefill_paged(const void *q, const void *k_cache, const void *
                        int Hq, int Hkv, int Lq, int D, void *out, float *lse, hipStream_t stream);
 
 /*
+ * The history-only GQA prefill of attn_prefill_paged, computed through a
+ * workspace: the same operation, arguments and requirements, the same
+ * result (the fp8 codes expand to bf16 exactly either way).
+ *
+ * Follows: the same page, "Layout" and "Current POC constraints"; its FP8
+ * K/V is consumed by bf16 matmuls.  Here the live history
+ * (actual_history_len keys of every KV head) is first expanded once per call
+ * into bf16 tiles of 32 keys laid out as the attention kernel's on-chip
+ * buffers hold them; the attention kernel then copies each tile from memory
+ * into on-chip storage directly, with no per-tile conversion.  Faster at long
+ * histories; costs one pass over the live history (fp8 read, bf16 written).
+ *   workspace: at least attn_prefill_paged_expanded_workspace_size(Hkv,
+ *   actual_history_len, D) bytes (Hkv * ceil(actual_history_len / 32) *
+ *   34816 at D = 256), 256-byte aligned, owned by the caller; contents on
+ *   entry ignored, overwritten.  Missing or too small: ATTN_ERR_WORKSPACE.
+ *   The size function returns 0 for invalid or unsupported arguments.
+ */
+ATTN_API size_t attn_prefill_paged_expanded_workspace_size(int Hkv, int actual_history_len, int D);
+ATTN_API int attn_prefill_paged_expanded(const void *q, const void *k_cache, const void *v_cache, float k_scale,
+                                float v_scale, const int32_t *block_table, int max_blocks, int num_blocks,
+                                int block_size, int actual_history_len, float softmax_scale, int num_kv_groups,
+                                int Hq, int Hkv, int Lq, int D, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Paged history plus causal current-token GQA prefill.
  *
  * Follows: Prefill Context-Parallel Attention POC for Trainium2, introduction

@@ -34,6 +34,7 @@ def test_header_declares_the_four_entry_points():
     for n in ("attn_encoder_fwd", "attn_decode_gqa", "attn_prefill_paged", "res_ln",
               "attn_decode_gqa_workspace_size", "attn_decode_gqa_window", "attn_decode_gqa_window_workspace_size",
               "attn_prefill_paged_causal", "attn_prefill_paged_causal_workspace_size",
+              "attn_prefill_paged_expanded", "attn_prefill_paged_expanded_workspace_size",
               "attn_encoder_rope_workspace_size", "attn_status_string", "attn_version"):
         assert n in names
 
@@ -54,7 +55,7 @@ def test_status_strings(lib):
     for s in range(5):
         assert taa.attn_status_string(s).startswith(("ATTN_OK", "ATTN_ERR"))
     assert taa.attn_status_string(99) == "unknown attn status"
-    assert taa.attn_version() == 10100
+    assert taa.attn_version() == 10200
 
 
 def _enc(**kw):
@@ -203,6 +204,39 @@ def _pre(**kw):
 ])
 def test_prefill_validation(lib, kw, expect):
     assert lib.attn_prefill_paged(*_pre(**kw)) == expect
+
+
+def _pex(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=1.0, vs=1.0, bt=FAKE, maxb=256, nb=256, bs=512, L=120000, scale=0.0625,
+             G=16, Hq=32, Hkv=2, Lq=4096, D=256, out=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return (a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["maxb"], a["nb"], a["bs"], a["L"], a["scale"],
+            a["G"], a["Hq"], a["Hkv"], a["Lq"], a["D"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(bt=None), taa.ATTN_ERR_INVALID_ARG),
+    (dict(L=0), taa.ATTN_ERR_INVALID_ARG),
+    (dict(L=256 * 512 + 1), taa.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=31), taa.ATTN_ERR_INVALID_ARG),
+    (dict(D=128), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(ks=0.0), taa.ATTN_ERR_INVALID_ARG),
+    (dict(out=BAD), taa.ATTN_ERR_INVALID_ARG),
+    (dict(ws=None), taa.ATTN_ERR_WORKSPACE),
+    (dict(wsb=2 * 3750 * 34816 - 1), taa.ATTN_ERR_WORKSPACE),   # one byte short of the live history's tiles
+    (dict(ws=FAKE + 16), taa.ATTN_ERR_INVALID_ARG),             # workspace must be 256-byte aligned
+])
+def test_prefill_expanded_validation(lib, kw, expect):
+    assert lib.attn_prefill_paged_expanded(*_pex(**kw)) == expect
+
+
+def test_prefill_expanded_workspace_size():
+    # per KV head, one 34816-byte image (16 KiB of K, 32 padded 576-byte V rows) per 32 live keys
+    assert taa.attn_prefill_paged_expanded_workspace_size(2, 120000, 256) == 2 * 3750 * 34816
+    assert taa.attn_prefill_paged_expanded_workspace_size(3, 33, 256) == 3 * 2 * 34816
+    assert taa.attn_prefill_paged_expanded_workspace_size(1, 1, 256) == 34816
+    assert taa.attn_prefill_paged_expanded_workspace_size(2, 0, 256) == 0
+    assert taa.attn_prefill_paged_expanded_workspace_size(2, 100, 128) == 0
 
 
 def _prc(**kw):

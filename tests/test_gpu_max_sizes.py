@@ -1,7 +1,8 @@
 """The largest shapes of each entry point against the fp64 oracle.
 
 - the paged prefill with the whole 131072-token history live (every block
-  full, no partial tile) at the target shape, sampled query tokens x all heads;
+  full, no partial tile) at the target shape, sampled query tokens x all heads,
+  and through the expanded-history workspace (bit for bit the same);
 - decode over a 32768-key cache (512 chunks per sequence) at head_dim 256 and
   512, and a 4096-key window at the end of it;
 - an encoder launch of 4096 workgroups (B 64, H 16, S 512), sampled batches.
@@ -36,6 +37,10 @@ def test_prefill_whole_history_live(gpu_lib):
     ref = oracle.prefill_paged(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale, case.block_table,
                                case.L_act, case.scale, rows)
     assert_close(out[:, rows.to(DEV)], ref, "prefill whole history")
+    exp = gpu_lib.attn_prefill_paged_expanded(d(case.q), d(case.k_cache), d(case.v_cache), case.k_scale,
+                                              case.v_scale, d(case.block_table), case.L_act, case.scale, case.G)
+    torch.cuda.synchronize()
+    assert torch.equal(exp, out), "expanded history differs from the direct path"
 
 
 @pytest.mark.parametrize("D", [256, 512])

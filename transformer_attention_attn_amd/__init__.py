@@ -9,7 +9,8 @@ is raised.
 Entry points (same names as the C ABI in include/mi355attn.h):
   attn_encoder_fwd, attn_decode_gqa, attn_decode_gqa_workspace_size,
   attn_decode_gqa_window, attn_decode_gqa_window_workspace_size,
-  attn_prefill_paged, attn_prefill_paged_causal, res_ln, attn_status_string, attn_version.
+  attn_prefill_paged, attn_prefill_paged_expanded, attn_prefill_paged_expanded_workspace_size,
+  attn_prefill_paged_causal, res_ln, attn_status_string, attn_version.
 """
 from __future__ import annotations
 
@@ -85,6 +86,10 @@ def load(path: str | None = None):
     L.attn_decode_gqa_window.restype = I
     L.attn_prefill_paged.argtypes = [P, P, P, F, F, P, I, I, I, I, F, I, I, I, I, I, P, P, P]
     L.attn_prefill_paged.restype = I
+    L.attn_prefill_paged_expanded.argtypes = [P, P, P, F, F, P, I, I, I, I, F, I, I, I, I, I, P, P, P, Z, P]
+    L.attn_prefill_paged_expanded.restype = I
+    L.attn_prefill_paged_expanded_workspace_size.argtypes = [I, I, I]
+    L.attn_prefill_paged_expanded_workspace_size.restype = Z
     L.attn_prefill_paged_causal.argtypes = [P, P, P, F, F, P, I, I, I, I, P, P, F, I, I, I, I, I, P, P, P, Z, P]
     L.attn_prefill_paged_causal_workspace_size.argtypes = [I, I, I, I]
     L.attn_prefill_paged_causal_workspace_size.restype = Z
@@ -301,6 +306,38 @@ def attn_prefill_paged(q, k_cache, v_cache, k_scale: float, v_scale: float, bloc
                                    float(softmax_scale), int(num_kv_groups), Hq, Hkv, Lq, D, _ptr(out), _ptr(lse),
                                    _stream(stream))
     _check(rc, "attn_prefill_paged")
+    return (out, lse) if lse is not None else out
+
+
+def attn_prefill_paged_expanded_workspace_size(Hkv: int, actual_history_len: int, D: int) -> int:
+    return int(load().attn_prefill_paged_expanded_workspace_size(Hkv, actual_history_len, D))
+
+
+def attn_prefill_paged_expanded(q, k_cache, v_cache, k_scale: float, v_scale: float, block_table,
+                                actual_history_len: int, softmax_scale: float, num_kv_groups: int, *, out=None,
+                                lse=None, want_lse: bool = False, workspace=None, stream=None):
+    """attn_prefill_paged through a workspace of bf16 tile images of the live
+    history (allocated here when not given).  Same arguments and result."""
+    _need_cuda(q, k_cache, v_cache, block_table)
+    if block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32")
+    for t in (q, k_cache, v_cache, block_table):
+        if not t.is_contiguous():
+            raise ValueError("prefill tensors must be contiguous")
+    Hq, Lq, D = q.shape
+    nb, Hkv, bs, _ = k_cache.shape
+    if out is None:
+        out = torch.empty(Hq, Lq, D, dtype=torch.bfloat16, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty(Hq, Lq, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = attn_prefill_paged_expanded_workspace_size(Hkv, int(actual_history_len), D)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    rc = load().attn_prefill_paged_expanded(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale),
+                                            _ptr(block_table), block_table.numel(), nb, bs, int(actual_history_len),
+                                            float(softmax_scale), int(num_kv_groups), Hq, Hkv, Lq, D, _ptr(out),
+                                            _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "attn_prefill_paged_expanded")
     return (out, lse) if lse is not None else out
 
 

@@ -91,6 +91,7 @@ int decode_common(const void *q, const void *k, const void *v, const float *attn
 
 }  // namespace
 extern "C" size_t attn_prefill_paged_causal_workspace_size(int Hq, int Hkv, int Lq, int D);
+extern "C" size_t attn_prefill_paged_expanded_workspace_size(int Hkv, int actual_history_len, int D);
 namespace {
 
 // Bytes of the history -> current-token handoff's O part: the normalised
@@ -107,7 +108,7 @@ int prefill_common(const void *q, const void *k_cache, const void *v_cache, floa
                    const int32_t *block_table, int max_blocks, int num_blocks, int block_size, int actual_history_len,
                    const void *k_cur, const void *v_cur, float softmax_scale, int num_kv_groups, int Hq, int Hkv,
                    int Lq, int D, void *out, float *lse, void *workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+                   void *img_ws, size_t img_bytes, hipStream_t stream) {
   const bool cur = k_cur != nullptr;
   if (!q || !k_cache || !v_cache || !block_table || !out) return ATTN_ERR_INVALID_ARG;
   if (max_blocks <= 0 || num_blocks <= 0 || block_size <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || D <= 0 ||
@@ -126,6 +127,10 @@ int prefill_common(const void *q, const void *k_cache, const void *v_cache, floa
     if (!workspace || workspace_bytes < attn_prefill_paged_causal_workspace_size(Hq, Hkv, Lq, D))
       return ATTN_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_INVALID_ARG;
+  }
+  if (img_ws) {
+    if (img_bytes < attn_prefill_paged_expanded_workspace_size(Hkv, actual_history_len, D)) return ATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(img_ws) & 255u) != 0) return ATTN_ERR_INVALID_ARG;
   }
   if (((int64_t)num_blocks * Hkv * block_size * D) > ((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)num_kv_groups * Lq > 0x7fffffffLL - 256) return ATTN_ERR_UNSUPPORTED;
@@ -157,6 +162,10 @@ int prefill_common(const void *q, const void *k_cache, const void *v_cache, floa
     L.ws_o = static_cast<float *>(workspace);
     L.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + prefill_handoff_o_bytes(Hq, Hkv, Lq, D));
   }
+  if (img_ws) {
+    L.img = static_cast<char *>(img_ws);
+    L.n_tiles = (actual_history_len + prefill_key_tile() - 1) / prefill_key_tile();
+  }
   L.out = static_cast<__bf16 *>(out);
   L.lse = lse;
   return hip_status(launch_prefill(L, stream));
@@ -177,7 +186,7 @@ const char *attn_status_string(int status) {
   }
 }
 
-int attn_version(void) { return 10100; }
+int attn_version(void) { return 10200; }
 
 size_t attn_encoder_rope_workspace_size(int B, int H, int S_kv, int D, attn_dtype_t in_dtype) {
   if (B <= 0 || H <= 0 || S_kv <= 0 || D <= 0) return 0;
@@ -344,7 +353,24 @@ int attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache, 
                        int D, void *out, float *lse, hipStream_t stream) {
   return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
                         actual_history_len, nullptr, nullptr, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out, lse,
-                        nullptr, 0, stream);
+                        nullptr, 0, nullptr, 0, stream);
+}
+
+size_t attn_prefill_paged_expanded_workspace_size(int Hkv, int actual_history_len, int D) {
+  if (Hkv <= 0 || actual_history_len <= 0 || D != 256) return 0;
+  const int64_t tiles = (actual_history_len + prefill_key_tile() - 1) / prefill_key_tile();
+  return (size_t)((int64_t)Hkv * tiles * prefill_tile_image_bytes());
+}
+
+int attn_prefill_paged_expanded(const void *q, const void *k_cache, const void *v_cache, float k_scale,
+                                float v_scale, const int32_t *block_table, int max_blocks, int num_blocks,
+                                int block_size, int actual_history_len, float softmax_scale, int num_kv_groups,
+                                int Hq, int Hkv, int Lq, int D, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace) return ATTN_ERR_WORKSPACE;
+  return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
+                        actual_history_len, nullptr, nullptr, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out, lse,
+                        nullptr, 0, workspace, workspace_bytes, stream);
 }
 
 size_t attn_prefill_paged_causal_workspace_size(int Hq, int Hkv, int Lq, int D) {
@@ -360,7 +386,7 @@ int attn_prefill_paged_causal(const void *q, const void *k_cache, const void *v_
   if (!k_cur || !v_cur) return ATTN_ERR_INVALID_ARG;
   return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
                         actual_history_len, k_cur, v_cur, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out, lse,
-                        workspace, workspace_bytes, stream);
+                        workspace, workspace_bytes, nullptr, 0, stream);
 }
 
 int res_ln(const float *residual, const void *x, attn_dtype_t x_dtype, const float *gamma, const float *beta,

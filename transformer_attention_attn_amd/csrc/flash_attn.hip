@@ -74,7 +74,7 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 
 template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int OCC_, bool VFIRST_ = false, int QL_ = 0,
-          bool PVPRIO_ = false>
+          bool PVPRIO_ = false, bool DMA_ = false>
 struct Geo {
   static constexpr int D = D_, BN = BN_, NT = NT_, RG = RG_, NSPLIT = NSPLIT_;
   static constexpr int GRP = GRP_;  // LDS fragments read ahead of the MFMAs that use them
@@ -91,7 +91,17 @@ struct Geo {
   // transposing read touches start in 4 different 64-byte bank groups.
   static constexpr int KROW = D * 2 + 16;
   static constexpr int VSH = (D * 2) % 256 == 0 ? 0 : 1;
-  static constexpr int KTILE = BN * KROW;
+  // DMA: tiles arrive as ready-made bf16 images copied global -> LDS by
+  // direct loads (1 KB per wave instruction, no registers, no conversion).
+  // A direct load cannot pad inside its 1 KB, so K is chunk-major instead of
+  // padded: the 16-byte chunk c (d = 8c .. 8c+7) of key k sits at
+  // c*BN*16 + k*16, which keeps the 32 keys one fragment read touches in 512
+  // contiguous bytes.  V keeps the padded row layout (its image carries the
+  // pads).  Three buffers per operand let a tile's copy run two iterations
+  // ahead of its use.
+  static constexpr bool DMA = DMA_;
+  static constexpr int NBUF = DMA ? 3 : 2;
+  static constexpr int KTILE = DMA ? BN * D * 2 : BN * KROW;
   static constexpr int VTILE = BN * D * 2 + (BN >> VSH) * 64;
   static constexpr int KSLOT = NSPLIT * KTILE;                    // one K buffer: every split's tile
   static constexpr int VSLOT = NSPLIT * VTILE + NSPLIT * BN * 4;  // one V buffer, then the tiles' staged key mask
@@ -111,16 +121,25 @@ struct Geo {
   // wave's softmax VALU, and the matrix pipe idles less (prefill ~1% faster;
   // the VALU-bound encoder gains nothing).
   static constexpr bool PVPRIO = PVPRIO_;
-  static constexpr int QOFF = 2 * (KSLOT + VSLOT) > MERGE ? 2 * (KSLOT + VSLOT) : MERGE;
+  static constexpr int QOFF = NBUF * (KSLOT + VSLOT) > MERGE ? NBUF * (KSLOT + VSLOT) : MERGE;
   static constexpr int LDS = QOFF + QL * NT * THREADS * 16;  // K/V double buffers (or merge space), Q slots
   // softmax VALU instructions issued between consecutive QK MFMA groups
   static constexpr int VPM = (NT * (7 * BN / 4 + 8) + NFQ - 1) / NFQ;
   static_assert(D % 64 == 0 && BN % 32 == 0 && (VSH == 0 || D == 64), "tile shape");
   static_assert(QL >= 0 && QL <= SD, "Q fragments in LDS");
+  static_assert(!DMA || (NSPLIT == 1 && VSH == 0 && KTILE % 1024 == 0 && VTILE % 1024 == 0),
+                "tile images: one key split, one pad per V row, 1 KB pieces");
   static_assert(LDS <= 160 * 1024, "LDS budget (gfx950: 160 KiB per workgroup)");
 
-  static __device__ __forceinline__ int k_row(int key) { return key * KROW; }
+  static __device__ __forceinline__ int k_row(int key) { static_assert(!DMA, "padded K rows"); return key * KROW; }
+  // byte offset of this lane's first QK fragment (key lane%32, chunk lane/32)
+  // and of fragment (32-key block kb, k-step sd) relative to it
+  static __device__ __forceinline__ int k_lane(int lane) {
+    return DMA ? (lane & 31) * 16 + (lane >> 5) * BN * 16 : (lane & 31) * KROW + 16 * (lane >> 5);
+  }
+  static constexpr int k_frag(int kb, int sd) { return DMA ? kb * 512 + sd * 2 * BN * 16 : kb * 32 * KROW + 32 * sd; }
   static __device__ __forceinline__ int v_row(int key) { return key * (D * 2) + (key >> VSH) * 64; }
+  static constexpr int v_row_bytes() { static_assert(VSH == 0, "one pad per row"); return D * 2 + 64; }
 };
 
 // ------------------------------------------------------------------ sources
@@ -348,6 +367,70 @@ struct PagedSrc {
   }
 };
 
+// Wait until at most N of this wave's vector memory operations are in flight
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Tile images of a KV head's history (G::DMA): tile t holds the K image
+// (chunk-major, G::KTILE bytes) then the V image (padded rows, G::VTILE
+// bytes), each exactly as the key loop's LDS buffers hold them, so a tile is
+// copied global -> LDS by direct buffer loads: 1 KB per wave instruction,
+// lane L's 16 bytes at LDS base + 16 L.  Wave w issues pieces w, w + WAVES,
+// ...  A tile at or past n_tiles gets an empty range and reads as zeros
+// (the range check alone decides: the piece offset is an SGPR, the lane
+// offset a VGPR inside the piece).
+template <class G>
+struct TileImgSrc {
+  static constexpr int TIMG = G::KTILE + G::VTILE;
+  static constexpr int KP = G::KTILE / 1024, VP = G::VTILE / 1024;  // 1 KB pieces
+  const char *img;  // this KV head's first tile
+  int n_tiles, n_keys;
+  // pieces one wave issues per tile step (for its memory-counter waits)
+  static constexpr int pieces(int wave) {
+    return (KP + G::WAVES - 1 - wave) / G::WAVES + (VP + G::WAVES - 1 - wave) / G::WAVES;
+  }
+  static constexpr int PMAX = pieces(0), PMIN = pieces(G::WAVES - 1);
+  static_assert(PMAX - PMIN <= 2, "wait_step covers three counts");
+  // wait until at most this wave's pieces of one tile step are in flight
+  static __device__ __forceinline__ void wait_step(int wave) {
+    const int pw = pieces(wave);
+    if (pw == PMAX) wait_vm<PMAX>();
+    else if (pw == PMAX - 1) wait_vm<(PMAX - 1 >= 0 ? PMAX - 1 : 0)>();
+    else wait_vm<(PMAX - 2 >= 0 ? PMAX - 2 : 0)>();
+  }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile(int t) const {
+    return make_rsrc(img + (int64_t)(t < n_tiles ? t : 0) * TIMG, t < n_tiles ? (uint32_t)TIMG : 0u);
+  }
+  static __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t r, char *dst, int first, int n, int wave,
+                                              int lane) {
+#pragma unroll
+    for (int j = 0; j < (n + G::WAVES - 1) / G::WAVES; ++j) {
+      const int piece = wave + j * G::WAVES;
+      if ((j + 1) * G::WAVES <= n || piece < n)  // the test folds away for whole rounds of pieces
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + piece * 1024), 16,
+                                                 lane * 16, first + piece * 1024, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void copy_k(char *dst, int t, int wave, int lane) const {
+    copy(tile(t), dst, 0, KP, wave, lane);
+  }
+  __device__ __forceinline__ void copy_v(char *dst, int t, int wave, int lane) const {
+    copy(tile(t), dst, G::KTILE, VP, wave, lane);
+  }
+};
+
+// Workgroup barrier without a memory fence: finishes this wave's LDS
+// operations and meets the other waves.  A __syncthreads() here would also
+// wait for the tile copies still in flight (a direct load counts as an LDS
+// store), which must keep running across the barrier; their completion is
+// waited for explicitly (wait_vm) before the barrier that publishes them.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ------------------------------------------------------------------ per-tile pieces
 
 template <class G>
@@ -387,13 +470,10 @@ __device__ __forceinline__ void q_to_lds(const u32x4_t (&qf)[G::NT][G::SD], char
 template <class G>
 __device__ __forceinline__ void qk_tile(f32x16_t (&s)[G::NT][G::KB], const u32x4_t (&qf)[G::NT][G::SD],
                                         const char *qa, const char *kt, int lane) {
-  const char *base = kt + (lane & 31) * G::KROW + 16 * (lane >> 5);
+  const char *base = kt + G::k_lane(lane);
   u32x4_t fb[G::NFQ];
 #pragma unroll
-  for (int f = 0; f < G::NFQ; ++f) {
-    const int kb = f % G::KB, sd = f / G::KB;
-    fb[f] = *reinterpret_cast<const u32x4_t *>(base + kb * 32 * G::KROW + 32 * sd);
-  }
+  for (int f = 0; f < G::NFQ; ++f) fb[f] = *reinterpret_cast<const u32x4_t *>(base + G::k_frag(f % G::KB, f / G::KB));
 #pragma unroll
   for (int f = 0; f < G::NFQ; ++f) {
     const int kb = f % G::KB, sd = f / G::KB;
@@ -556,7 +636,7 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
   constexpr int SPA = SLOTS >= NP && NP > 1 ? (SLOTS - 1) / (NP - 1) : 0;
   static_assert(SLOTS >= 1, "QK slots");
   const int h = lane >> 5;
-  const char *kbase = kt + (lane & 31) * G::KROW + 16 * h;
+  const char *kbase = kt + G::k_lane(lane);
 
   u32x4_t fb[G::NFQ];
   u32x4_t ql[G::QL > 0 ? G::QL : 1][G::NT];
@@ -571,7 +651,7 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
     for (int nt = 0; nt < G::NT; ++nt) ql[sd][nt] = q_lds<G>(qa, nt, sd);
 #pragma unroll
   for (int f = 0; f < RA; ++f)
-    fb[f] = *reinterpret_cast<const u32x4_t *>(kbase + (f % G::KB) * 32 * G::KROW + 32 * (f / G::KB));
+    fb[f] = *reinterpret_cast<const u32x4_t *>(kbase + G::k_frag(f % G::KB, f / G::KB));
   if constexpr (HAS_MASK) {
 #pragma unroll
     for (int kb = 0; kb < G::KB; ++kb)
@@ -591,7 +671,7 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
     }
     if (f + RA < G::NFQ) {
       const int g = f + RA;
-      fb[g] = *reinterpret_cast<const u32x4_t *>(kbase + (g % G::KB) * 32 * G::KROW + 32 * (g / G::KB));
+      fb[g] = *reinterpret_cast<const u32x4_t *>(kbase + G::k_frag(g % G::KB, g / G::KB));
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -830,6 +910,101 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
     step(it, s, s2);
     step(it + 1, s2, s);
   }
+}
+
+// The key loop over tile images (G::DMA, one key split).  Three K buffers
+// (kA, kB, kC) and three V buffers: at step `it` they hold K(it), K(it+1),
+// K(it+2) and V(it), V(it+1), V(it+2) in an order that rotates with it % 3.
+// Phase A reads K(it+1), phase B reads V(it), and the step copies K(it+3)
+// into K(it)'s buffer and V(it+2) into V(it-1)'s, both released by the
+// barrier that ended the step before.  Before its closing barrier a step
+// waits for the copies of the step before (K(it+2), V(it+1), which the next
+// step reads) and leaves its own in flight, so every copy has a full step
+// to land.  The buffers are __restrict__ parameters and every step names
+// its four by role (the loop runs six steps per pass: three rotations times
+// the S / SN alternation), so the compiler can tell that a copy in flight
+// never aliases the LDS reads that follow it; otherwise it would wait for
+// every copy before each LDS read.  Same phases, schedule and masks as
+// flash_loop.
+template <class G, class Mask>
+__device__ __forceinline__ void dma_loop_body(WaveState<G> &ws, const TileImgSrc<G> &src,
+                                              const u32x4_t (&qf)[G::NT][G::SD], char *__restrict__ kA,
+                                              char *__restrict__ kB, char *__restrict__ kC, char *__restrict__ vA,
+                                              char *__restrict__ vB, char *__restrict__ vC,
+                                              const char *__restrict__ qa, float c, const Mask &mk, int lane,
+                                              int wave, int n_iter) {
+  src.copy_k(kA, 0, wave, lane);
+  src.copy_v(vA, 0, wave, lane);
+  src.copy_k(kB, 1, wave, lane);
+  src.copy_v(vB, 1, wave, lane);
+  src.copy_k(kC, 2, wave, lane);
+  wait_vm<0>();
+  lds_barrier();
+
+  f32x16_t s[G::NT][G::KB], s2[G::NT][G::KB];
+  qk_tile<G>(s, qf, qa, kA, lane);
+  mk.template apply<G>(s, 0, lane);
+  lds_barrier();  // K(0) read by every wave before K(3) replaces it
+
+  // kr: K(it+1), read; kw: K(it)'s buffer, receives K(it+3); vr: V(it), read;
+  // vw: V(it-1)'s buffer, receives V(it+2)
+  auto step = [&](int it, char *__restrict__ kr, char *__restrict__ kw, char *__restrict__ vr,
+                  char *__restrict__ vw, f32x16_t (&S)[G::NT][G::KB], f32x16_t (&SN)[G::NT][G::KB]) {
+    PCarry<G> pc;
+    float alpha[G::NT];
+    const bool any = phase_a<G, false>(ws, pc, SN, S, alpha, qf, qa, kr, nullptr, c, lane);
+    if (any) {
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] *= alpha[nt];
+    }
+    phase_b<G, false>(ws, pc, S, c, vr, lane, [&](int k) {
+      if (k == 0) src.copy_k(kw, it + 3, wave, lane);
+      if (k == 1) src.copy_v(vw, it + 2, wave, lane);
+    });
+    TileImgSrc<G>::wait_step(wave);  // the step before's copies have landed
+    lds_barrier();
+    mk.template apply<G>(SN, (it + 1) * G::BN, lane);
+  };
+  for (int it = 0; it < n_iter; it += 6) {
+    step(it, kB, kA, vA, vC, s, s2);
+    if (it + 1 >= n_iter) break;
+    step(it + 1, kC, kB, vB, vA, s2, s);
+    if (it + 2 >= n_iter) break;
+    step(it + 2, kA, kC, vC, vB, s, s2);
+    if (it + 3 >= n_iter) break;
+    step(it + 3, kB, kA, vA, vC, s2, s);
+    if (it + 4 >= n_iter) break;
+    step(it + 4, kC, kB, vB, vA, s, s2);
+    if (it + 5 >= n_iter) break;
+    step(it + 5, kA, kC, vC, vB, s2, s);
+  }
+  wait_vm<0>();  // no copy may still be writing into LDS the epilogue reuses
+  lds_barrier();
+}
+
+template <class G, class Mask>
+__device__ __forceinline__ void flash_loop_dma(WaveState<G> &ws, const TileImgSrc<G> &src,
+                                               const u32x4_t (&qf)[G::NT][G::SD], char *smem, float c, const Mask &mk,
+                                               bool fresh, unsigned tid) {
+  static_assert(G::DMA && G::NSPLIT == 1, "tile images: one key split");
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const int n_iter = (src.n_keys + G::BN - 1) / G::BN;
+  if (fresh) {
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) {
+      ws.m[nt] = -INFINITY;
+      ws.l[nt] = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] = f32x16_t{};
+    }
+  }
+  if (n_iter <= 0) return;
+  char *const vbuf = smem + 3 * G::KSLOT;
+  dma_loop_body<G>(ws, src, qf, smem, smem + G::KSLOT, smem + 2 * G::KSLOT, vbuf, vbuf + G::VSLOT,
+                   vbuf + 2 * G::VSLOT, smem + G::QOFF + tid * 16, c, mk, lane, wave, n_iter);
 }
 
 // Merge the NSPLIT key-split partial states into the split-0 waves (LDS).
@@ -1082,18 +1257,25 @@ void prefill_paged_kernel(PrefillLaunch a) {
           r < rows ? ldg<u32x4_t>(a.q + (row_base + r) * G::D + 16 * sd + 8 * hh) : u32x4_t{0, 0, 0, 0}, qsign);
   }
 
-  PagedSrc<G> src;
-  src.kc = a.kc;
-  src.vc = a.vc;
-  src.bt = (const __attribute__((address_space(4))) int32_t *)(a.bt);
-  src.head_off = (int64_t)kvh * a.bs * G::D;
-  src.blk_stride = (int64_t)a.Hkv * a.bs * G::D;
-  src.bs = a.bs;
-  src.n_keys = a.L_act;
-
   q_to_lds<G>(qf, smem, threadIdx.x);
   WaveState<G> ws;
-  flash_loop<G, false>(ws, src, qf, smem, a.c, TailMask{a.L_act}, true, threadIdx.x);
+  if constexpr (G::DMA) {
+    TileImgSrc<G> src;
+    src.img = a.img + (int64_t)kvh * a.n_tiles * TileImgSrc<G>::TIMG;
+    src.n_tiles = a.n_tiles;
+    src.n_keys = a.L_act;
+    flash_loop_dma<G>(ws, src, qf, smem, a.c, TailMask{a.L_act}, true, threadIdx.x);
+  } else {
+    PagedSrc<G> src;
+    src.kc = a.kc;
+    src.vc = a.vc;
+    src.bt = (const __attribute__((address_space(4))) int32_t *)(a.bt);
+    src.head_off = (int64_t)kvh * a.bs * G::D;
+    src.blk_stride = (int64_t)a.Hkv * a.bs * G::D;
+    src.bs = a.bs;
+    src.n_keys = a.L_act;
+    flash_loop<G, false>(ws, src, qf, smem, a.c, TailMask{a.L_act}, true, threadIdx.x);
+  }
 
   prefill_epilogue<G, HANDOFF>(ws, a, rt, kvh, rg, lane, a.v_scale);
 }
@@ -1187,12 +1369,44 @@ void prefill_current_kernel(PrefillLaunch a) {
   prefill_epilogue<G, false>(ws, a, rt, kvh, rg, lane, 1.0f);
 }
 
+// ------------------------------------------------------------------ tile images
+
+// Expand the live history of the paged FP8 cache into the bf16 tile images
+// the DMA key loop copies (TileImgSrc): one workgroup per (tile, KV head).
+// e4m3fn -> bf16 is exact; keys at or past L_act and the V row pads are
+// written as zeros.  K reads run along each key row (coalesced) and write
+// chunk-major; V rows are read and written in order.
+template <class G>
+__global__ __launch_bounds__(256) void prefill_tile_images_kernel(PrefillLaunch a) {
+  constexpr int CH = G::D / 8;                  // 16-byte bf16 chunks per key
+  constexpr int VROW = G::v_row_bytes();        // padded V row
+  constexpr int VCH = VROW / 16;
+  const int t = blockIdx.x, kvh = blockIdx.y;
+  char *const img = a.img + ((int64_t)kvh * a.n_tiles + t) * TileImgSrc<G>::TIMG;
+  auto src8 = [&](const uint8_t *cache, int key, int c) -> u32x4_t {
+    const int32_t phys = a.bt[key / a.bs];
+    const uint8_t *p = cache + (((int64_t)phys * a.Hkv + kvh) * a.bs + key % a.bs) * G::D + c * 8;
+    return PagedSrc<G>::cvt8(*reinterpret_cast<const u32x2_t *>(p));
+  };
+  for (int i = threadIdx.x; i < G::BN * CH; i += 256) {
+    const int k = i / CH, c = i % CH, key = t * G::BN + k;
+    const u32x4_t x = key < a.L_act ? src8(a.kc, key, c) : u32x4_t{0, 0, 0, 0};
+    *reinterpret_cast<u32x4_t *>(img + c * (G::BN * 16) + k * 16) = x;
+  }
+  for (int i = threadIdx.x; i < G::BN * VCH; i += 256) {
+    const int k = i / VCH, c = i % VCH, key = t * G::BN + k;
+    const u32x4_t x = c < CH && key < a.L_act ? src8(a.vc, key, c) : u32x4_t{0, 0, 0, 0};
+    *reinterpret_cast<u32x4_t *>(img + G::KTILE + k * VROW + c * 16) = x;
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 
 using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true>;      // BM 128, 8 waves: 4 row groups x 2 key splits, 32-key tiles, 4 waves/SIMD
 using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: mask values held in registers, 2 waves/SIMD
 using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: twice the staging registers per tile
 using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 3, true>;  // BM 256, 8 waves of 32 rows, 2 waves per SIMD, 3 Q fragments in LDS, PV priority
+using PrefImgGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 1, true, true>;  // the same over bf16 tile images copied by DMA (1 Q fragment in LDS: no staging registers)
 
 // Launch with G::LDS bytes of dynamic LDS; kernels above 64 KiB are opted in
 // once per process (hipFuncSetAttribute is per function, not per device).
@@ -1233,9 +1447,18 @@ hipError_t launch_encoder(const EncoderLaunch &a, bool f32_in, hipStream_t strea
 
 int encoder_rows_per_block() { return EncGeo::BM; }
 
+int64_t prefill_tile_image_bytes() { return TileImgSrc<PrefImgGeo>::TIMG; }
+
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream) {
   const int rows = a.G * a.Lq;
   const int n_rt = (rows + PrefGeo::BM - 1) / PrefGeo::BM;
+  static_assert(PrefImgGeo::BM == PrefGeo::BM && PrefImgGeo::BN == PrefGeo::BN, "same tiles");
+  if (!a.kcur && a.img) {
+    hipLaunchKernelGGL(prefill_tile_images_kernel<PrefImgGeo>, dim3(a.n_tiles, a.Hkv), dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_lds<PrefImgGeo>(prefill_paged_kernel<PrefImgGeo, false>, dim3(n_rt * a.Hkv), a, stream);
+  }
   if (!a.kcur) return launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo, false>, dim3(n_rt * a.Hkv), a, stream);
   if (a.L_act > 0) {
     const hipError_t e = launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo, true>, dim3(n_rt * a.Hkv), a, stream);

@@ -48,6 +48,8 @@ struct PrefillLaunch {
   const __bf16 *kcur, *vcur;  // nullable: current tokens' K/V [Hkv, Lq, D] (causal part)
   float c_cur;                // |softmax_scale| * log2(e), > 0
   float *ws_o, *ws_ml;        // history -> current-token handoff (causal part with a history)
+  char *img;                  // nullable: bf16 tile images of the history [Hkv, n_tiles, image] (workspace)
+  int n_tiles;                // tiles of prefill_key_tile() keys per KV head in img
   __bf16 *out;
   float *lse;     // nullable
 };
@@ -82,6 +84,7 @@ int encoder_rows_per_block();
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream);
 int prefill_key_tile();
 int prefill_rows_per_block();
+int64_t prefill_tile_image_bytes();  // bytes of one tile's K and V images
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
 int decode_chunk_keys();
 int decode_max_groups();
