@@ -145,7 +145,8 @@ def time_next_workloads(taa, dev, flush, pre_dev, reps: int = 20):
     the decode at head_dim 512 (global layers) and over a 1024-key sliding
     window at head_dim 256, each call timed alone after the cache flush; and
     the paged prefill with causal attention among the 4096 current tokens
-    (the history inputs of the step, already on the device)."""
+    (the history inputs of the step, already on the device; history through
+    its tile images), and the step's prefill without a workspace."""
     out = {}
 
     def timed_flushed(fn):
@@ -256,10 +257,11 @@ def time_next_workloads(taa, dev, flush, pre_dev, reps: int = 20):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    pws = torch.empty(taa.attn_prefill_paged_causal_workspace_size(pre.Hq, pre.Hkv, pre.Lq, pre.D),
-                      dtype=torch.uint8, device=dev)
-    ms = timed_b2b(lambda: taa.attn_prefill_paged_causal(p_q, p_k, p_v, pre.k_scale, pre.v_scale, p_bt, pre.L_act,
-                                                         kc, vc, pre.scale, pre.G, out=o, workspace=pws), r3)
+    pws = torch.empty(taa.attn_prefill_paged_causal_expanded_workspace_size(pre.Hq, pre.Hkv, pre.Lq, pre.L_act,
+                                                                            pre.D), dtype=torch.uint8, device=dev)
+    ms = timed_b2b(lambda: taa.attn_prefill_paged_causal_expanded(p_q, p_k, p_v, pre.k_scale, pre.v_scale, p_bt,
+                                                                  pre.L_act, kc, vc, pre.scale, pre.G, out=o,
+                                                                  workspace=pws), r3)
     f_hist = acc.prefill_flops(pre.Lq, pre.Hq, pre.L_act, pre.D)
     f_cur = acc.causal_flops(pre.Lq, pre.Hq, pre.D)
     tf = (f_hist + f_cur) / (ms * 1e-3) / 1e12

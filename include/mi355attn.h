@@ -286,6 +286,29 @@ ATTN_API int attn_prefill_paged_causal(const void *q, const void *k_cache, const
                               float softmax_scale, int num_kv_groups, int Hq, int Hkv, int Lq, int D,
                               void *out, float *lse, void *workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/*
+ * attn_prefill_paged_causal with the history taken through expanded bf16
+ * tile images, as attn_prefill_paged_expanded does for the history-only
+ * prefill: the same operation, arguments, requirements and result.
+ *
+ * Follows: the passages of attn_prefill_paged_causal and of
+ * attn_prefill_paged_expanded.
+ *   workspace: at least attn_prefill_paged_causal_expanded_workspace_size(Hq,
+ *   Hkv, Lq, actual_history_len, D) bytes, 256-byte aligned, owned by the
+ *   caller: the hand-off state of attn_prefill_paged_causal (rounded up to 256
+ *   bytes), then the tile images (none for an empty history).  Contents on
+ *   entry ignored.  Missing or too small: ATTN_ERR_WORKSPACE.  The size
+ *   function returns 0 for invalid or unsupported arguments.
+ */
+ATTN_API size_t attn_prefill_paged_causal_expanded_workspace_size(int Hq, int Hkv, int Lq, int actual_history_len,
+                                                                  int D);
+ATTN_API int attn_prefill_paged_causal_expanded(const void *q, const void *k_cache, const void *v_cache,
+                                       float k_scale, float v_scale, const int32_t *block_table, int max_blocks,
+                                       int num_blocks, int block_size, int actual_history_len, const void *k_cur,
+                                       const void *v_cur, float softmax_scale, int num_kv_groups, int Hq, int Hkv,
+                                       int Lq, int D, void *out, float *lse, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
 ATTN_API size_t attn_prefill_paged_causal_workspace_size(int Hq, int Hkv, int Lq, int D);
 
 /*

@@ -35,6 +35,7 @@ def test_header_declares_the_four_entry_points():
               "attn_decode_gqa_workspace_size", "attn_decode_gqa_window", "attn_decode_gqa_window_workspace_size",
               "attn_prefill_paged_causal", "attn_prefill_paged_causal_workspace_size",
               "attn_prefill_paged_expanded", "attn_prefill_paged_expanded_workspace_size",
+              "attn_prefill_paged_causal_expanded", "attn_prefill_paged_causal_expanded_workspace_size",
               "attn_encoder_rope_workspace_size", "attn_status_string", "attn_version"):
         assert n in names
 
@@ -228,6 +229,18 @@ def _pex(**kw):
 ])
 def test_prefill_expanded_validation(lib, kw, expect):
     assert lib.attn_prefill_paged_expanded(*_pex(**kw)) == expect
+
+
+def test_prefill_causal_expanded_workspace_size():
+    # the causal hand-off state (rounded up to 256 bytes), then the history's tile images
+    hand = 32 * 4096 * 256 * 4 + 32 * 4096 * 4
+    assert taa.attn_prefill_paged_causal_expanded_workspace_size(32, 2, 4096, 120000, 256) == hand + 2 * 3750 * 34816
+    hand = (6 * 100 * 256 * 4 + 6 * 100 * 4 + 255) // 256 * 256  # 616800 bytes, rounded up to 616960
+    assert hand == 616960
+    assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 33, 256) == hand + 2 * 2 * 34816
+    assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 0, 256) == hand  # no history
+    assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 4, 100, 33, 256) == 0
+    assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 33, 128) == 0
 
 
 def test_prefill_expanded_workspace_size():

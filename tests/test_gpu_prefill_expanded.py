@@ -101,3 +101,35 @@ def test_expanded_workspace_too_small_is_an_error(gpu_lib):
     ws = torch.empty(need - 1, dtype=torch.uint8, device=DEV)
     with pytest.raises(RuntimeError, match="WORKSPACE"):
         _both(taa, case, workspace=ws)
+
+
+@pytest.mark.parametrize("L", [700, 0])
+def test_causal_expanded_equals_causal(gpu_lib, L):
+    taa = gpu_lib
+    case = W.prefill_paged(180 + L, 8, 2, 300, 256, 6, 128, max(L, 1))
+    case.L_act = L
+    kc, vc = (t.to(DEV) for t in W.prefill_current_kv(181, 2, 300))
+    d = lambda t: t.to(DEV)
+    args = (d(case.q), d(case.k_cache), d(case.v_cache), case.k_scale, case.v_scale, d(case.block_table), L, kc, vc,
+            case.scale, case.G)
+    _say(f"[expanded] causal L_act={L}")
+    po, pl = taa.attn_prefill_paged_causal(*args, want_lse=True)
+    eo, el = taa.attn_prefill_paged_causal_expanded(*args, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(eo, po) and torch.equal(el, pl)
+    ref = oracle.prefill_causal(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale, case.block_table, L,
+                                kc.cpu(), vc.cpu(), case.scale, torch.arange(case.Lq))
+    assert_close(eo, ref, "causal expanded")
+
+
+def test_causal_expanded_workspace_too_small_is_an_error(gpu_lib):
+    taa = gpu_lib
+    case = W.prefill_paged(182, 4, 2, 16, 256, 4, 64, 200)
+    kc, vc = (t.to(DEV) for t in W.prefill_current_kv(183, 2, 16))
+    need = taa.attn_prefill_paged_causal_expanded_workspace_size(case.Hq, case.Hkv, case.Lq, case.L_act, case.D)
+    ws = torch.empty(need - 1, dtype=torch.uint8, device=DEV)
+    d = lambda t: t.to(DEV)
+    with pytest.raises(RuntimeError, match="WORKSPACE"):
+        taa.attn_prefill_paged_causal_expanded(d(case.q), d(case.k_cache), d(case.v_cache), case.k_scale,
+                                               case.v_scale, d(case.block_table), case.L_act, kc, vc, case.scale,
+                                               case.G, workspace=ws)

@@ -10,7 +10,7 @@ Entry points (same names as the C ABI in include/mi355attn.h):
   attn_encoder_fwd, attn_decode_gqa, attn_decode_gqa_workspace_size,
   attn_decode_gqa_window, attn_decode_gqa_window_workspace_size,
   attn_prefill_paged, attn_prefill_paged_expanded, attn_prefill_paged_expanded_workspace_size,
-  attn_prefill_paged_causal, res_ln, attn_status_string, attn_version.
+  attn_prefill_paged_causal, attn_prefill_paged_causal_expanded, res_ln, attn_status_string, attn_version.
 """
 from __future__ import annotations
 
@@ -91,6 +91,11 @@ def load(path: str | None = None):
     L.attn_prefill_paged_expanded_workspace_size.argtypes = [I, I, I]
     L.attn_prefill_paged_expanded_workspace_size.restype = Z
     L.attn_prefill_paged_causal.argtypes = [P, P, P, F, F, P, I, I, I, I, P, P, F, I, I, I, I, I, P, P, P, Z, P]
+    L.attn_prefill_paged_causal_expanded.argtypes = [P, P, P, F, F, P, I, I, I, I, P, P, F, I, I, I, I, I, P, P, P, Z,
+                                                     P]
+    L.attn_prefill_paged_causal_expanded.restype = I
+    L.attn_prefill_paged_causal_expanded_workspace_size.argtypes = [I, I, I, I, I]
+    L.attn_prefill_paged_causal_expanded_workspace_size.restype = Z
     L.attn_prefill_paged_causal_workspace_size.argtypes = [I, I, I, I]
     L.attn_prefill_paged_causal_workspace_size.restype = Z
     L.attn_prefill_paged_causal.restype = I
@@ -347,10 +352,12 @@ def attn_prefill_paged_causal_workspace_size(Hq: int, Hkv: int, Lq: int, D: int)
 
 def attn_prefill_paged_causal(q, k_cache, v_cache, k_scale: float, v_scale: float, block_table,
                               actual_history_len: int, k_cur, v_cur, softmax_scale: float, num_kv_groups: int, *,
-                              out=None, lse=None, want_lse: bool = False, workspace=None, stream=None):
+                              out=None, lse=None, want_lse: bool = False, workspace=None, stream=None,
+                              expanded: bool = False):
     """Paged history plus causal current-token GQA prefill: as
     attn_prefill_paged, plus the current tokens' K/V k_cur/v_cur [Hkv,Lq,D]
-    bf16.  Returns out [Hq,Lq,D] bf16 (and the joined lse)."""
+    bf16.  Returns out [Hq,Lq,D] bf16 (and the joined lse).  expanded=True
+    calls attn_prefill_paged_causal_expanded (history through tile images)."""
     _need_cuda(q, k_cache, v_cache, block_table, k_cur, v_cur)
     if block_table.dtype != torch.int32:
         raise ValueError("block_table must be int32")
@@ -368,15 +375,27 @@ def attn_prefill_paged_causal(q, k_cache, v_cache, k_scale: float, v_scale: floa
     if want_lse and lse is None:
         lse = torch.empty(Hq, Lq, dtype=torch.float32, device=q.device)
     if workspace is None:
-        need = attn_prefill_paged_causal_workspace_size(Hq, Hkv, Lq, D)
+        need = (attn_prefill_paged_causal_expanded_workspace_size(Hq, Hkv, Lq, int(actual_history_len), D)
+                if expanded else attn_prefill_paged_causal_workspace_size(Hq, Hkv, Lq, D))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    rc = load().attn_prefill_paged_causal(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale),
-                                          _ptr(block_table), block_table.numel(), nb, bs, int(actual_history_len),
-                                          _ptr(k_cur), _ptr(v_cur), float(softmax_scale), int(num_kv_groups), Hq,
-                                          Hkv, Lq, D, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
-                                          _stream(stream))
-    _check(rc, "attn_prefill_paged_causal")
+    fn = load().attn_prefill_paged_causal_expanded if expanded else load().attn_prefill_paged_causal
+    rc = fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), float(k_scale), float(v_scale), _ptr(block_table),
+            block_table.numel(), nb, bs, int(actual_history_len), _ptr(k_cur), _ptr(v_cur), float(softmax_scale),
+            int(num_kv_groups), Hq, Hkv, Lq, D, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+            _stream(stream))
+    _check(rc, "attn_prefill_paged_causal_expanded" if expanded else "attn_prefill_paged_causal")
     return (out, lse) if lse is not None else out
+
+
+def attn_prefill_paged_causal_expanded_workspace_size(Hq: int, Hkv: int, Lq: int, actual_history_len: int,
+                                                      D: int) -> int:
+    return int(load().attn_prefill_paged_causal_expanded_workspace_size(Hq, Hkv, Lq, actual_history_len, D))
+
+
+def attn_prefill_paged_causal_expanded(*args, **kw):
+    """attn_prefill_paged_causal with the history through expanded tile images
+    (C-ABI attn_prefill_paged_causal_expanded); same arguments and result."""
+    return attn_prefill_paged_causal(*args, expanded=True, **kw)
 
 
 def res_ln(residual, x=None, gamma=None, beta=None, eps: float = 1e-6, *, residual_out=None, y=None,

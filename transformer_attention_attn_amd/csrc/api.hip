@@ -92,6 +92,8 @@ int decode_common(const void *q, const void *k, const void *v, const float *attn
 }  // namespace
 extern "C" size_t attn_prefill_paged_causal_workspace_size(int Hq, int Hkv, int Lq, int D);
 extern "C" size_t attn_prefill_paged_expanded_workspace_size(int Hkv, int actual_history_len, int D);
+extern "C" size_t attn_prefill_paged_causal_expanded_workspace_size(int Hq, int Hkv, int Lq, int actual_history_len,
+                                                                      int D);
 namespace {
 
 // Bytes of the history -> current-token handoff's O part: the normalised
@@ -376,6 +378,37 @@ int attn_prefill_paged_expanded(const void *q, const void *k_cache, const void *
 size_t attn_prefill_paged_causal_workspace_size(int Hq, int Hkv, int Lq, int D) {
   if (Hq <= 0 || Hkv <= 0 || Lq <= 0 || D <= 0 || Hq % Hkv) return 0;
   return (size_t)prefill_handoff_o_bytes(Hq, Hkv, Lq, D) + (size_t)Hq * Lq * 4;
+}
+
+size_t attn_prefill_paged_causal_expanded_workspace_size(int Hq, int Hkv, int Lq, int actual_history_len, int D) {
+  const size_t hand = attn_prefill_paged_causal_workspace_size(Hq, Hkv, Lq, D);
+  if (hand == 0 || actual_history_len < 0) return 0;
+  const size_t img = actual_history_len > 0 ? attn_prefill_paged_expanded_workspace_size(Hkv, actual_history_len, D) : 0;
+  if (actual_history_len > 0 && img == 0) return 0;
+  return (hand + 255) / 256 * 256 + img;
+}
+
+int attn_prefill_paged_causal_expanded(const void *q, const void *k_cache, const void *v_cache, float k_scale,
+                                       float v_scale, const int32_t *block_table, int max_blocks, int num_blocks,
+                                       int block_size, int actual_history_len, const void *k_cur,
+                                       const void *v_cur, float softmax_scale, int num_kv_groups, int Hq, int Hkv,
+                                       int Lq, int D, void *out, float *lse, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  if (!k_cur || !v_cur) return ATTN_ERR_INVALID_ARG;
+  if (!workspace) return ATTN_ERR_WORKSPACE;
+  const size_t need = attn_prefill_paged_causal_expanded_workspace_size(Hq, Hkv, Lq, actual_history_len, D);
+  if (need == 0) {  // invalid or unsupported arguments: let the shared validation name them
+    return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
+                          actual_history_len, k_cur, v_cur, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out,
+                          lse, workspace, workspace_bytes, nullptr, 0, stream);
+  }
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  // hand-off state first, then the tile images (256-byte aligned)
+  const size_t hand = (attn_prefill_paged_causal_workspace_size(Hq, Hkv, Lq, D) + 255) / 256 * 256;
+  char *img = actual_history_len > 0 ? static_cast<char *>(workspace) + hand : nullptr;
+  return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
+                        actual_history_len, k_cur, v_cur, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out, lse,
+                        workspace, hand, img, workspace_bytes - hand, stream);
 }
 
 int attn_prefill_paged_causal(const void *q, const void *k_cache, const void *v_cache, float k_scale, float v_scale,

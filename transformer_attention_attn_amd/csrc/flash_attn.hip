@@ -1453,15 +1453,18 @@ hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream) {
   const int rows = a.G * a.Lq;
   const int n_rt = (rows + PrefGeo::BM - 1) / PrefGeo::BM;
   static_assert(PrefImgGeo::BM == PrefGeo::BM && PrefImgGeo::BN == PrefGeo::BN, "same tiles");
-  if (!a.kcur && a.img) {
+  const dim3 grid(n_rt * a.Hkv);
+  if (a.img && a.L_act > 0) {  // the history through its tile images
     hipLaunchKernelGGL(prefill_tile_images_kernel<PrefImgGeo>, dim3(a.n_tiles, a.Hkv), dim3(256), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_lds<PrefImgGeo>(prefill_paged_kernel<PrefImgGeo, false>, dim3(n_rt * a.Hkv), a, stream);
-  }
-  if (!a.kcur) return launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo, false>, dim3(n_rt * a.Hkv), a, stream);
-  if (a.L_act > 0) {
-    const hipError_t e = launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo, true>, dim3(n_rt * a.Hkv), a, stream);
+    if (!a.kcur) return launch_lds<PrefImgGeo>(prefill_paged_kernel<PrefImgGeo, false>, grid, a, stream);
+    const hipError_t e2 = launch_lds<PrefImgGeo>(prefill_paged_kernel<PrefImgGeo, true>, grid, a, stream);
+    if (e2 != hipSuccess) return e2;
+  } else if (!a.kcur) {
+    return launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo, false>, grid, a, stream);
+  } else if (a.L_act > 0) {
+    const hipError_t e = launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo, true>, grid, a, stream);
     if (e != hipSuccess) return e;
   }
   return launch_lds<PrefGeo>(prefill_current_kernel<PrefGeo>, dim3(n_rt * a.Hkv), a, stream);
