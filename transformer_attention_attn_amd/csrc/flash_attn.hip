@@ -457,14 +457,38 @@ template <class G>
 __device__ __forceinline__ u32x4_t q_lds(const char *qa, int nt, int sd) {
   return *reinterpret_cast<const u32x4_t *>(qa + (sd * G::NT + nt) * G::THREADS * 16);
 }
-// Store the LDS-resident Q fragments of this thread (before the key loop).
+// Store the LDS-resident Q fragments of this thread into its slots (qa, as
+// q_lds reads them; only this thread reads them back, so no barrier).
 template <class G>
-__device__ __forceinline__ void q_to_lds(const u32x4_t (&qf)[G::NT][G::SD], char *smem, unsigned tid) {
+__device__ __forceinline__ void q_to_lds(const u32x4_t (&qf)[G::NT][G::SD], char *qa) {
 #pragma unroll
   for (int sd = 0; sd < G::QL; ++sd)
 #pragma unroll
     for (int nt = 0; nt < G::NT; ++nt)
-      *reinterpret_cast<u32x4_t *>(smem + G::QOFF + ((sd * G::NT + nt) * G::THREADS + tid) * 16) = qf[nt][sd];
+      *reinterpret_cast<u32x4_t *>(qa + (sd * G::NT + nt) * G::THREADS * 16) = qf[nt][sd];
+}
+
+// A negative softmax scale is applied as a positive one on -q (exact), so the
+// kernels only ever see c > 0.
+__device__ __forceinline__ u32x4_t neg_bf16x8(u32x4_t x, uint32_t sign) {
+  return u32x4_t{x[0] ^ sign, x[1] ^ sign, x[2] ^ sign, x[3] ^ sign};
+}
+
+// Q fragments of a prefill row tile: the tile's rows (rows tile_rows of a
+// contiguous [., D] bf16 array starting at q) as one buffer range, so rows
+// past the end read as zeros without a branch, and no wait on these loads
+// comes before the first K/V tiles are requested.
+template <class G>
+__device__ __forceinline__ void load_q_rows(u32x4_t (&qf)[G::NT][G::SD], const __bf16 *q, int tile_rows, int rg,
+                                            int lane, uint32_t qsign) {
+  const auto rq = make_rsrc(q, (uint32_t)tile_rows * G::D * 2);
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const uint32_t lr = (uint32_t)((rg * G::NT + nt) * 32 + (lane & 31));
+#pragma unroll
+    for (int sd = 0; sd < G::SD; ++sd)
+      qf[nt][sd] = neg_bf16x8(buf_load16(rq, (lr * G::D + 16 * sd + 8 * (lane >> 5)) * 2), qsign);
+  }
 }
 
 template <class G>
@@ -852,6 +876,7 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
   src.load_k(st, 0, b0, tid);
   src.load_v(st, 0, b0, tid);
   src.load_k(st1, 1, b1, tid);
+  q_to_lds<G>(qf, smem + G::QOFF + tid * 16);  // own Q slots: after the tile loads are on their way
   src.store_k(st, kbuf, tid);
   src.store_v(st, vbuf, 0, tid);
   src.store_k(st1, kbuf + G::KSLOT, tid);
@@ -931,13 +956,14 @@ __device__ __forceinline__ void dma_loop_body(WaveState<G> &ws, const TileImgSrc
                                               const u32x4_t (&qf)[G::NT][G::SD], char *__restrict__ kA,
                                               char *__restrict__ kB, char *__restrict__ kC, char *__restrict__ vA,
                                               char *__restrict__ vB, char *__restrict__ vC,
-                                              const char *__restrict__ qa, float c, const Mask &mk, int lane,
+                                              char *__restrict__ qa, float c, const Mask &mk, int lane,
                                               int wave, int n_iter) {
   src.copy_k(kA, 0, wave, lane);
   src.copy_v(vA, 0, wave, lane);
   src.copy_k(kB, 1, wave, lane);
   src.copy_v(vB, 1, wave, lane);
   src.copy_k(kC, 2, wave, lane);
+  q_to_lds<G>(qf, qa);  // own Q slots: after the tile copies are on their way
   wait_vm<0>();
   lds_barrier();
 
@@ -1061,12 +1087,6 @@ __device__ __forceinline__ int xcd_remap(int lin, int total) {
   return (lin % 8) * (total / 8) + lin / 8;
 }
 
-// A negative softmax scale is applied as a positive one on -q (exact), so the
-// kernels only ever see c > 0.
-__device__ __forceinline__ u32x4_t neg_bf16x8(u32x4_t x, uint32_t sign) {
-  return u32x4_t{x[0] ^ sign, x[1] ^ sign, x[2] ^ sign, x[3] ^ sign};
-}
-
 // ------------------------------------------------------------------ encoder kernel
 
 template <class G, bool F32IN, bool HAS_MASK, int ROPE>
@@ -1089,18 +1109,23 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   // with sd + SD/2)
   u32x4_t qf[G::NT][G::SD];
   const char *qb = reinterpret_cast<const char *>(a.q) + (b * a.qs[0] + h * a.qs[1]) * ES;
+  // This tile's rows as one buffer range ending with the last row's data
+  // (row stride < 2^24 bytes, checked on the host, so offsets fit 32 bits):
+  // rows past Sq read as zeros without a branch, and no wait on these loads
+  // comes before the first K/V tiles are requested.
+  const uint32_t qrow = (uint32_t)(a.qs[2] * ES);
+  const int row0 = qt * G::BM, nrow = min(a.Sq - row0, G::BM);
+  const auto rq = make_rsrc(qb + (int64_t)row0 * a.qs[2] * ES, (uint32_t)(nrow - 1) * qrow + G::D * ES);
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
-    const int row = qt * G::BM + (rg * G::NT + nt) * 32 + l32;
+    const int lrow = (rg * G::NT + nt) * 32 + l32, row = row0 + lrow;
     float f[G::SD][8];
 #pragma unroll
     for (int sd = 0; sd < G::SD; ++sd) {
-      const char *p = qb + (row * a.qs[2] + 16 * sd + 8 * hh) * ES;
-      u32x4_t x[F32IN ? 2 : 1] = {};
-      if (row < a.Sq) {
-        x[0] = ldg<u32x4_t>(p);
-        if constexpr (F32IN) x[1] = ldg<u32x4_t>(p + 16);
-      }
+      const uint32_t off = (uint32_t)lrow * qrow + (16 * sd + 8 * hh) * ES;
+      u32x4_t x[F32IN ? 2 : 1];
+      x[0] = buf_load16(rq, off);
+      if constexpr (F32IN) x[1] = buf_load16(rq, off + 16);
       unpack8<F32IN>(x, f[sd]);
     }
     if (ROPE != 0 && row < a.Sq) {
@@ -1140,7 +1165,6 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   src.n_keys = a.Skv;
   src.mask = HAS_MASK ? a.mask + b * a.mask_sb : nullptr;
 
-  q_to_lds<G>(qf, smem, threadIdx.x);
   WaveState<G> ws;
   flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c, TailMask{a.Skv}, true, threadIdx.x);
 
@@ -1248,16 +1272,8 @@ void prefill_paged_kernel(PrefillLaunch a) {
   const uint32_t qsign = a.q_neg ? 0x80008000u : 0u;
 
   u32x4_t qf[G::NT][G::SD];
-#pragma unroll
-  for (int nt = 0; nt < G::NT; ++nt) {
-    const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
-#pragma unroll
-    for (int sd = 0; sd < G::SD; ++sd)
-      qf[nt][sd] = neg_bf16x8(
-          r < rows ? ldg<u32x4_t>(a.q + (row_base + r) * G::D + 16 * sd + 8 * hh) : u32x4_t{0, 0, 0, 0}, qsign);
-  }
+  load_q_rows<G>(qf, a.q + (row_base + rt * G::BM) * G::D, min(rows - rt * G::BM, G::BM), rg, lane, qsign);
 
-  q_to_lds<G>(qf, smem, threadIdx.x);
   WaveState<G> ws;
   if constexpr (G::DMA) {
     TileImgSrc<G> src;
@@ -1310,35 +1326,32 @@ void prefill_current_kernel(PrefillLaunch a) {
   const uint32_t qsign = a.q_neg ? 0x80008000u : 0u;
 
   u32x4_t qf[G::NT][G::SD];
-#pragma unroll
-  for (int nt = 0; nt < G::NT; ++nt) {
-    const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
-#pragma unroll
-    for (int sd = 0; sd < G::SD; ++sd)
-      qf[nt][sd] = neg_bf16x8(
-          r < rows ? ldg<u32x4_t>(a.q + (row_base + r) * G::D + 16 * sd + 8 * hh) : u32x4_t{0, 0, 0, 0}, qsign);
-  }
+  load_q_rows<G>(qf, a.q + (row_base + rt * G::BM) * G::D, min(rows - rt * G::BM, G::BM), rg, lane, qsign);
 
-  q_to_lds<G>(qf, smem, threadIdx.x);
   // With a history: its normalised output O_h (fp32) and lse_h, i.e. the
   // state m = lse_h (log2 units), l = 1, O = O_h, which the loop continues.
   WaveState<G> ws;
   const bool fresh = a.L_act == 0;
   if (!fresh) {
+    // the tile's rows of both buffers as buffer ranges: no branch around the
+    // loads, so they do not hold up the first K/V tile loads
+    const int nrow = min(rows - rt * G::BM, G::BM);
+    const auto ro = make_rsrc(a.ws_o + (row_base + rt * G::BM) * G::D, (uint32_t)nrow * G::D * 4);
+    const auto rm = make_rsrc(a.ws_ml + row_base + rt * G::BM, (uint32_t)nrow * 4);
 #pragma unroll
     for (int nt = 0; nt < G::NT; ++nt) {
-      const int r = rt * G::BM + (rg * G::NT + nt) * 32 + l32;
-      const bool ok = r < rows;
+      const uint32_t lr = (uint32_t)((rg * G::NT + nt) * 32 + l32);
+      const bool ok = rt * G::BM + (int)lr < rows;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4_t x = ok ? ldg<f32x4_t>(a.ws_o + (row_base + r) * G::D + mt * 32 + r4 * 8 + 4 * hh)
-                               : f32x4_t{0, 0, 0, 0};
+          const u32x4_t x = buf_load16(ro, (lr * G::D + mt * 32 + r4 * 8 + 4 * hh) * 4);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) ws.o[nt][mt][4 * r4 + c] = x[c];
+          for (int c = 0; c < 4; ++c) ws.o[nt][mt][4 * r4 + c] = __uint_as_float(x[c]);
         }
-      ws.m[nt] = ok ? a.ws_ml[row_base + r] * kLog2e : -INFINITY;
+      const float lse_h = buf_load_f32(rm, lr * 4);
+      ws.m[nt] = ok ? lse_h * kLog2e : -INFINITY;
       ws.l[nt] = ok && hh == 0 ? 1.0f : 0.0f;  // the pair sum of the two halves gives l = 1
     }
   }
