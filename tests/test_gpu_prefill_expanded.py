@@ -133,3 +133,26 @@ def test_causal_expanded_workspace_too_small_is_an_error(gpu_lib):
         taa.attn_prefill_paged_causal_expanded(d(case.q), d(case.k_cache), d(case.v_cache), case.k_scale,
                                                case.v_scale, d(case.block_table), case.L_act, kc, vc, case.scale,
                                                case.G, workspace=ws)
+
+
+def test_expanded_shared_physical_blocks(gpu_lib):
+    # logical blocks that share physical blocks (a shared prefix): the table is
+    # read per tile, so every logical key still resolves to its own row
+    case = W.prefill_paged(190, 8, 4, 48, 256, 4, 64, 600)
+    case.block_table = torch.tensor([2, 0, 2, 1, 0, 3, 2, 1, 0, 2], dtype=torch.int32)
+    _say("[expanded] shared physical blocks, L_act=600 over a 10-entry table of 4 blocks")
+    plain, exp = _both(gpu_lib, case)
+    ref = oracle.prefill_paged(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale, case.block_table,
+                               case.L_act, case.scale, torch.arange(case.Lq))
+    assert_close(exp, ref, "expanded prefill, shared blocks")
+    assert torch.equal(exp, plain)
+
+
+def test_expanded_many_kv_heads(gpu_lib):
+    case = W.prefill_paged(191, 32, 8, 72, 256, 12, 128, 1400, n_rows=72)
+    _say("[expanded] Hq=32 Hkv=8 Lq=72 L_act=1400")
+    plain, exp = _both(gpu_lib, case)
+    ref = oracle.prefill_paged(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale, case.block_table,
+                               case.L_act, case.scale, torch.arange(case.Lq))
+    assert_close(exp, ref, "expanded prefill, 8 KV heads")
+    assert torch.equal(exp, plain)
