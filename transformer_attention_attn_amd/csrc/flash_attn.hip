@@ -1419,7 +1419,7 @@ using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true>;      // BM 128, 8 waves: 4 row 
 using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: mask values held in registers, 2 waves/SIMD
 using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: twice the staging registers per tile
 using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 3, true>;  // BM 256, 8 waves of 32 rows, 2 waves per SIMD, 3 Q fragments in LDS, PV priority
-using PrefImgGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 1, true, true>;  // the same over bf16 tile images copied by DMA (1 Q fragment in LDS: no staging registers)
+using PrefImgGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 1, false, true>;  // the same over bf16 tile images copied by DMA (1 Q fragment in LDS: no staging registers; no PV priority)
 
 // Launch with G::LDS bytes of dynamic LDS; kernels above 64 KiB are opted in
 // once per process (hipFuncSetAttribute is per function, not per device).
