@@ -297,9 +297,11 @@ ATTN_API int attn_prefill_paged_causal(const void *q, const void *k_cache, const
  *   workspace: at least attn_prefill_paged_causal_expanded_workspace_size(Hq,
  *   Hkv, Lq, actual_history_len, D) bytes, 256-byte aligned, owned by the
  *   caller: the hand-off state of attn_prefill_paged_causal (rounded up to 256
- *   bytes), then the tile images (none for an empty history).  Contents on
- *   entry ignored.  Missing or too small: ATTN_ERR_WORKSPACE.  The size
- *   function returns 0 for invalid or unsupported arguments.
+ *   bytes), then the history's tile images (none for an empty history), then
+ *   the current tokens' K/V as tile images of their own (Hkv * ceil(Lq / 32)
+ *   * 34816 bytes at D = 256).  Contents on entry ignored.  Missing or too
+ *   small: ATTN_ERR_WORKSPACE.  The size function returns 0 for invalid or
+ *   unsupported arguments.
  */
 ATTN_API size_t attn_prefill_paged_causal_expanded_workspace_size(int Hq, int Hkv, int Lq, int actual_history_len,
                                                                   int D);

@@ -232,13 +232,16 @@ def test_prefill_expanded_validation(lib, kw, expect):
 
 
 def test_prefill_causal_expanded_workspace_size():
-    # the causal hand-off state (rounded up to 256 bytes), then the history's tile images
+    # the causal hand-off state (rounded up to 256 bytes), then the history's tile images, then the
+    # current tokens' (34816 bytes per KV head and 32 keys each)
     hand = 32 * 4096 * 256 * 4 + 32 * 4096 * 4
-    assert taa.attn_prefill_paged_causal_expanded_workspace_size(32, 2, 4096, 120000, 256) == hand + 2 * 3750 * 34816
+    assert taa.attn_prefill_paged_causal_expanded_workspace_size(32, 2, 4096, 120000, 256) == \
+        hand + 2 * 3750 * 34816 + 2 * 128 * 34816
     hand = (6 * 100 * 256 * 4 + 6 * 100 * 4 + 255) // 256 * 256  # 616800 bytes, rounded up to 616960
     assert hand == 616960
-    assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 33, 256) == hand + 2 * 2 * 34816
-    assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 0, 256) == hand  # no history
+    cur = 2 * 4 * 34816  # ceil(100 / 32) tiles per KV head
+    assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 33, 256) == hand + 2 * 2 * 34816 + cur
+    assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 0, 256) == hand + cur  # no history
     assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 4, 100, 33, 256) == 0
     assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 33, 128) == 0
 

@@ -110,7 +110,7 @@ int prefill_common(const void *q, const void *k_cache, const void *v_cache, floa
                    const int32_t *block_table, int max_blocks, int num_blocks, int block_size, int actual_history_len,
                    const void *k_cur, const void *v_cur, float softmax_scale, int num_kv_groups, int Hq, int Hkv,
                    int Lq, int D, void *out, float *lse, void *workspace, size_t workspace_bytes,
-                   void *img_ws, size_t img_bytes, hipStream_t stream) {
+                   void *img_ws, size_t img_bytes, void *img_cur, hipStream_t stream) {
   const bool cur = k_cur != nullptr;
   if (!q || !k_cache || !v_cache || !block_table || !out) return ATTN_ERR_INVALID_ARG;
   if (max_blocks <= 0 || num_blocks <= 0 || block_size <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || D <= 0 ||
@@ -167,6 +167,10 @@ int prefill_common(const void *q, const void *k_cache, const void *v_cache, floa
   if (img_ws) {
     L.img = static_cast<char *>(img_ws);
     L.n_tiles = (actual_history_len + prefill_key_tile() - 1) / prefill_key_tile();
+  }
+  if (img_cur) {
+    L.img_cur = static_cast<char *>(img_cur);
+    L.n_tiles_cur = (Lq + prefill_key_tile() - 1) / prefill_key_tile();
   }
   L.out = static_cast<__bf16 *>(out);
   L.lse = lse;
@@ -355,7 +359,7 @@ int attn_prefill_paged(const void *q, const void *k_cache, const void *v_cache, 
                        int D, void *out, float *lse, hipStream_t stream) {
   return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
                         actual_history_len, nullptr, nullptr, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out, lse,
-                        nullptr, 0, nullptr, 0, stream);
+                        nullptr, 0, nullptr, 0, nullptr, stream);
 }
 
 size_t attn_prefill_paged_expanded_workspace_size(int Hkv, int actual_history_len, int D) {
@@ -372,7 +376,7 @@ int attn_prefill_paged_expanded(const void *q, const void *k_cache, const void *
   if (!workspace) return ATTN_ERR_WORKSPACE;
   return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
                         actual_history_len, nullptr, nullptr, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out, lse,
-                        nullptr, 0, workspace, workspace_bytes, stream);
+                        nullptr, 0, workspace, workspace_bytes, nullptr, stream);
 }
 
 size_t attn_prefill_paged_causal_workspace_size(int Hq, int Hkv, int Lq, int D) {
@@ -384,8 +388,9 @@ size_t attn_prefill_paged_causal_expanded_workspace_size(int Hq, int Hkv, int Lq
   const size_t hand = attn_prefill_paged_causal_workspace_size(Hq, Hkv, Lq, D);
   if (hand == 0 || actual_history_len < 0) return 0;
   const size_t img = actual_history_len > 0 ? attn_prefill_paged_expanded_workspace_size(Hkv, actual_history_len, D) : 0;
-  if (actual_history_len > 0 && img == 0) return 0;
-  return (hand + 255) / 256 * 256 + img;
+  const size_t cur = attn_prefill_paged_expanded_workspace_size(Hkv, Lq, D);  // the current tokens' images
+  if ((actual_history_len > 0 && img == 0) || cur == 0) return 0;
+  return (hand + 255) / 256 * 256 + img + cur;
 }
 
 int attn_prefill_paged_causal_expanded(const void *q, const void *k_cache, const void *v_cache, float k_scale,
@@ -400,15 +405,18 @@ int attn_prefill_paged_causal_expanded(const void *q, const void *k_cache, const
   if (need == 0) {  // invalid or unsupported arguments: let the shared validation name them
     return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
                           actual_history_len, k_cur, v_cur, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out,
-                          lse, workspace, workspace_bytes, nullptr, 0, stream);
+                          lse, workspace, workspace_bytes, nullptr, 0, nullptr, stream);
   }
   if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  // hand-off state first, then the tile images (256-byte aligned)
+  // hand-off state first, then the history's tile images, then the current
+  // tokens' (each a multiple of 256 bytes)
   const size_t hand = (attn_prefill_paged_causal_workspace_size(Hq, Hkv, Lq, D) + 255) / 256 * 256;
-  char *img = actual_history_len > 0 ? static_cast<char *>(workspace) + hand : nullptr;
+  const size_t himg =
+      actual_history_len > 0 ? attn_prefill_paged_expanded_workspace_size(Hkv, actual_history_len, D) : 0;
+  char *const base = static_cast<char *>(workspace);
   return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
                         actual_history_len, k_cur, v_cur, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out, lse,
-                        workspace, hand, img, workspace_bytes - hand, stream);
+                        workspace, hand, himg ? base + hand : nullptr, himg, base + hand + himg, stream);
 }
 
 int attn_prefill_paged_causal(const void *q, const void *k_cache, const void *v_cache, float k_scale, float v_scale,
@@ -419,7 +427,7 @@ int attn_prefill_paged_causal(const void *q, const void *k_cache, const void *v_
   if (!k_cur || !v_cur) return ATTN_ERR_INVALID_ARG;
   return prefill_common(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks, num_blocks, block_size,
                         actual_history_len, k_cur, v_cur, softmax_scale, num_kv_groups, Hq, Hkv, Lq, D, out, lse,
-                        workspace, workspace_bytes, nullptr, 0, stream);
+                        workspace, workspace_bytes, nullptr, 0, nullptr, stream);
 }
 
 int res_ln(const float *residual, const void *x, attn_dtype_t x_dtype, const float *gamma, const float *beta,

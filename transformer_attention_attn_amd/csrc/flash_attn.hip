@@ -1370,45 +1370,62 @@ void prefill_current_kernel(PrefillLaunch a) {
   // keys this tile needs: one past its largest token (all of them when its
   // rows span two heads)
   const int first = rt * G::BM, last = min(first + G::BM, rows) - 1;
-  EncSrc<G, false, false> cs;
-  cs.kb = reinterpret_cast<const char *>(a.kcur + (int64_t)kvh * a.Lq * G::D);
-  cs.vb = reinterpret_cast<const char *>(a.vcur + (int64_t)kvh * a.Lq * G::D);
-  cs.krow = cs.vrow = G::D * 2;
-  cs.kstep = cs.vstep = (int64_t)G::NSPLIT * G::BN * G::D * 2;
-  cs.n_keys = first / a.Lq == last / a.Lq ? last % a.Lq + 1 : a.Lq;
-  cs.mask = nullptr;
-  flash_loop<G, false>(ws, cs, qf, smem, a.c_cur, cm, fresh, threadIdx.x);
+  const int n_keys = first / a.Lq == last / a.Lq ? last % a.Lq + 1 : a.Lq;
+  if constexpr (G::DMA) {  // the current K/V as tile images
+    TileImgSrc<G> src;
+    src.img = a.img_cur + (int64_t)kvh * a.n_tiles_cur * TileImgSrc<G>::TIMG;
+    src.n_tiles = a.n_tiles_cur;
+    src.n_keys = n_keys;
+    flash_loop_dma<G>(ws, src, qf, smem, a.c_cur, cm, fresh, threadIdx.x);
+  } else {
+    EncSrc<G, false, false> cs;
+    cs.kb = reinterpret_cast<const char *>(a.kcur + (int64_t)kvh * a.Lq * G::D);
+    cs.vb = reinterpret_cast<const char *>(a.vcur + (int64_t)kvh * a.Lq * G::D);
+    cs.krow = cs.vrow = G::D * 2;
+    cs.kstep = cs.vstep = (int64_t)G::NSPLIT * G::BN * G::D * 2;
+    cs.n_keys = n_keys;
+    cs.mask = nullptr;
+    flash_loop<G, false>(ws, cs, qf, smem, a.c_cur, cm, fresh, threadIdx.x);
+  }
 
   prefill_epilogue<G, false>(ws, a, rt, kvh, rg, lane, 1.0f);
 }
 
 // ------------------------------------------------------------------ tile images
 
-// Expand the live history of the paged FP8 cache into the bf16 tile images
-// the DMA key loop copies (TileImgSrc): one workgroup per (tile, KV head).
-// e4m3fn -> bf16 is exact; keys at or past L_act and the V row pads are
-// written as zeros.  K reads run along each key row (coalesced) and write
-// chunk-major; V rows are read and written in order.
-template <class G>
+// Write the bf16 tile images the DMA key loop copies (TileImgSrc): one
+// workgroup per (tile, KV head).  Source: the live history of the paged FP8
+// cache (e4m3fn -> bf16, exact), or with CUR the current tokens' bf16 K/V
+// [Hkv, Lq, D].  Keys past the end and the V row pads are written as zeros.
+// K reads run along each key row (coalesced) and write chunk-major; V rows are
+// read and written in order.
+template <class G, bool CUR>
 __global__ __launch_bounds__(256) void prefill_tile_images_kernel(PrefillLaunch a) {
   constexpr int CH = G::D / 8;                  // 16-byte bf16 chunks per key
   constexpr int VROW = G::v_row_bytes();        // padded V row
   constexpr int VCH = VROW / 16;
   const int t = blockIdx.x, kvh = blockIdx.y;
-  char *const img = a.img + ((int64_t)kvh * a.n_tiles + t) * TileImgSrc<G>::TIMG;
-  auto src8 = [&](const uint8_t *cache, int key, int c) -> u32x4_t {
-    const int32_t phys = a.bt[key / a.bs];
-    const uint8_t *p = cache + (((int64_t)phys * a.Hkv + kvh) * a.bs + key % a.bs) * G::D + c * 8;
-    return PagedSrc<G>::cvt8(*reinterpret_cast<const u32x2_t *>(p));
+  const int n_keys = CUR ? a.Lq : a.L_act;
+  char *const img = (CUR ? a.img_cur : a.img) + ((int64_t)kvh * (CUR ? a.n_tiles_cur : a.n_tiles) + t) *
+                                                    TileImgSrc<G>::TIMG;
+  auto src16 = [&](bool is_k, int key, int c) -> u32x4_t {  // 8 bf16 of key `key`, chunk c
+    if constexpr (CUR) {
+      const __bf16 *p = (is_k ? a.kcur : a.vcur) + ((int64_t)kvh * a.Lq + key) * G::D + c * 8;
+      return *reinterpret_cast<const u32x4_t *>(p);
+    } else {
+      const int32_t phys = a.bt[key / a.bs];
+      const uint8_t *p = (is_k ? a.kc : a.vc) + (((int64_t)phys * a.Hkv + kvh) * a.bs + key % a.bs) * G::D + c * 8;
+      return PagedSrc<G>::cvt8(*reinterpret_cast<const u32x2_t *>(p));
+    }
   };
   for (int i = threadIdx.x; i < G::BN * CH; i += 256) {
     const int k = i / CH, c = i % CH, key = t * G::BN + k;
-    const u32x4_t x = key < a.L_act ? src8(a.kc, key, c) : u32x4_t{0, 0, 0, 0};
+    const u32x4_t x = key < n_keys ? src16(true, key, c) : u32x4_t{0, 0, 0, 0};
     *reinterpret_cast<u32x4_t *>(img + c * (G::BN * 16) + k * 16) = x;
   }
   for (int i = threadIdx.x; i < G::BN * VCH; i += 256) {
     const int k = i / VCH, c = i % VCH, key = t * G::BN + k;
-    const u32x4_t x = c < CH && key < a.L_act ? src8(a.vc, key, c) : u32x4_t{0, 0, 0, 0};
+    const u32x4_t x = c < CH && key < n_keys ? src16(false, key, c) : u32x4_t{0, 0, 0, 0};
     *reinterpret_cast<u32x4_t *>(img + G::KTILE + k * VROW + c * 16) = x;
   }
 }
@@ -1420,6 +1437,7 @@ using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: mask values hel
 using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: twice the staging registers per tile
 using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 3, true>;  // BM 256, 8 waves of 32 rows, 2 waves per SIMD, 3 Q fragments in LDS, PV priority
 using PrefImgGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 1, false, true>;  // the same over bf16 tile images copied by DMA (1 Q fragment in LDS: no staging registers; no PV priority)
+using PrefCurImgGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 4, false, true>;  // current tokens over their images: the causal state needs 4 Q fragments in LDS to stay out of scratch
 
 // Launch with G::LDS bytes of dynamic LDS; kernels above 64 KiB are opted in
 // once per process (hipFuncSetAttribute is per function, not per device).
@@ -1468,7 +1486,8 @@ hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream) {
   static_assert(PrefImgGeo::BM == PrefGeo::BM && PrefImgGeo::BN == PrefGeo::BN, "same tiles");
   const dim3 grid(n_rt * a.Hkv);
   if (a.img && a.L_act > 0) {  // the history through its tile images
-    hipLaunchKernelGGL(prefill_tile_images_kernel<PrefImgGeo>, dim3(a.n_tiles, a.Hkv), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_tile_images_kernel<PrefImgGeo, false>), dim3(a.n_tiles, a.Hkv), dim3(256), 0, stream,
+                       a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (!a.kcur) return launch_lds<PrefImgGeo>(prefill_paged_kernel<PrefImgGeo, false>, grid, a, stream);
@@ -1480,7 +1499,16 @@ hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream) {
     const hipError_t e = launch_lds<PrefGeo>(prefill_paged_kernel<PrefGeo, true>, grid, a, stream);
     if (e != hipSuccess) return e;
   }
-  return launch_lds<PrefGeo>(prefill_current_kernel<PrefGeo>, dim3(n_rt * a.Hkv), a, stream);
+  if (a.img_cur) {  // the current tokens through their tile images
+    static_assert(PrefCurImgGeo::BM == PrefGeo::BM && TileImgSrc<PrefCurImgGeo>::TIMG == TileImgSrc<PrefImgGeo>::TIMG,
+                  "same row tiles and tile images");
+    hipLaunchKernelGGL((prefill_tile_images_kernel<PrefImgGeo, true>), dim3(a.n_tiles_cur, a.Hkv), dim3(256), 0,
+                       stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_lds<PrefCurImgGeo>(prefill_current_kernel<PrefCurImgGeo>, grid, a, stream);
+  }
+  return launch_lds<PrefGeo>(prefill_current_kernel<PrefGeo>, grid, a, stream);
 }
 
 int prefill_key_tile() { return PrefGeo::BN; }

@@ -50,6 +50,8 @@ struct PrefillLaunch {
   float *ws_o, *ws_ml;        // history -> current-token handoff (causal part with a history)
   char *img;                  // nullable: bf16 tile images of the history [Hkv, n_tiles, image] (workspace)
   int n_tiles;                // tiles of prefill_key_tile() keys per KV head in img
+  char *img_cur;              // nullable: tile images of the current tokens' K/V [Hkv, n_tiles_cur, image]
+  int n_tiles_cur;
   __bf16 *out;
   float *lse;     // nullable
 };
