@@ -278,6 +278,46 @@ def time_next_workloads(taa, dev, flush, pre_dev, reps: int = 20):
     return out
 
 
+def pcp_shapes(reps: int = 10) -> None:
+    """The paged prefill at the PCP page's Q-scaling shapes (32 query heads over 2 KV
+    heads, head_dim 256, 8192 history keys in 512-token blocks, Lq 1024 .. 16384):
+    both entry points timed back to back on one GPU, printed as a markdown table
+    beside the page's 4-chip times (another machine: context only)."""
+    import transformer_attention_attn_amd as taa
+
+    taa.load()
+    dev = torch.device("cuda:0")
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "page_throughput_figures.json")))
+    page = {row[0]: row[1] for row in gold["pcp_q_scaling_hist8192"]["rows"]}
+    print("| Lq | expanded ms | TFLOP/s | % bf16 peak | no-workspace ms | TFLOP/s | page, 4 chips (ms) |")
+    print("|---|---|---|---|---|---|---|")
+    for Lq in (1024, 4096, 8192, 16384):
+        case = W.prefill_paged(2000 + Lq, 32, 2, Lq, 256, 16, 512, 8192, n_rows=1)
+        q, k, v, bt = (t.to(dev) for t in (case.q, case.k_cache, case.v_cache, case.block_table))
+        out = torch.empty_like(q)
+        ws = torch.empty(taa.attn_prefill_paged_expanded_workspace_size(case.Hkv, case.L_act, case.D),
+                         dtype=torch.uint8, device=dev)
+        args = (q, k, v, case.k_scale, case.v_scale, bt, case.L_act, case.scale, case.G)
+        f = acc.prefill_flops(Lq, case.Hq, case.L_act, case.D)
+        res = []
+        for fn in (lambda: taa.attn_prefill_paged_expanded(*args, out=out, workspace=ws),
+                   lambda: taa.attn_prefill_paged(*args, out=out)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) / reps)
+        tf = [f / (ms * 1e-3) / 1e12 for ms in res]
+        print(f"| {Lq} | {res[0]:.3f} | {tf[0]:.0f} | {100 * tf[0] / acc.PEAK_BF16_TFLOPS:.1f} | {res[1]:.3f} | "
+              f"{tf[1]:.0f} | {page[Lq]} |", flush=True)
+        del q, k, v, bt, out, ws
+
+
 def _short(name: str) -> str:
     """Kernel family name from a demangled rocprofv3 kernel name."""
     for k in ("prefill_paged_kernel", "prefill_tile_images_kernel", "encoder_fwd_kernel", "res_ln_kernel",
@@ -365,6 +405,8 @@ def main():
                     help="run a single kernel family (profiling runs)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the workload variants reported under parts.next (profiling runs of the step)")
+    ap.add_argument("--pcp-shapes", action="store_true",
+                    help="only time the paged prefill at the PCP page's Q-scaling shapes (markdown table)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (scales the rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -381,6 +423,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 4}))
+        return
+    if args.pcp_shapes:
+        pcp_shapes()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
