@@ -81,6 +81,24 @@ def test_causal_prefill_in_a_graph(gpu_lib):
     assert torch.equal(lse, eager_lse)
 
 
+def test_causal_expanded_prefill_in_a_graph(gpu_lib):
+    taa = gpu_lib
+    case = W.prefill_paged(1205, 8, 2, 300, 256, 6, 128, 700)
+    kc, vc = (t.to(DEV) for t in W.prefill_current_kv(1206, 2, 300))
+    d = lambda t: t.to(DEV)
+    q, k, v, bt = d(case.q), d(case.k_cache), d(case.v_cache), d(case.block_table)
+    out = torch.empty_like(q)
+    ws = torch.empty(taa.attn_prefill_paged_causal_expanded_workspace_size(case.Hq, case.Hkv, case.Lq, case.L_act,
+                                                                         case.D), dtype=torch.uint8, device=DEV)
+    call = lambda: taa.attn_prefill_paged_causal_expanded(q, k, v, case.k_scale, case.v_scale, bt, case.L_act, kc,
+                                                          vc, case.scale, case.G, out=out, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    _say("[graph] causal prefill over tile images (four kernels)")
+    _replays_match(call, out, eager)
+
+
 def test_expanded_prefill_in_a_graph(gpu_lib):
     taa = gpu_lib
     case = W.prefill_paged(1204, 8, 2, 300, 256, 6, 128, 700)
