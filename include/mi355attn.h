@@ -240,7 +240,7 @@ ATTN_API int attn_prefill_paged(const void *q, const void *k_cache, const void *
  * histories; costs one pass over the live history (fp8 read, bf16 written).
  *   workspace: at least attn_prefill_paged_expanded_workspace_size(Hkv,
  *   actual_history_len, D) bytes (Hkv * ceil(actual_history_len / 32) *
- *   34816 at D = 256), 256-byte aligned, owned by the caller; contents on
+ *   32768 at D = 256), 256-byte aligned, owned by the caller; contents on
  *   entry ignored, overwritten.  Missing or too small: ATTN_ERR_WORKSPACE.
  *   The size function returns 0 for invalid or unsupported arguments.
  */
@@ -299,7 +299,7 @@ ATTN_API int attn_prefill_paged_causal(const void *q, const void *k_cache, const
  *   caller: the hand-off state of attn_prefill_paged_causal (rounded up to 256
  *   bytes), then the history's tile images (none for an empty history), then
  *   the current tokens' K/V as tile images of their own (Hkv * ceil(Lq / 32)
- *   * 34816 bytes at D = 256).  Contents on entry ignored.  Missing or too
+ *   * 32768 bytes at D = 256).  Contents on entry ignored.  Missing or too
  *   small: ATTN_ERR_WORKSPACE.  The size function returns 0 for invalid or
  *   unsupported arguments.
  */

@@ -56,7 +56,7 @@ def test_status_strings(lib):
     for s in range(5):
         assert taa.attn_status_string(s).startswith(("ATTN_OK", "ATTN_ERR"))
     assert taa.attn_status_string(99) == "unknown attn status"
-    assert taa.attn_version() == 10200
+    assert taa.attn_version() == 10300
 
 
 def _enc(**kw):
@@ -224,7 +224,7 @@ def _pex(**kw):
     (dict(ks=0.0), taa.ATTN_ERR_INVALID_ARG),
     (dict(out=BAD), taa.ATTN_ERR_INVALID_ARG),
     (dict(ws=None), taa.ATTN_ERR_WORKSPACE),
-    (dict(wsb=2 * 3750 * 34816 - 1), taa.ATTN_ERR_WORKSPACE),   # one byte short of the live history's tiles
+    (dict(wsb=2 * 3750 * 32768 - 1), taa.ATTN_ERR_WORKSPACE),   # one byte short of the live history's tiles
     (dict(ws=FAKE + 16), taa.ATTN_ERR_INVALID_ARG),             # workspace must be 256-byte aligned
 ])
 def test_prefill_expanded_validation(lib, kw, expect):
@@ -233,24 +233,24 @@ def test_prefill_expanded_validation(lib, kw, expect):
 
 def test_prefill_causal_expanded_workspace_size():
     # the causal hand-off state (rounded up to 256 bytes), then the history's tile images, then the
-    # current tokens' (34816 bytes per KV head and 32 keys each)
+    # current tokens' (32768 bytes per KV head and 32 keys each)
     hand = 32 * 4096 * 256 * 4 + 32 * 4096 * 4
     assert taa.attn_prefill_paged_causal_expanded_workspace_size(32, 2, 4096, 120000, 256) == \
-        hand + 2 * 3750 * 34816 + 2 * 128 * 34816
+        hand + 2 * 3750 * 32768 + 2 * 128 * 32768
     hand = (6 * 100 * 256 * 4 + 6 * 100 * 4 + 255) // 256 * 256  # 616800 bytes, rounded up to 616960
     assert hand == 616960
-    cur = 2 * 4 * 34816  # ceil(100 / 32) tiles per KV head
-    assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 33, 256) == hand + 2 * 2 * 34816 + cur
+    cur = 2 * 4 * 32768  # ceil(100 / 32) tiles per KV head
+    assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 33, 256) == hand + 2 * 2 * 32768 + cur
     assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 0, 256) == hand + cur  # no history
     assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 4, 100, 33, 256) == 0
     assert taa.attn_prefill_paged_causal_expanded_workspace_size(6, 2, 100, 33, 128) == 0
 
 
 def test_prefill_expanded_workspace_size():
-    # per KV head, one 34816-byte image (16 KiB of K, 32 padded 576-byte V rows) per 32 live keys
-    assert taa.attn_prefill_paged_expanded_workspace_size(2, 120000, 256) == 2 * 3750 * 34816
-    assert taa.attn_prefill_paged_expanded_workspace_size(3, 33, 256) == 3 * 2 * 34816
-    assert taa.attn_prefill_paged_expanded_workspace_size(1, 1, 256) == 34816
+    # per KV head, one 32768-byte image (16 KiB of K, 16 KiB of V^T) per 32 live keys
+    assert taa.attn_prefill_paged_expanded_workspace_size(2, 120000, 256) == 2 * 3750 * 32768
+    assert taa.attn_prefill_paged_expanded_workspace_size(3, 33, 256) == 3 * 2 * 32768
+    assert taa.attn_prefill_paged_expanded_workspace_size(1, 1, 256) == 32768
     assert taa.attn_prefill_paged_expanded_workspace_size(2, 0, 256) == 0
     assert taa.attn_prefill_paged_expanded_workspace_size(2, 100, 128) == 0
 

@@ -192,7 +192,7 @@ const char *attn_status_string(int status) {
   }
 }
 
-int attn_version(void) { return 10200; }
+int attn_version(void) { return 10300; }
 
 size_t attn_encoder_rope_workspace_size(int B, int H, int S_kv, int D, attn_dtype_t in_dtype) {
   if (B <= 0 || H <= 0 || S_kv <= 0 || D <= 0) return 0;

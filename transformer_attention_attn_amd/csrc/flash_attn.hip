@@ -43,9 +43,10 @@
 // of the PV MFMA (d on M, keys on K) with ds_read_b64_tr_b16.  The pads make
 // the 16-byte K reads, the transposing V reads and the 16-byte writes all
 // bank-conflict-free while every fragment address stays one per-lane base
-// plus an immediate.  Global
-// K/V loads are raw buffer loads whose range ends at the last valid key, so
-// out-of-range keys read as zeros without a branch.
+// plus an immediate.  (Tile images copied by DMA hold K chunk-major and V
+// transposed instead: see Geo.)  Global K/V loads are raw buffer loads whose
+// range ends at the last valid key, so out-of-range keys read as zeros
+// without a branch.
 #include "device_common.h"
 #include "launch.h"
 
@@ -96,13 +97,18 @@ struct Geo {
   // A direct load cannot pad inside its 1 KB, so K is chunk-major instead of
   // padded: the 16-byte chunk c (d = 8c .. 8c+7) of key k sits at
   // c*BN*16 + k*16, which keeps the 32 keys one fragment read touches in 512
-  // contiguous bytes.  V keeps the padded row layout (its image carries the
-  // pads).  Three buffers per operand let a tile's copy run two iterations
-  // ahead of its use.
+  // contiguous bytes.  V is stored transposed (V^T), so that a PV A fragment
+  // (d = lane%32, 8 keys) is one 16-byte read instead of two 8-byte
+  // transposing reads: each k-step's 16 keys fill one half of the image, a
+  // 32-byte row per d (vt_off), so the k-step and the d tile are immediate
+  // offsets; within a row the two 16-byte chunks swap on d bit 2 ^ bit 3,
+  // which puts 8 (and 16) consecutive lanes in 8 (and 16) different 16-byte
+  // bank groups.  Three buffers per operand let a tile's copy run two
+  // iterations ahead of its use.
   static constexpr bool DMA = DMA_;
   static constexpr int NBUF = DMA ? 3 : 2;
   static constexpr int KTILE = DMA ? BN * D * 2 : BN * KROW;
-  static constexpr int VTILE = BN * D * 2 + (BN >> VSH) * 64;
+  static constexpr int VTILE = DMA ? BN * D * 2 : BN * D * 2 + (BN >> VSH) * 64;
   static constexpr int KSLOT = NSPLIT * KTILE;                    // one K buffer: every split's tile
   static constexpr int VSLOT = NSPLIT * VTILE + NSPLIT * BN * 4;  // one V buffer, then the tiles' staged key mask
   static constexpr int KB = BN / 32;  // 32-key blocks per tile
@@ -127,8 +133,8 @@ struct Geo {
   static constexpr int VPM = (NT * (7 * BN / 4 + 8) + NFQ - 1) / NFQ;
   static_assert(D % 64 == 0 && BN % 32 == 0 && (VSH == 0 || D == 64), "tile shape");
   static_assert(QL >= 0 && QL <= SD, "Q fragments in LDS");
-  static_assert(!DMA || (NSPLIT == 1 && VSH == 0 && KTILE % 1024 == 0 && VTILE % 1024 == 0),
-                "tile images: one key split, one pad per V row, 1 KB pieces");
+  static_assert(!DMA || (NSPLIT == 1 && BN == 32 && KTILE % 1024 == 0 && VTILE % 1024 == 0),
+                "tile images: one key split, 32-key tiles, 1 KB pieces");
   static_assert(LDS <= 160 * 1024, "LDS budget (gfx950: 160 KiB per workgroup)");
 
   static __device__ __forceinline__ int k_row(int key) { static_assert(!DMA, "padded K rows"); return key * KROW; }
@@ -139,7 +145,14 @@ struct Geo {
   }
   static constexpr int k_frag(int kb, int sd) { return DMA ? kb * 512 + sd * 2 * BN * 16 : kb * 32 * KROW + 32 * sd; }
   static __device__ __forceinline__ int v_row(int key) { return key * (D * 2) + (key >> VSH) * 64; }
-  static constexpr int v_row_bytes() { static_assert(VSH == 0, "one pad per row"); return D * 2 + 64; }
+  // DMA: the V^T chunk of (d, k-step kk, lane half h) holds, as elements
+  // j = 0..7, the keys 16kk + 8(j/4) + 4h + j%4 (the key order of P's B
+  // fragment) and sits at vt_off(d, kk, h).
+  static __host__ __device__ constexpr int vt_swz(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
+  static __host__ __device__ constexpr int vt_off(int d, int kk, int h) {
+    return kk * D * 32 + d * 32 + 16 * (h ^ vt_swz(d));
+  }
+  static __host__ __device__ constexpr int vt_key(int kk, int h, int j) { return 16 * kk + 8 * (j >> 2) + 4 * h + (j & 3); }
 };
 
 // ------------------------------------------------------------------ sources
@@ -377,7 +390,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Tile images of a KV head's history (G::DMA): tile t holds the K image
-// (chunk-major, G::KTILE bytes) then the V image (padded rows, G::VTILE
+// (chunk-major, G::KTILE bytes) then the V^T image (G::VTILE
 // bytes), each exactly as the key loop's LDS buffers hold them, so a tile is
 // copied global -> LDS by direct buffer loads: 1 KB per wave instruction,
 // lane L's 16 bytes at LDS base + 16 L.  Wave w issues pieces w, w + WAVES,
@@ -791,13 +804,19 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
   constexpr int WS = (G::NFV - 1 - G::MT) / 2;
   static_assert(SPB == 0 || (WS >= 1 && G::MT + 2 * WS < G::NFV), "phase B schedule");
   const int h = lane >> 5, j = (lane >> 2) & 3, m = lane & 3, g2 = (lane >> 4) & 1;
-  const char *vbase = vt + G::v_row(4 * h) + G::v_row(j) + 32 * g2 + 8 * m;
+  const char *vbase = vt + (G::DMA ? 0 : G::v_row(4 * h) + G::v_row(j) + 32 * g2 + 8 * m);
+  // V^T (DMA): d = mt*32 + lane%32, and the swizzle sees d bits 2, 3 only
+  const int vto = G::vt_off(lane & 31, 0, h);
   u32x4_t fb[G::NFV];
   auto read = [&](int q) {
     const int mt = q % G::MT, kk = (q / G::MT) % 2, kb = q / (2 * G::MT);
-    const char *p = vbase + G::v_row(kb * 32 + kk * 16) + 64 * mt;
-    const u32x2_t a0 = lds_read_tr16(p), a1 = lds_read_tr16(p + G::v_row(8));
-    fb[q] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    if constexpr (G::DMA) {
+      fb[q] = *reinterpret_cast<const u32x4_t *>(vt + vto + G::vt_off(32 * mt, kk, 0));
+    } else {
+      const char *p = vbase + G::v_row(kb * 32 + kk * 16) + 64 * mt;
+      const u32x2_t a0 = lds_read_tr16(p), a1 = lds_read_tr16(p + G::v_row(8));
+      fb[q] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    }
   };
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1396,14 +1415,12 @@ void prefill_current_kernel(PrefillLaunch a) {
 // Write the bf16 tile images the DMA key loop copies (TileImgSrc): one
 // workgroup per (tile, KV head).  Source: the live history of the paged FP8
 // cache (e4m3fn -> bf16, exact), or with CUR the current tokens' bf16 K/V
-// [Hkv, Lq, D].  Keys past the end and the V row pads are written as zeros.
-// K reads run along each key row (coalesced) and write chunk-major; V rows are
-// read and written in order.
+// [Hkv, Lq, D].  Keys past the end are written as zeros.  K reads run along
+// each key row (coalesced) and write chunk-major; V is transposed through
+// LDS.
 template <class G, bool CUR>
 __global__ __launch_bounds__(256) void prefill_tile_images_kernel(PrefillLaunch a) {
   constexpr int CH = G::D / 8;                  // 16-byte bf16 chunks per key
-  constexpr int VROW = G::v_row_bytes();        // padded V row
-  constexpr int VCH = VROW / 16;
   const int t = blockIdx.x, kvh = blockIdx.y;
   const int n_keys = CUR ? a.Lq : a.L_act;
   char *const img = (CUR ? a.img_cur : a.img) + ((int64_t)kvh * (CUR ? a.n_tiles_cur : a.n_tiles) + t) *
@@ -1423,10 +1440,23 @@ __global__ __launch_bounds__(256) void prefill_tile_images_kernel(PrefillLaunch 
     const u32x4_t x = key < n_keys ? src16(true, key, c) : u32x4_t{0, 0, 0, 0};
     *reinterpret_cast<u32x4_t *>(img + c * (G::BN * 16) + k * 16) = x;
   }
-  for (int i = threadIdx.x; i < G::BN * VCH; i += 256) {
-    const int k = i / VCH, c = i % VCH, key = t * G::BN + k;
-    const u32x4_t x = c < CH && key < n_keys ? src16(false, key, c) : u32x4_t{0, 0, 0, 0};
-    *reinterpret_cast<u32x4_t *>(img + G::KTILE + k * VROW + c * 16) = x;
+  // V^T: the tile's rows go through LDS ([key][d] bf16), then thread i
+  // writes the image's 16-byte chunk i (consecutive threads, consecutive
+  // bytes): k-step i / 2D, d = (i / 2) % D, stored chunk i % 2
+  __shared__ u32x4_t vstage[G::BN * CH];
+  for (int i = threadIdx.x; i < G::BN * CH; i += 256) {
+    const int k = i / CH, c = i % CH, key = t * G::BN + k;
+    vstage[i] = key < n_keys ? src16(false, key, c) : u32x4_t{0, 0, 0, 0};
+  }
+  __syncthreads();
+  const uint16_t *vs = reinterpret_cast<const uint16_t *>(vstage);
+  for (int i = threadIdx.x; i < G::D * 4; i += 256) {
+    const int kk = i / (2 * G::D), d = (i / 2) % G::D, h = (i % 2) ^ G::vt_swz(d);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = vs[G::vt_key(kk, h, 2 * e) * G::D + d] | (uint32_t)vs[G::vt_key(kk, h, 2 * e + 1) * G::D + d] << 16;
+    *reinterpret_cast<u32x4_t *>(img + G::KTILE + i * 16) = u32x4_t{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -1436,7 +1466,7 @@ using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true>;      // BM 128, 8 waves: 4 row 
 using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: mask values held in registers, 2 waves/SIMD
 using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: twice the staging registers per tile
 using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 3, true>;  // BM 256, 8 waves of 32 rows, 2 waves per SIMD, 3 Q fragments in LDS, PV priority
-using PrefImgGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 1, false, true>;  // the same over bf16 tile images copied by DMA (1 Q fragment in LDS: no staging registers; no PV priority)
+using PrefImgGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 0, false, true>;  // the same over bf16 tile images copied by DMA (no staging registers: Q fits in registers; no PV priority)
 using PrefCurImgGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 4, false, true>;  // current tokens over their images: the causal state needs 4 Q fragments in LDS to stay out of scratch
 
 // Launch with G::LDS bytes of dynamic LDS; kernels above 64 KiB are opted in
