@@ -790,7 +790,9 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
 // it: in 16-lane group g the reading lane 4m + j names the 8 bytes
 // V[kb*32 + 16kk + 8t + 4h + j][mt*32 + 16(g%2) + 4m ..], and output lane
 // 16g + 4m + c receives element c of those four rows.  Row bases are
-// multiples of 4, so v_row(base + j) = v_row(base) + v_row(j).
+// multiples of 4, so v_row(base + j) = v_row(base) + v_row(j).  Over tile
+// images (G::DMA) V^T already holds those keys in that order: one 16-byte
+// read at vt_off.
 template <class G, bool HAS_MASK, class Work>
 __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f32x16_t (&s)[G::NT][G::KB],
                                         float c, const char *vt, int lane, Work &&work) {
