@@ -156,3 +156,23 @@ def test_expanded_many_kv_heads(gpu_lib):
                                case.L_act, case.scale, torch.arange(case.Lq))
     assert_close(exp, ref, "expanded prefill, 8 KV heads")
     assert torch.equal(exp, plain)
+
+
+def test_causal_expanded_full_config(gpu_lib):
+    # the causal call over tile images at the full prefill shape (the bench's):
+    # bit for bit the converting path, and sampled rows against the oracle
+    taa = gpu_lib
+    case = W.prefill_paged()
+    kc, vc = (t.to(DEV) for t in W.prefill_current_kv(1105, case.Hkv, case.Lq))
+    rows = torch.cat([case.rows[:6], torch.tensor([0, case.Lq - 1])])
+    d = lambda t: t.to(DEV)
+    args = (d(case.q), d(case.k_cache), d(case.v_cache), case.k_scale, case.v_scale, d(case.block_table), case.L_act,
+            kc, vc, case.scale, case.G)
+    _say(f"[expanded] causal full cfg Lq={case.Lq} L_act={case.L_act}, {len(rows)} tokens x all heads")
+    po, pl = taa.attn_prefill_paged_causal(*args, want_lse=True)
+    eo, el = taa.attn_prefill_paged_causal_expanded(*args, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(eo, po) and torch.equal(el, pl)
+    ref = oracle.prefill_causal(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale, case.block_table,
+                                case.L_act, kc.cpu(), vc.cpu(), case.scale, rows)
+    assert_close(eo[:, rows.to(DEV)], ref, "causal expanded full (sampled rows)")
