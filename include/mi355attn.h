@@ -97,7 +97,10 @@ ATTN_API int attn_version(void);
  *                contiguous [B,S_q,H*D]; requires residual_out.
  *   ln_mean/ln_rstd  fp32 [B*S_q] statistics of that LayerNorm (nullable).
  * gamma/beta are fp32 [H*D] and nullable (affine-free LayerNorm).
- * mask is nullable fp32 [B,1,1,S_kv] with batch stride mask_stride_b.
+ * mask is nullable fp32 [B,1,1,S_kv], 4-byte aligned, row b at mask + b *
+ * mask_stride_b: a stride of at least S_kv (rows do not overlap), or 0 for one
+ * row [1,1,1,S_kv] shared by the whole batch; a negative stride, or one in
+ * 1..S_kv-1 with B > 1, is ATTN_ERR_INVALID_ARG.
  *
  * Fused RoPE prologue (rope != ATTN_ROPE_NONE; vit-encoder-neuron-kernels,
  * "Kernels": the rotate-half and interleaved pairings; V-JEPA2 ViT-L Encoder

@@ -42,7 +42,7 @@ def lib():
         P, I, D, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_int64
         L.oracle_sdpa.argtypes = [P, I, P, I, P, I, P, I, I, I, I, I, I, D, P, P]
         L.oracle_layernorm.argtypes = [P, I64, I, P, P, D, P, P, P]
-        L.oracle_encoder_block.argtypes = [P, P, P, I, P, I, I, I, I, D, P, P, P, D, P, P, P, P, P]
+        L.oracle_encoder_block.argtypes = [P, P, P, I, P, I, I, I, I, I, D, P, P, P, D, P, P, P, P, P]
         L.oracle_prefill_paged.argtypes = [P, I, P, P, D, D, P, I, I, I, I, D, I, I, I, I, P, I, P, P]
         L.oracle_prefill_causal.argtypes = [P, I, P, P, D, D, P, I, I, I, I, P, P, I, D, I, I, I, I, P, I, P, P]
         L.oracle_decode.argtypes = [P, I, I64, P]
@@ -211,9 +211,11 @@ def layernorm(x, gamma=None, beta=None, eps: float = 1e-6):
 
 
 def encoder_block(q, k, v, scale, residual, gamma=None, beta=None, eps=1e-6, mask=None):
-    """Attention -> token-major [B,S,H*D] -> + fp32 residual -> LayerNorm.
+    """Attention -> token-major [B,S_q,H*D] -> + fp32 residual -> LayerNorm.
 
-    Returns dict with attn [B,H,S,D], res_out [B,S,H*D], ln_out, mean, rstd (fp64).
+    q [B,H,S_q,D], k/v [B,H,S_kv,D], mask additive [B,1,1,S_kv] (nullable),
+    residual [B,S_q,H*D].  Returns dict with attn [B,H,S_q,D], res_out
+    [B,S_q,H*D], ln_out, mean, rstd (fp64).
     """
     import torch
 
@@ -222,16 +224,21 @@ def encoder_block(q, k, v, scale, residual, gamma=None, beta=None, eps=1e-6, mas
     vr, vt = _raw(v)
     if not (qt == kt == vt):
         raise TypeError("encoder_block: q/k/v must share a dtype")
-    B, H, S, D = qr.shape
+    B, H, Sq, D = qr.shape
+    Skv = kr.shape[2]
+    if kr.shape != (B, H, Skv, D) or vr.shape != kr.shape:
+        raise ValueError("encoder_block: k and v must be [B, H, S_kv, D] with q's B, H and D")
     res = residual.detach().cpu().contiguous().to(torch.float32).numpy() \
         if isinstance(residual, torch.Tensor) else np.ascontiguousarray(residual, dtype=np.float32)
-    m = None if mask is None else _f64(mask).reshape(B, S)
-    attn = np.empty((B, H, S, D))
-    res_out = np.empty((B, S, H * D))
-    ln = np.empty((B, S, H * D))
-    mean = np.empty(B * S)
-    rstd = np.empty(B * S)
-    rc = lib().oracle_encoder_block(_ptr(qr), _ptr(kr), _ptr(vr), qt, _ptr(m), B, H, S, D, float(scale),
+    if res.size != B * Sq * H * D:
+        raise ValueError("encoder_block: residual must be [B, S_q, H*D]")
+    m = None if mask is None else _f64(mask).reshape(B, Skv)
+    attn = np.empty((B, H, Sq, D))
+    res_out = np.empty((B, Sq, H * D))
+    ln = np.empty((B, Sq, H * D))
+    mean = np.empty(B * Sq)
+    rstd = np.empty(B * Sq)
+    rc = lib().oracle_encoder_block(_ptr(qr), _ptr(kr), _ptr(vr), qt, _ptr(m), B, H, Sq, Skv, D, float(scale),
                                     _ptr(res), _ptr(_f64(gamma)), _ptr(_f64(beta)), float(eps), _ptr(attn),
                                     _ptr(res_out), _ptr(ln), _ptr(mean), _ptr(rstd))
     if rc:

@@ -179,32 +179,33 @@ int oracle_layernorm(const double *x, int64_t rows, int N, const double *gamma, 
 }
 
 /*
- * Encoder block: attention (Hq == Hkv == H), the head outputs laid out
- * token-major as [B, S, H*D] (head h owns columns h*D .. h*D+D-1), added to
- * the fp32 residual stream, then LayerNorm over H*D.
- *   attn_out  [B,H,S,D] fp64 (nullable)
- *   res_out   [B,S,H*D] fp64 = residual + attention
- *   ln_out    [B,S,H*D] fp64, mean/rstd [B*S] (nullable)
+ * Encoder block: attention (Hq == Hkv == H; S_q query tokens over S_kv keys,
+ * mask [B, S_kv]), the head outputs laid out token-major as [B, S_q, H*D]
+ * (head h owns columns h*D .. h*D+D-1), added to the fp32 residual stream,
+ * then LayerNorm over H*D.
+ *   attn_out  [B,H,S_q,D] fp64 (nullable)
+ *   res_out   [B,S_q,H*D] fp64 = residual + attention
+ *   ln_out    [B,S_q,H*D] fp64, mean/rstd [B*S_q] (nullable)
  */
 int oracle_encoder_block(const void *q, const void *k, const void *v, int in_dtype, const double *mask,
-                         int B, int H, int S, int D, double scale, const float *residual,
+                         int B, int H, int Sq, int Skv, int D, double scale, const float *residual,
                          const double *gamma, const double *beta, double eps, double *attn_out,
                          double *res_out, double *ln_out, double *mean, double *rstd) {
-    const int64_t n_attn = (int64_t)B * H * S * D;
+    const int64_t n_attn = (int64_t)B * H * Sq * D;
     double *o = attn_out ? attn_out : (double *)malloc(sizeof(double) * n_attn);
     if (!o) return -2;
-    int rc = oracle_sdpa(q, in_dtype, k, in_dtype, v, in_dtype, mask, B, H, H, S, S, D, scale, o, NULL);
+    int rc = oracle_sdpa(q, in_dtype, k, in_dtype, v, in_dtype, mask, B, H, H, Sq, Skv, D, scale, o, NULL);
     if (rc) { if (!attn_out) free(o); return rc; }
     const int N = H * D;
     for (int b = 0; b < B; ++b)
-        for (int s = 0; s < S; ++s)
+        for (int s = 0; s < Sq; ++s)
             for (int h = 0; h < H; ++h)
                 for (int d = 0; d < D; ++d) {
-                    int64_t t = ((int64_t)b * S + s) * N + (int64_t)h * D + d;
-                    res_out[t] = (double)residual[t] + o[(((int64_t)b * H + h) * S + s) * D + d];
+                    int64_t t = ((int64_t)b * Sq + s) * N + (int64_t)h * D + d;
+                    res_out[t] = (double)residual[t] + o[(((int64_t)b * H + h) * Sq + s) * D + d];
                 }
     if (!attn_out) free(o);
-    if (ln_out) rc = oracle_layernorm(res_out, (int64_t)B * S, N, gamma, beta, eps, ln_out, mean, rstd);
+    if (ln_out) rc = oracle_layernorm(res_out, (int64_t)B * Sq, N, gamma, beta, eps, ln_out, mean, rstd);
     return rc;
 }
 

@@ -61,3 +61,18 @@ def test_decode_finite_bias(gpu_lib, D):
     torch.cuda.synchronize()
     ref = oracle.decode_window(case.q, case.k, case.v, case.scale, mask, beg, end, 600)
     assert_close(outw, ref, f"decode window with biases D={D}")
+
+
+def test_encoder_mask_row_shared_by_the_batch(gpu_lib):
+    """A [1,1,1,S_kv] mask (batch stride 0) applies its one row to every
+    batch entry: the same result as the row repeated per batch entry."""
+    case = W.encoder_custom(1420, 3, 2, 200)
+    row = _bias(1421, 1, 200)
+    _say("[bias] encoder B=3 H=2 S=200, one mask row for the batch")
+    d = lambda t: t.to(DEV)
+    shared = gpu_lib.attn_encoder_fwd(d(case.q), d(case.k), d(case.v), case.scale, d(row), want_ln=False)["out"]
+    full = row.expand(3, 1, 1, 200).contiguous()
+    per_b = gpu_lib.attn_encoder_fwd(d(case.q), d(case.k), d(case.v), case.scale, d(full), want_ln=False)["out"]
+    torch.cuda.synchronize()
+    assert torch.equal(shared, per_b)
+    assert_close(shared, oracle.sdpa(case.q, case.k, case.v, case.scale, full), "encoder with a shared mask row")

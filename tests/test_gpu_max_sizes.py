@@ -28,7 +28,7 @@ def _say(msg):
 
 def test_prefill_whole_history_live(gpu_lib):
     case = W.prefill_paged(1300, L_act=256 * 512)
-    rows = torch.cat([case.rows[:10], torch.tensor([0, case.Lq - 1])])
+    rows = torch.cat([case.rows[:64], torch.tensor([0, case.Lq - 1])])
     _say(f"[max] prefill L_act={case.L_act} (all {case.num_blocks} blocks), {len(rows)} tokens x all heads")
     d = lambda t: t.to(DEV)
     out = gpu_lib.attn_prefill_paged(d(case.q), d(case.k_cache), d(case.v_cache), case.k_scale, case.v_scale,

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import prefill_full
 import workloads as W
 from parity import LSE_ABS, assert_close, assert_ln_stats, metrics, to64
 
@@ -276,14 +277,15 @@ def test_prefill_small_full_check(gpu_lib, Hq, Hkv, Lq, nb, bs, L):
 
 
 def test_prefill_full_config_sampled_rows(gpu_lib):
-    case = W.prefill_paged()
-    rows = case.rows[:16]
+    # all 256 sampled token positions x all 32 heads (the workload's stated check)
+    case = prefill_full.case()
+    rows = case.rows
     _say(f"[prefill] full cfg: Lq={case.Lq} Hq={case.Hq} L_act={case.L_act}, checking {len(rows)} tokens x all heads")
-    out = _pre_run(gpu_lib, case)
-    ref = oracle.prefill_paged(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale, case.block_table,
-                               case.L_act, case.scale, rows)
-    got = out[:, rows.to(out.device)]
-    assert_close(got, ref, "prefill full (sampled rows)")
+    out, lse = _pre_run(gpu_lib, case, want_lse=True)
+    ref, rlse = prefill_full.history_ref()
+    r = rows.to(out.device)
+    assert_close(out[:, r], ref, "prefill full (256 sampled rows)")
+    assert metrics(lse[:, r], rlse)["max_abs"] < LSE_ABS
     o2 = _pre_run(gpu_lib, case)
     assert torch.equal(out, o2)
 

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+import prefill_full
 import workloads as W
 from parity import LSE_ABS, assert_close, metrics
 
@@ -61,12 +62,12 @@ def test_prefill_causal_small_full_check(gpu_lib, Hq, Hkv, Lq, nb, bs, L):
 
 
 def test_prefill_causal_full_config_sampled_rows(gpu_lib):
-    case = W.prefill_paged()
-    kc, vc = W.prefill_current_kv(1105, case.Hkv, case.Lq)
-    rows = torch.cat([case.rows[:14], torch.tensor([0, case.Lq - 1])])
+    case = prefill_full.case()
+    kc, vc = prefill_full.current_kv()
+    rows = prefill_full.causal_rows()
     _say(f"[prefill-causal] full cfg Lq={case.Lq} L_act={case.L_act}, {len(rows)} tokens x all heads")
     out, lse = _run(gpu_lib, case, kc, vc, want_lse=True)
-    ref, rlse = _ref(case, kc, vc, rows, lse=True)
+    ref, rlse = prefill_full.causal_ref()
     r = rows.to(DEV)
     assert_close(out[:, r], ref, "prefill causal full (sampled rows)")
     assert metrics(lse[:, r], rlse)["max_abs"] < LSE_ABS

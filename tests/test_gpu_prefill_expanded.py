@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+import prefill_full
 import workloads as W
 from parity import LSE_ABS, assert_close, metrics
 
@@ -53,14 +54,17 @@ def test_expanded_small_full_check(gpu_lib, Hq, Hkv, Lq, nb, bs, L):
 
 
 def test_expanded_full_config_sampled_rows(gpu_lib):
-    case = W.prefill_paged()
-    rows = case.rows[:16]
+    # the bench's entry point at the full shape: all 256 sampled token
+    # positions x all 32 heads against the oracle, bit for bit the plain path
+    case = prefill_full.case()
+    rows = case.rows
     _say(f"[expanded] full cfg: Lq={case.Lq} Hq={case.Hq} L_act={case.L_act}, {len(rows)} tokens x all heads")
-    plain, exp = _both(gpu_lib, case)
-    ref = oracle.prefill_paged(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale, case.block_table,
-                               case.L_act, case.scale, rows)
-    assert_close(exp[:, rows.to(exp.device)], ref, "expanded prefill full (sampled rows)")
-    assert torch.equal(exp, plain)
+    (po, pl), (eo, el) = _both(gpu_lib, case, want_lse=True)
+    ref, rlse = prefill_full.history_ref()
+    r = rows.to(eo.device)
+    assert_close(eo[:, r], ref, "expanded prefill full (256 sampled rows)")
+    assert metrics(el[:, r], rlse)["max_abs"] < LSE_ABS
+    assert torch.equal(eo, po) and torch.equal(el, pl)
 
 
 def test_expanded_poisoned_tail_ignored(gpu_lib):
@@ -159,12 +163,13 @@ def test_expanded_many_kv_heads(gpu_lib):
 
 
 def test_causal_expanded_full_config(gpu_lib):
-    # the causal call over tile images at the full prefill shape (the bench's):
-    # bit for bit the converting path, and sampled rows against the oracle
+    # the causal call over tile images at the full prefill shape: bit for bit
+    # the converting path, and all 256 sampled token positions (plus the
+    # first and last) x all heads against the oracle
     taa = gpu_lib
-    case = W.prefill_paged()
-    kc, vc = (t.to(DEV) for t in W.prefill_current_kv(1105, case.Hkv, case.Lq))
-    rows = torch.cat([case.rows[:6], torch.tensor([0, case.Lq - 1])])
+    case = prefill_full.case()
+    kc, vc = (t.to(DEV) for t in prefill_full.current_kv())
+    rows = prefill_full.causal_rows()
     d = lambda t: t.to(DEV)
     args = (d(case.q), d(case.k_cache), d(case.v_cache), case.k_scale, case.v_scale, d(case.block_table), case.L_act,
             kc, vc, case.scale, case.G)
@@ -173,6 +178,7 @@ def test_causal_expanded_full_config(gpu_lib):
     eo, el = taa.attn_prefill_paged_causal_expanded(*args, want_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(eo, po) and torch.equal(el, pl)
-    ref = oracle.prefill_causal(case.q, case.k_cache, case.v_cache, case.k_scale, case.v_scale, case.block_table,
-                                case.L_act, kc.cpu(), vc.cpu(), case.scale, rows)
-    assert_close(eo[:, rows.to(DEV)], ref, "causal expanded full (sampled rows)")
+    ref, rlse = prefill_full.causal_ref()
+    r = rows.to(DEV)
+    assert_close(eo[:, r], ref, "causal expanded full (sampled rows)")
+    assert metrics(el[:, r], rlse)["max_abs"] < LSE_ABS

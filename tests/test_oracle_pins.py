@@ -253,6 +253,77 @@ def test_encoder_block_matches_torch_chain():
     assert _relmax(out["ln_out"], ln.numpy()) < 1e-12
 
 
+def test_encoder_block_queries_and_keys_of_different_lengths():
+    """S_q != S_kv: attention of S_q query tokens over S_kv keys, then the
+    residual stream of S_q rows, against the torch fp64 chain."""
+    g = torch.Generator().manual_seed(15)
+    B, H, Sq, Skv, D = 2, 2, 7, 12, 8
+    q = _rand(g, B, H, Sq, D).to(torch.bfloat16)
+    k, v = (_rand(g, B, H, Skv, D).to(torch.bfloat16) for _ in range(2))
+    res = torch.randn(B, Sq, H * D, generator=g)
+    gamma, beta = torch.rand(H * D, generator=g) + 0.5, torch.randn(H * D, generator=g)
+    mask = torch.zeros(B, 1, 1, Skv)
+    mask[0, ..., 9:] = -math.inf
+    out = oracle.encoder_block(q, k, v, 0.4, res, gamma, beta, 1e-5, mask)
+    attn = _torch_sdpa64(q, k, v, 0.4, mask.to(torch.float64))
+    x = res.to(torch.float64) + torch.from_numpy(attn).permute(0, 2, 1, 3).reshape(B, Sq, H * D)
+    ln = torch.nn.functional.layer_norm(x, (H * D,), gamma.double(), beta.double(), 1e-5)
+    assert out["attn"].shape == (B, H, Sq, D)
+    assert _relmax(out["attn"], attn) < 1e-12
+    assert np.max(np.abs(out["res_out"] - x.numpy())) < 1e-13
+    assert _relmax(out["ln_out"], ln.numpy()) < 1e-12
+
+
+def _complex_rotate(x, theta, pairing):
+    """x [..., S, D] fp64 with each lane pair taken as one complex number and
+    multiplied by e^{i theta[s, k]} (torch complex arithmetic)."""
+    D = x.shape[-1]
+    if pairing == "half":
+        z = torch.complex(x[..., : D // 2], x[..., D // 2:])
+    else:
+        z = torch.view_as_complex(x.reshape(*x.shape[:-1], D // 2, 2).contiguous())
+    r = z * torch.polar(torch.ones_like(theta), theta)
+    if pairing == "half":
+        return torch.cat([r.real, r.imag], dim=-1)
+    return torch.view_as_real(r).reshape(x.shape)
+
+
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+@pytest.mark.parametrize("Sq,Skv", [(9, 9), (6, 11)])
+def test_encoder_block_rope_matches_complex_rotation_chain(pairing, Sq, Skv):
+    """The encoder block on rotated q/k: query token i turns by table row i and
+    key j by row j (the tables hold more rows than either length), rotation as
+    complex multiplication, then torch fp64 SDPA, the token-major residual add
+    and torch LayerNorm."""
+    g = torch.Generator().manual_seed(31 + Sq)
+    B, H, D, rows = 2, 3, 8, 14
+    q = _rand(g, B, H, Sq, D).to(torch.bfloat16)
+    k, v = (_rand(g, B, H, Skv, D).to(torch.bfloat16) for _ in range(2))
+    res = torch.randn(B, Sq, H * D, generator=g)
+    gamma, beta = torch.rand(H * D, generator=g) + 0.5, torch.randn(H * D, generator=g)
+    mask = torch.zeros(B, 1, 1, Skv)
+    mask[1, ..., Skv - 2:] = -math.inf
+    th = _angles(rows, D // 2, 32)
+    out = oracle.encoder_block_rope(q, k, v, 0.35, res, gamma, beta, 1e-6, mask, torch.cos(th), torch.sin(th),
+                                    pairing)
+    qr = _complex_rotate(q.double(), th[:Sq], pairing)
+    kr = _complex_rotate(k.double(), th[:Skv], pairing)
+    attn = torch.nn.functional.scaled_dot_product_attention(qr, kr, v.double(), attn_mask=mask.double(),
+                                                            scale=0.35)
+    x = res.double() + attn.permute(0, 2, 1, 3).reshape(B, Sq, H * D)
+    ln = torch.nn.functional.layer_norm(x, (H * D,), gamma.double(), beta.double(), 1e-6)
+    assert _relmax(out["attn"], attn.numpy()) < 1e-12
+    assert np.max(np.abs(out["res_out"] - x.numpy())) < 1e-12
+    assert _relmax(out["ln_out"], ln.numpy()) < 1e-12
+    # a plausible slip, the key rows of the table taken from the query rows'
+    # end, is caught: the result moves far beyond round-off
+    if Sq != Skv:
+        wrong = _complex_rotate(k.double(), th[rows - Skv:], pairing)
+        a2 = torch.nn.functional.scaled_dot_product_attention(qr, wrong, v.double(), attn_mask=mask.double(),
+                                                              scale=0.35)
+        assert _relmax(out["attn"], a2.numpy()) > 1e-3
+
+
 # ----------------------------------------------------------------------------- paged prefill
 
 

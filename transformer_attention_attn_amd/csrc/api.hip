@@ -227,7 +227,10 @@ int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
       if (a->out_stride[i] < 0 || a->out_stride[i] % 8) return ATTN_ERR_INVALID_ARG;
   }
   if (a->residual && (!aligned16(a->residual) || !aligned16(a->residual_out))) return ATTN_ERR_INVALID_ARG;
-  if (a->mask && (a->mask_stride_b < a->S_kv && a->B > 1)) return ATTN_ERR_INVALID_ARG;
+  // per-batch mask rows must not overlap; stride 0 shares one row across the batch
+  if (a->mask && (a->mask_stride_b < 0 || (a->B > 1 && a->mask_stride_b != 0 && a->mask_stride_b < a->S_kv)))
+    return ATTN_ERR_INVALID_ARG;
+  if (a->mask && (reinterpret_cast<uintptr_t>(a->mask) & 3u)) return ATTN_ERR_INVALID_ARG;
   const int64_t hidden = (int64_t)a->H * a->D;
   if (a->ln_out) {
     if (a->ln_dtype != ATTN_BF16 && a->ln_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
