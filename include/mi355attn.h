@@ -177,6 +177,28 @@ ATTN_API int attn_decode_gqa(const void *q, const void *k, const void *v, const 
                     void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_decode_gqa without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same operation, operands,
+ * requirements and result bits as attn_decode_gqa; the chunk partials go to
+ * a device array of ATTN_DECODE_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU, held until the process ends.  The call allocates nothing.
+ *   - A problem whose attn_decode_gqa_workspace_size() exceeds
+ *     ATTN_DECODE_NOALLOC_SCRATCH_BYTES returns ATTN_ERR_WORKSPACE (use
+ *     attn_decode_gqa with a workspace of that size instead).
+ *   - Every call on one GPU uses that GPU's one array: calls that can overlap
+ *     on the same GPU (two streams, or two host threads) race on it and must
+ *     be serialised by the caller.  The array's contents on entry are never
+ *     read as state.
+ *   - The first call on each device looks the array up (hipGetSymbolAddress);
+ *     a failure there returns ATTN_ERR_HIP.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ATTN_API int attn_decode_gqa_noalloc(const void *q, const void *k, const void *v, const float *attn_mask,
+                                     float softmax_scale, int num_kv_groups, int B, int Hq, int Hkv, int S_ctx,
+                                     int D, void *out, hipStream_t stream);
+
+/*
  * GQA single-token decode over a per-sequence key range (sliding-window
  * layers).
  *

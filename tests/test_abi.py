@@ -36,7 +36,7 @@ def test_header_declares_the_four_entry_points():
               "attn_prefill_paged_causal", "attn_prefill_paged_causal_workspace_size",
               "attn_prefill_paged_expanded", "attn_prefill_paged_expanded_workspace_size",
               "attn_prefill_paged_causal_expanded", "attn_prefill_paged_causal_expanded_workspace_size",
-              "attn_encoder_rope_workspace_size", "attn_status_string", "attn_version"):
+              "attn_encoder_rope_workspace_size", "attn_status_string", "attn_version", "attn_decode_gqa_noalloc"):
         assert n in names
 
 
@@ -313,3 +313,35 @@ def test_encoder_rope_workspace_size():
     assert taa.attn_encoder_rope_workspace_size(1, 16, 2048, 64) == 16 * 2048 * 64 * 2
     assert taa.attn_encoder_rope_workspace_size(2, 3, 100, 64, torch.float32) == 2 * 3 * 100 * 64 * 4
     assert taa.attn_encoder_rope_workspace_size(0, 3, 100, 64) == 0
+
+
+def _dec_na(**kw):
+    a = _dec(**kw)
+    return a[:12] + (None,)  # no workspace arguments
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), taa.ATTN_ERR_INVALID_ARG),
+    (dict(out=None), taa.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=15), taa.ATTN_ERR_INVALID_ARG),
+    (dict(D=128), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(G=3, Hq=24), taa.ATTN_ERR_UNSUPPORTED),
+    (dict(k=BAD), taa.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), taa.ATTN_ERR_INVALID_ARG),
+    # partials beyond the library's scratch: 8 x 64 heads x 64 chunks x (512 + 2) x 4 B = 67 MB
+    (dict(D=512, Hq=64, Hkv=8, G=8), taa.ATTN_ERR_WORKSPACE),
+    (dict(S=131072), taa.ATTN_ERR_WORKSPACE),
+])
+def test_decode_noalloc_validation(lib, kw, expect):
+    """Every argument is checked, and the scratch limit enforced, before the
+    device is touched (these calls run without a GPU)."""
+    assert lib.attn_decode_gqa_noalloc(*_dec_na(**kw)) == expect
+
+
+def test_decode_noalloc_limit_matches_the_header(lib):
+    text = open(HEADER).read()
+    assert "#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in text
+    assert taa.DECODE_NOALLOC_SCRATCH_BYTES == 32 << 20
+    # the bench's decode (8 x 16 heads, 4096 keys, D 256) and the D 512 one fit
+    assert taa.attn_decode_gqa_workspace_size(8, 16, 4096, 256) <= taa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert taa.attn_decode_gqa_workspace_size(8, 16, 4096, 512) <= taa.DECODE_NOALLOC_SCRATCH_BYTES

@@ -81,6 +81,8 @@ def load(path: str | None = None):
     L.attn_decode_gqa_workspace_size.restype = Z
     L.attn_decode_gqa.argtypes = [P, P, P, P, F, I, I, I, I, I, I, P, P, Z, P]
     L.attn_decode_gqa.restype = I
+    L.attn_decode_gqa_noalloc.argtypes = [P, P, P, P, F, I, I, I, I, I, I, P, P]
+    L.attn_decode_gqa_noalloc.restype = I
     L.attn_decode_gqa_window_workspace_size.argtypes = [I, I, I, I, I]
     L.attn_decode_gqa_window_workspace_size.restype = Z
     L.attn_decode_gqa_window.argtypes = [P, P, P, P, P, P, I, F, I, I, I, I, I, I, P, P, Z, P]
@@ -317,6 +319,25 @@ def attn_decode_gqa(q, k, v, attn_mask, softmax_scale: float, num_kv_groups: int
                                     int(num_kv_groups), B, Hq, Hkv, S_ctx, D, _ptr(out), _ptr(workspace),
                                     workspace.numel(), _stream(stream))
     _check(rc, "attn_decode_gqa")
+    return out
+
+
+# bytes of the library's device scratch behind attn_decode_gqa_noalloc
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def attn_decode_gqa_noalloc(q, k, v, attn_mask, softmax_scale: float, num_kv_groups: int, *, out, stream=None):
+    """attn_decode_gqa without a workspace: the partials go to the library's
+    own device scratch (DECODE_NOALLOC_SCRATCH_BYTES per GPU; calls that can
+    overlap on one GPU race on it).  `out` [B,Hq,1,D] bf16 is required: this
+    call allocates nothing."""
+    if out is None:
+        raise ValueError("out is required: attn_decode_gqa_noalloc allocates nothing")
+    B, Hq, Hkv, S_ctx, D = _decode_shapes(q, k, v, attn_mask, out, None)
+    _need_cuda(q, k, v, attn_mask, out)
+    rc = load().attn_decode_gqa_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(attn_mask), float(softmax_scale),
+                                        int(num_kv_groups), B, Hq, Hkv, S_ctx, D, _ptr(out), _stream(stream))
+    _check(rc, "attn_decode_gqa_noalloc")
     return out
 
 

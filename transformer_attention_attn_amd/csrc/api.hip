@@ -8,6 +8,8 @@
 
 using namespace mi355;
 
+static_assert(kDecodeScratchBytes == ATTN_DECODE_NOALLOC_SCRATCH_BYTES, "scratch size stated in the header");
+
 namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -45,10 +47,9 @@ int64_t decode_chunks(int S_ctx, int max_keys, bool ranged) {
   return n < all ? n : all;
 }
 
-int decode_common(const void *q, const void *k, const void *v, const float *attn_mask, const int32_t *key_begin,
-                  const int32_t *key_end, int max_keys, bool ranged, float softmax_scale, int num_kv_groups, int B,
-                  int Hq, int Hkv, int S_ctx, int D, void *out, void *workspace, size_t workspace_bytes,
-                  hipStream_t stream) {
+// Checks of the decode's operands (everything but the workspace).
+int decode_check(const void *q, const void *k, const void *v, const float *attn_mask, float softmax_scale,
+                 int num_kv_groups, int B, int Hq, int Hkv, int S_ctx, int D, const void *out) {
   if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_ctx <= 0 || D <= 0 || num_kv_groups <= 0) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)Hkv * num_kv_groups != Hq) return ATTN_ERR_INVALID_ARG;
@@ -58,6 +59,15 @@ int decode_common(const void *q, const void *k, const void *v, const float *attn
   if (!finite(softmax_scale)) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
   if (attn_mask && !aligned16(attn_mask)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+int decode_common(const void *q, const void *k, const void *v, const float *attn_mask, const int32_t *key_begin,
+                  const int32_t *key_end, int max_keys, bool ranged, float softmax_scale, int num_kv_groups, int B,
+                  int Hq, int Hkv, int S_ctx, int D, void *out, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  const int rc = decode_check(q, k, v, attn_mask, softmax_scale, num_kv_groups, B, Hq, Hkv, S_ctx, D, out);
+  if (rc != ATTN_OK) return rc;
   const int64_t n_chunks = decode_chunks(S_ctx, max_keys, ranged);
   const size_t need = ranged ? attn_decode_gqa_window_workspace_size(B, Hq, S_ctx, max_keys, D)
                              : attn_decode_gqa_workspace_size(B, Hq, S_ctx, D);
@@ -342,6 +352,20 @@ int attn_decode_gqa(const void *q, const void *k, const void *v, const float *at
                     size_t workspace_bytes, hipStream_t stream) {
   return decode_common(q, k, v, attn_mask, nullptr, nullptr, S_ctx, false, softmax_scale, num_kv_groups, B, Hq,
                        Hkv, S_ctx, D, out, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_gqa_noalloc(const void *q, const void *k, const void *v, const float *attn_mask,
+                            float softmax_scale, int num_kv_groups, int B, int Hq, int Hkv, int S_ctx, int D,
+                            void *out, hipStream_t stream) {
+  // every argument is checked before the device is touched
+  const int rc = decode_check(q, k, v, attn_mask, softmax_scale, num_kv_groups, B, Hq, Hkv, S_ctx, D, out);
+  if (rc != ATTN_OK) return rc;
+  const size_t need = attn_decode_gqa_workspace_size(B, Hq, S_ctx, D);
+  if (need == 0 || need > kDecodeScratchBytes) return ATTN_ERR_WORKSPACE;
+  void *scratch = nullptr;
+  if (decode_scratch(stream, &scratch) != hipSuccess) return ATTN_ERR_HIP;
+  return decode_common(q, k, v, attn_mask, nullptr, nullptr, S_ctx, false, softmax_scale, num_kv_groups, B, Hq,
+                       Hkv, S_ctx, D, out, scratch, kDecodeScratchBytes, stream);
 }
 
 int attn_decode_gqa_window(const void *q, const void *k, const void *v, const float *attn_mask,

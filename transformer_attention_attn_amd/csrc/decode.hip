@@ -31,6 +31,8 @@
 //          (m, l in log2 units, unnormalised o) goes to the workspace.
 // Combine kernel, per (b, query head): M = max m_c, L = sum 2^(m_c-M) l_c,
 //   o = sum 2^(m_c-M) o_c / L over the chunks in index order (deterministic).
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -362,6 +364,38 @@ hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
     case 512: return launch_decode_d<512>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Scratch of the allocation-free decode entry point: the chunk partials live
+// in this file-scope device array instead of a caller workspace.  Each GPU
+// holds its own copy at its own address (found once per device with
+// hipGetSymbolAddress; in host code the array's name is only a stand-in and
+// is never passed to a kernel).  Every call on one GPU shares it.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(hipStream_t stream, void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *per_device[kMaxDevices];
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (e2 != hipSuccess) return e2;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 int decode_chunk_keys() { return kDecChunk; }

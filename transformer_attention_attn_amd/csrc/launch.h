@@ -88,6 +88,10 @@ int prefill_key_tile();
 int prefill_rows_per_block();
 int64_t prefill_tile_image_bytes();  // bytes of one tile's K and V images
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
+// Bytes of the decode's file-scope device scratch, and its address on the
+// device of `stream` (looked up once per device).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(hipStream_t stream, void **ptr);
 int decode_chunk_keys();
 int decode_max_groups();
 hipError_t launch_res_ln(const ResLnLaunch &a, hipStream_t stream);
