@@ -2,8 +2,10 @@
 """Benchmark of the flash-attention hot path on one MI355X.
 
 One step = one pass over every kernel of the path, each on its workload:
-  * encoder block: V-JEPA2 ViT-L attention (B=1, 16 heads, 2048 tokens, D=64,
-    bf16) + residual add into the fp32 [2048,1024] stream + LayerNorm;
+  * encoder blocks: V-JEPA2 ViT-L attention (B=1, 16 heads, 2048 tokens,
+    D=64) and DINOv3 ViT-L/16 at 448 px (B=2, 16 heads, 789 tokens: ragged
+    tiles), bf16, each + residual add into the fp32 [B,S,1024] stream +
+    LayerNorm;
   * GQA decode: B=8, 16 query / 8 KV heads, head_dim 256, S_ctx 4096,
     ragged lengths len_b ~ U{1..4096};
   * paged FP8 prefill: 4096 query tokens x 32 heads over 2 KV heads, D=256,
@@ -13,11 +15,14 @@ One step = one pass over every kernel of the path, each on its workload:
 All inputs are synthetic, seeded, and resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is the step's attention throughput (QK^T + PV
-FLOPs of the three attention calls over the step time); `parts` gives each
-kernel's own metric (TFLOP/s and % of the bf16 MFMA peak, or GB/s and % of
-HBM peak) from HIP events recorded on the stream the kernels run on;
-`roofline` is the dominant call's (the prefill: its two kernels).  `cpu_baseline` times the
-fp64 oracle on a bounded sample of the prefill workload on the host cores.
+FLOPs of the four attention calls over the step time); `parts` gives each
+call's own metric (TFLOP/s and % of the bf16 MFMA peak, or GB/s and % of HBM
+peak) from HIP events recorded on the stream the kernels run on, with
+min/median/mean/P90/max; each encoder block also gets its attention alone
+(epilogue pointers null) and the softmax's VALU bound; `roofline` is the
+dominant call's (the prefill: its two kernels).  `cpu_baseline` times the
+fp64 oracle on the host cores: workloads 1-4 whole, the prefill on its 256
+sampled tokens x 32 heads.
 """
 from __future__ import annotations
 
@@ -119,22 +124,60 @@ class Timer:
         return [s.elapsed_time(e) for s, e in self.pairs]
 
 
-def cpu_baseline(pre, n_rows: int):
-    """Time the fp64 oracle on n_rows query tokens x all heads of the prefill."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cases, pre, n_rows: int, reps: int = 3):
+    """The fp64 oracle on the host cores: the tiny, V-JEPA2 and DINOv3 encoder
+    blocks and the decode computed whole (median of `reps` runs each), the
+    prefill on its first n_rows sampled tokens x all heads (one run).  Input
+    generation is outside the timings."""
     import oracle
 
     oracle.build()
-    rows = pre.rows[:n_rows]
     cores = len(os.sched_getaffinity(0))
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    per = {}
+
+    def timed(fn, n):
+        ts = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    for key, c in cases.items():
+        if key == "gemma_gqa_decode_d256_ctx4096":
+            dt = timed(lambda: oracle.sdpa(c.q, c.k, c.v, c.scale, c.mask), reps)
+            f = 4 * int(c.lens.sum()) * c.Hq * c.D
+        else:
+            dt = timed(lambda: oracle.encoder_block(c.q, c.k, c.v, c.scale, c.residual, c.gamma, c.beta, c.eps,
+                                                    c.mask), reps)
+            f = acc.encoder_flops(c.B, c.H, c.S, c.S, c.D)
+        per[key] = {"s": dt, "gflops": f / dt / 1e9, "scope": "whole output", "runs": reps}
+    rows = pre.rows[:n_rows]
     t0 = time.perf_counter()
     oracle.prefill_paged(pre.q, pre.k_cache, pre.v_cache, pre.k_scale, pre.v_scale, pre.block_table, pre.L_act,
                          pre.scale, rows)
     dt = time.perf_counter() - t0
-    flops = acc.prefill_flops(len(rows), pre.Hq, pre.L_act, pre.D)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, cores), "kind": "oracle",
-            "sample": f"paged FP8 prefill, {len(rows)} query tokens x {pre.Hq} heads x {pre.L_act} keys "
-                      f"(fp64 C oracle incl. KV decode), {dt:.1f} s wall"}
+    f = acc.prefill_flops(len(rows), pre.Hq, pre.L_act, pre.D)
+    per["paged_fp8_prefill_q4096_hist120000"] = {
+        "s": dt, "gflops": f / dt / 1e9, "rows_per_s": len(rows) * pre.Hq / dt, "runs": 1,
+        "scope": f"{len(rows)} sampled tokens x {pre.Hq} heads x {pre.L_act} keys (of {pre.Lq} tokens; "
+                 f"all {pre.Lq} would take about {dt * pre.Lq / len(rows):.0f} s, extrapolated)"}
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, cores), "kind": "oracle",
+            "sample": f"fp64 C oracle (OpenMP over rows): paged FP8 prefill on {len(rows)} sampled query tokens x "
+                      f"{pre.Hq} heads x {pre.L_act} keys incl. the KV decode ({dt:.1f} s) = value; workloads "
+                      f"1-4 whole in per_config",
+            "cpu_model": _cpu_model(), "per_config": per}
 
 
 def time_next_workloads(taa, dev, flush, pre_dev, reps: int = 20):
@@ -320,18 +363,80 @@ def pcp_shapes(reps: int = 10) -> None:
 
 def _short(name: str) -> str:
     """Kernel family name from a demangled rocprofv3 kernel name."""
-    for k in ("prefill_paged_kernel", "prefill_tile_images_kernel", "encoder_fwd_kernel", "res_ln_kernel",
-              "decode_split_kernel", "decode_combine_kernel", "copyBuffer"):
+    for k in ("prefill_paged_kernel", "prefill_tile_images_kernel", "prefill_current_kernel", "encoder_fwd_kernel",
+              "res_ln_kernel", "rope_k_kernel", "decode_split_kernel", "decode_combine_kernel", "copyBuffer"):
         if k in name:
             return k
     return None
 
 
+def _grid(row: dict) -> str:
+    """Launch grid of a rocprofv3 CSV row in work-items (the kernel trace gives
+    Grid_Size_X/Y/Z, the counter collection their product as Grid_Size)."""
+    if row.get("Grid_Size") not in (None, ""):
+        return str(int(float(row["Grid_Size"])))
+    n = 1
+    for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"):
+        if row.get(k) not in (None, ""):
+            n *= int(float(row[k]))
+    return str(n)
+
+
+def _pct(xs, q):
+    xs = sorted(xs)
+    i = min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))
+    return xs[i]
+
+
+def _launches(rows):
+    """This library's launches of one rocprofv3 CSV (one row per dispatch, or
+    one per (dispatch, counter)), in dispatch order, each with its role: an
+    encoder launch followed by a LayerNorm launch belongs to a fused block,
+    any other encoder launch is attention alone."""
+    by_id = {}
+    for r in rows:
+        f = _short(r["Kernel_Name"])
+        if not f:
+            continue
+        d = int(r["Dispatch_Id"])
+        e = by_id.setdefault(d, {"family": f, "grid": _grid(r), "kernel": r["Kernel_Name"], "row": r, "value": 0.0})
+        if "Counter_Value" in r:
+            e["value"] += float(r["Counter_Value"])
+    ordered = [by_id[d] for d in sorted(by_id)]
+    ours = [e for e in ordered if e["family"] != "copyBuffer"]
+    for i, e in enumerate(ours):
+        nxt = ours[i + 1]["family"] if i + 1 < len(ours) else None
+        e["role"] = e["family"]
+        if e["family"] == "encoder_fwd_kernel":
+            e["role"] = "encoder_fwd_kernel" if nxt == "res_ln_kernel" else "encoder_fwd_kernel(alone)"
+    return ordered
+
+
+# Workloads of the step as they appear in a kernel trace: the encoder blocks in
+# step order (V-JEPA2 first), then the decode and the prefill.
+PROFILE_WORKLOADS = [
+    ("encoder_fwd_kernel__vjepa2_s2048_block", "vjepa2_encoder_block_s2048", 0),
+    ("encoder_fwd_kernel__dinov3_s789_block", "dinov3_encoder_block_s789", 1),
+    ("decode_gqa__gemma_d256_b8_ctx4096", "gemma_gqa_decode_d256_ctx4096", None),
+    ("prefill_paged_kernel__paged_fp8_prefill_q4096_hist120000", "paged_fp8_prefill_q4096_hist120000", None),
+]
+
+PROFILE_COMMANDS = """cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace -o bench -- python3 <repo>/bench.py --steps 10 --warmup 3 --cpu-rows 0 --no-next
+cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/FETCH_SIZE -o bench -- python3 <repo>/bench.py --steps 2 --warmup 1 --cpu-rows 0 --no-next
+cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/WRITE_SIZE -o bench -- python3 <repo>/bench.py --steps 2 --warmup 1 --cpu-rows 0 --no-next
+cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/FETCH_SIZE_copy -o copy -- python3 <repo>/bench.py --copy-calibration
+cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/WRITE_SIZE_copy -o copy -- python3 <repo>/bench.py --copy-calibration
+python3 <repo>/bench.py --summarize <out>      # writes profiles/traffic.json and these summaries"""
+
+
 def summarize(prof_dir: str) -> None:
     """Turn the rocprofv3 CSV output of the profiling commands (kernel trace in
     <dir>/trace, FETCH_SIZE / WRITE_SIZE passes of the bench in <dir>/<C> and of
-    --copy-calibration in <dir>/<C>_copy) into profiles/traffic.json, and print
-    the per-kernel duration and traffic tables.  Reads CSV only; no GPU."""
+    --copy-calibration in <dir>/<C>_copy) into profiles/traffic.json, and, when
+    <dir>/bench.json holds the bench line of the same lease, into one markdown
+    summary per workload of the step under profiles/.  Launches are grouped by
+    role (see _launches) and launch grid (the two encoder workloads share one
+    kernel).  Reads CSV and JSON only; no GPU."""
     import csv
     import glob
 
@@ -341,42 +446,50 @@ def summarize(prof_dir: str) -> None:
             raise SystemExit(f"summarize: no {pattern} under {prof_dir}")
         return hits[0]
 
-    def per_dispatch(path):
-        vals = {}
-        for r in csv.DictReader(open(path)):
-            key = (r["Dispatch_Id"], r["Kernel_Name"])
-            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
-        fam = {}
-        for (_, name), v in vals.items():
-            if _short(name):
-                fam.setdefault(_short(name), []).append(v)
-        return {k: statistics.fmean(v) for k, v in fam.items()}
+    def groups(path, field):
+        g = {}
+        for e in _launches(list(csv.DictReader(open(path)))):
+            key = (e.get("role", e["family"]), e["grid"])
+            g.setdefault(key, {"kernel": e["kernel"], "vals": [], "first": int(e["row"]["Dispatch_Id"])})
+            g[key]["vals"].append(field(e))
+        return g
 
-    stats = {}
-    for r in csv.DictReader(open(one("trace/*kernel_stats.csv"))):
-        if not _short(r["Name"]):  # not one of this library's kernels (e.g. the cache flush)
-            continue
-        if _short(r["Name"]) in stats:
-            raise SystemExit(f"summarize: two kernels of family {_short(r['Name'])} in the trace; profile the "
-                             "step alone (bench.py --no-next)")
-        stats[_short(r["Name"])] = {"kernel": r["Name"], "calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
-                                    "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
+    trace = groups(one("trace/*kernel_trace.csv"),
+                   lambda e: float(e["row"]["End_Timestamp"]) - float(e["row"]["Start_Timestamp"]))
+    roles = {}
+    for (r, gr) in trace:
+        roles.setdefault(r, []).append(gr)
+    label = {(r, gr): (r if len(roles[r]) == 1 else f"{r}@{gr}") for (r, gr) in trace}
+
     cal = {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        kib = per_dispatch(one(f"{c}_copy/*counter_collection.csv"))["copyBuffer"]
-        cal[c] = kib * 1024 / COPY_BYTES
-    fetch = per_dispatch(one("FETCH_SIZE/*counter_collection.csv"))
-    write = per_dispatch(one("WRITE_SIZE/*counter_collection.csv"))
+        d = groups(one(f"{c}_copy/*counter_collection.csv"), lambda e: e["value"])
+        # the 1 GiB copies: the copyBuffer launches of the largest grid
+        copies = sorted((int(gr), statistics.fmean(v["vals"])) for (r, gr), v in d.items() if r == "copyBuffer")
+        cal[c] = copies[-1][1] * 1024 / COPY_BYTES
+    fetch = {k: statistics.fmean(v["vals"]) for k, v in
+             groups(one("FETCH_SIZE/*counter_collection.csv"), lambda e: e["value"]).items()}
+    write = {k: statistics.fmean(v["vals"]) for k, v in
+             groups(one("WRITE_SIZE/*counter_collection.csv"), lambda e: e["value"]).items()}
     kernels = {}
-    for k, st in stats.items():
-        if k == "copyBuffer" or k not in fetch or k not in write:
+    for key, st in sorted(trace.items(), key=lambda kv: kv[1]["first"]):
+        if key[0] == "copyBuffer":
             continue
-        kernels[k] = {"kernel": st["kernel"], "fetch_kib_raw": fetch[k], "write_kib_raw": write[k],
-                      "hbm_bytes_per_launch": int(fetch[k] * 1024 / cal["FETCH_SIZE"] + write[k] * 1024 / cal["WRITE_SIZE"]),
-                      "avg_duration_ns": st["avg_ns"]}
+        ns = st["vals"]
+        entry = {"kernel": st["kernel"], "role": key[0], "grid_work_items": int(key[1]), "launches": len(ns),
+                 "first_dispatch": st["first"],
+                 "avg_duration_ns": statistics.fmean(ns), "min_duration_ns": min(ns),
+                 "median_duration_ns": statistics.median(ns), "p90_duration_ns": _pct(ns, 0.9),
+                 "max_duration_ns": max(ns)}
+        if key in fetch and key in write:
+            entry.update({"fetch_kib_raw": fetch[key], "write_kib_raw": write[key],
+                          "hbm_bytes_per_launch": int(fetch[key] * 1024 / cal["FETCH_SIZE"]
+                                                      + write[key] * 1024 / cal["WRITE_SIZE"])})
+        kernels[label[key]] = entry
     out = {"source_hash": kernel_source_hash(),
-           "note": "rocprofv3 FETCH_SIZE/WRITE_SIZE (KiB per dispatch, L2 <-> memory fabric) divided by the ratio "
-                   "the same counter reads for a 1 GiB device copy",
+           "note": "rocprofv3 kernel trace (per-launch durations) and FETCH_SIZE/WRITE_SIZE (KiB per dispatch, "
+                   "L2 <-> memory fabric) divided by the ratio the same counter reads for a 1 GiB device copy; "
+                   "launches grouped by role and grid (work-items)",
            "calibration": {"copy_bytes": COPY_BYTES, "fetch_ratio": cal["FETCH_SIZE"], "write_ratio": cal["WRITE_SIZE"]},
            "kernels": kernels}
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -385,13 +498,124 @@ def summarize(prof_dir: str) -> None:
         f.write("\n")
     print(f"wrote {path} (sources {out['source_hash']}; copy calibration fetch x{cal['FETCH_SIZE']:.4f}, "
           f"write x{cal['WRITE_SIZE']:.4f})")
-    print("\n| kernel | calls | avg (us) | min (us) | max (us) |\n|---|---|---|---|---|")
-    for k, st in sorted(stats.items(), key=lambda kv: -kv[1]["avg_ns"] * kv[1]["calls"]):
-        print(f"| `{st['kernel']}` | {st['calls']} | {st['avg_ns'] / 1e3:.2f} | {st['min_ns'] / 1e3:.2f} | "
-              f"{st['max_ns'] / 1e3:.2f} |")
-    print("\n| kernel | FETCH_SIZE raw (KiB) | WRITE_SIZE raw (KiB) | scaled bytes / launch |\n|---|---|---|---|")
-    for k, v in kernels.items():
-        print(f"| {k} | {v['fetch_kib_raw']:.1f} | {v['write_kib_raw']:.1f} | {v['hbm_bytes_per_launch'] / 1e6:.1f} MB |")
+    bench_path = os.path.join(prof_dir, "bench.json")
+    if os.path.exists(bench_path):
+        _write_profiles(json.load(open(bench_path)), kernels, cal)
+
+
+def _kernel_rows(ks):
+    t = ["| kernel | launches | min (us) | median (us) | mean (us) | P90 (us) | max (us) | HBM bytes / launch |",
+         "|---|---|---|---|---|---|---|---|"]
+    for name, e in ks:
+        hb = e.get("hbm_bytes_per_launch")
+        t.append(f"| `{name}` | {e['launches']} | {e['min_duration_ns'] / 1e3:.2f} | {e['median_duration_ns'] / 1e3:.2f} | "
+                 f"{e['avg_duration_ns'] / 1e3:.2f} | {e['p90_duration_ns'] / 1e3:.2f} | "
+                 f"{e['max_duration_ns'] / 1e3:.2f} | {'-' if hb is None else f'{hb / 1e6:.1f} MB'} |")
+    t.append("")
+    t.append("Full kernel names (grid in work-items):")
+    t.append("")
+    for name, e in ks:
+        t.append(f"- `{name}`: `{e['kernel']}`, grid {e['grid_work_items']}")
+    return t
+
+
+def _write_profiles(line, kernels, cal):
+    """One markdown summary per workload of the step: the same lease's bench
+    line (HIP events) beside the kernel trace and the traffic counters."""
+    parts = line["parts"]
+    by_role = {}
+    for name, e in sorted(kernels.items(), key=lambda kv: kv[1]["first_dispatch"]):
+        by_role.setdefault(e["role"], []).append((name, e))
+    head = ["Measured on one MI355X (gfx950, 256 CUs) in one lease: the bench line and the rocprofv3 runs below, "
+            f"kernel code hash `{kernel_source_hash()}` (comments and layout ignored; `bench.py` -> "
+            "`kernel_source_hash()`).", "",
+            "Commands (run from the repository root copy `<repo>`, output dir `<out>`; the bench line comes from "
+            "`python3 <repo>/bench.py > <out>/bench.json` in the same lease):", "", "```", PROFILE_COMMANDS, "```", "",
+            f"Traffic scaling: a 1 GiB device copy reads FETCH_SIZE = {cal['FETCH_SIZE']:.4f} x and WRITE_SIZE = "
+            f"{cal['WRITE_SIZE']:.4f} x its true byte count; the counters see L2 <-> memory fabric traffic "
+            "(Infinity Cache hits included), per dispatch, summed over all XCDs.", ""]
+    for fname, key, enc_idx in PROFILE_WORKLOADS:
+        p = parts.get(key)
+        if p is None:
+            continue
+        L = []
+        if enc_idx is not None:
+            enc = by_role.get("encoder_fwd_kernel", [])
+            lns = by_role.get("res_ln_kernel", [])
+            alone = by_role.get("encoder_fwd_kernel(alone)", [])
+            if len(enc) <= enc_idx or len(lns) <= enc_idx:
+                continue
+            ks = [enc[enc_idx], lns[enc_idx]] + ([alone[enc_idx]] if len(alone) > enc_idx else [])
+            sh = p["shape"]
+            t_blk = (ks[0][1]["avg_duration_ns"] + ks[1][1]["avg_duration_ns"]) / 1e3
+            t_att = ks[2][1]["avg_duration_ns"] / 1e3 if len(ks) > 2 else None
+            L += [f"# Encoder block, {key} (B {sh['B']}, H {sh['H']}, S {sh['S']}, D {sh['D']}, fused residual add, "
+                  f"then LayerNorm over {sh['hidden']})", ""] + head
+            L += ["## Bench line of the same lease (HIP events, warm)", "",
+                  "| call | mean (us) | median (us) | min (us) | P90 (us) | TFLOP/s | % bf16 peak |", "|---|---|---|---|---|---|---|",
+                  f"| block (attention + residual, LayerNorm) | {p['mean_ms'] * 1e3:.1f} | {p['median_ms'] * 1e3:.1f} | "
+                  f"{p['min_ms'] * 1e3:.1f} | {p['p90_ms'] * 1e3:.1f} | {p['tflops']:.0f} | {100 * p['frac_bf16_peak']:.1f} |",
+                  f"| attention alone | {p['attention_only']['mean_ms'] * 1e3:.1f} | {p['attention_only']['median_ms'] * 1e3:.1f} | "
+                  f"{p['attention_only']['min_ms'] * 1e3:.1f} | {p['attention_only']['p90_ms'] * 1e3:.1f} | "
+                  f"{p['attention_only']['tflops']:.0f} | {100 * p['attention_only']['frac_bf16_peak']:.1f} |", "",
+                  "## Kernel trace", ""] + _kernel_rows(ks) + [""]
+            L += [f"Algorithmic work: {p['flops'] / 1e9:.2f} GFLOP of attention (QK^T + PV); MFMA bound at the "
+                  f"bf16 peak {p['mfma_bound_us']:.2f} us; softmax VALU bound {p['valu_bound']['us']:.2f} us "
+                  f"({p['valu_bound']['per_score']}).  From the trace: block {t_blk:.1f} us = "
+                  f"{p['flops'] / (t_blk * 1e-6) / 1e12:.0f} TFLOP/s ({100 * p['flops'] / (t_blk * 1e-6) / 1e12 / acc.PEAK_BF16_TFLOPS:.1f}% "
+                  "of bf16 peak)" + (f"; attention alone {t_att:.1f} us = {p['flops'] / (t_att * 1e-6) / 1e12:.0f} "
+                                     f"TFLOP/s ({100 * p['flops'] / (t_att * 1e-6) / 1e12 / acc.PEAK_BF16_TFLOPS:.1f}%), "
+                                     f"{100 * p['valu_bound']['us'] / t_att:.0f}% of the VALU bound's speed"
+                                     if t_att else "") + ".", ""]
+        elif key.startswith("gemma"):
+            ks = by_role.get("decode_split_kernel", []) + by_role.get("decode_combine_kernel", [])
+            if not ks:
+                continue
+            t = sum(e["avg_duration_ns"] for _, e in ks) / 1e3
+            L += ["# Gemma-style GQA decode (B 8, 16 Q / 8 KV heads, D 256, S_ctx 4096, per-row lengths from the seed)",
+                  ""] + head
+            L += ["## Bench line of the same lease (HIP events, 512 MiB written before each call)", "",
+                  "| mean (us) | median (us) | min (us) | P90 (us) | GB/s | % HBM peak |", "|---|---|---|---|---|---|",
+                  f"| {p['mean_ms'] * 1e3:.1f} | {p['median_ms'] * 1e3:.1f} | {p['min_ms'] * 1e3:.1f} | "
+                  f"{p['p90_ms'] * 1e3:.1f} | {p['gbps']:.0f} | {100 * p['frac_hbm_peak']:.1f} |", "",
+                  "## Kernel trace", ""] + _kernel_rows(ks) + [""]
+            L += [f"Algorithmic bytes: the live K/V rows (sum_b len_b x 8 KV heads x 256 x 2 B x 2) plus mask, q and "
+                  f"out: {p['bytes'] / 1e6:.1f} MB.  From the trace: the kernels take {t:.1f} us = "
+                  f"{p['bytes'] / (t * 1e-6) / 1e9:.0f} GB/s ({100 * p['bytes'] / (t * 1e-6) / 1e9 / acc.PEAK_HBM_GBPS:.1f}% "
+                  "of 8 TB/s).", ""]
+        else:
+            ks = by_role.get("prefill_tile_images_kernel", []) + by_role.get("prefill_paged_kernel", [])
+            if not ks:
+                continue
+            t = sum(e["avg_duration_ns"] for _, e in ks) / 1e3
+            tmin = sum(e["min_duration_ns"] for _, e in ks) / 1e3
+            r = line.get("roofline") or {}
+            L += ["# Paged FP8 prefill (4096 query tokens x 32 heads over 2 KV heads, D 256, 120000 of 131072 "
+                  "history keys, 512-token blocks)", ""] + head
+            L += ["## Bench line of the same lease (HIP events, warm)", "",
+                  "| mean (ms) | median (ms) | min (ms) | P90 (ms) | TFLOP/s | % bf16 peak |", "|---|---|---|---|---|---|",
+                  f"| {p['mean_ms']:.3f} | {p['median_ms']:.3f} | {p['min_ms']:.3f} | {p['p90_ms']:.3f} | "
+                  f"{p['tflops']:.0f} | {100 * p['frac_bf16_peak']:.1f} |", "",
+                  f"The line's `ms_per_step` (all four calls of the step, wall clock) is {line['ms_per_step']:.2f} ms.",
+                  "", "## Kernel trace", ""] + _kernel_rows(ks) + [""]
+            tr = sum(e.get("hbm_bytes_per_launch", 0) for _, e in ks)
+            L += [f"Algorithmic work: {p['flops'] / 1e12:.3f} TFLOP (QK^T + PV over the live keys).  From the trace: "
+                  f"image pass + key loop {t / 1e3:.3f} ms mean ({tmin / 1e3:.3f} ms min) = "
+                  f"{p['flops'] / (t * 1e-6) / 1e12:.0f} TFLOP/s, {100 * p['flops'] / (t * 1e-6) / 1e12 / acc.PEAK_BF16_TFLOPS:.1f}% "
+                  f"of the bf16 MFMA peak (the bench line: {100 * p['frac_bf16_peak']:.1f}%).  HBM-side traffic "
+                  f"{tr / 1e6:.0f} MB per call against {r.get('algorithmic_bytes', 0) / 1e6:.0f} MB of algorithmic "
+                  f"bytes (q, out, the live fp8 K/V once): "
+                  f"{tr / r['algorithmic_bytes'] if r.get('algorithmic_bytes') else float('nan'):.1f}x, the image pass "
+                  "writing the bf16 images and the key loop re-reading them from each XCD; at under 0.2 TB/s this is "
+                  "not what bounds the call.", ""]
+        with open(os.path.join(ROOT, "profiles", fname + ".md"), "w") as f:
+            f.write("\n".join(L))
+        print(f"wrote profiles/{fname}.md")
+
+
+def _stats(ms):
+    return {"mean_ms": statistics.fmean(ms), "median_ms": statistics.median(ms), "min_ms": min(ms),
+            "p90_ms": _pct(ms, 0.9), "max_ms": max(ms)}
 
 
 def main():
@@ -399,10 +623,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=160,
-                    help="query tokens in the CPU-baseline sample, about 10 s of oracle work on 16 cores (0: skip)")
-    ap.add_argument("--only", choices=["all", "encoder", "decode", "prefill", "next"], default="all",
-                    help="run a single kernel family (profiling runs)")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="prefill tokens in the CPU-baseline sample (256: the workload's sampled rows; 0: skip "
+                         "the CPU baseline)")
+    ap.add_argument("--only", choices=["all", "vjepa2", "dinov3", "decode", "prefill", "next"], default="all",
+                    help="run a single workload of the step (profiling runs)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the workload variants reported under parts.next (profiling runs of the step)")
     ap.add_argument("--pcp-shapes", action="store_true",
@@ -438,17 +663,37 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     _log("[bench] generating inputs")
-    enc = W.encoder_vjepa2()
+    encs = {"vjepa2_encoder_block_s2048": W.encoder_vjepa2(), "dinov3_encoder_block_s789": W.encoder_dinov3()}
     dec = W.decode_gemma()
     pre = W.prefill_paged()
 
-    e_q, e_k, e_v = (t.to(dev) for t in (enc.q, enc.k, enc.v))
-    e_res, e_g, e_b = enc.residual.to(dev), enc.gamma.to(dev), enc.beta.to(dev)
-    e_out = torch.empty_like(e_q)
-    e_rout = torch.empty_like(e_res)
-    e_ln = torch.empty(enc.B, enc.S, enc.H * enc.D, dtype=torch.bfloat16, device=dev)
-    e_mean = torch.empty(enc.B * enc.S, device=dev)
-    e_rstd = torch.empty(enc.B * enc.S, device=dev)
+    class EncDev:
+        def __init__(self, c):
+            self.c = c
+            self.q, self.k, self.v = (t.to(dev) for t in (c.q, c.k, c.v))
+            self.res, self.g, self.b = c.residual.to(dev), c.gamma.to(dev), c.beta.to(dev)
+            self.out = torch.empty_like(self.q)
+            self.rout = torch.empty_like(self.res)
+            self.ln = torch.empty(c.B, c.S, c.H * c.D, dtype=torch.bfloat16, device=dev)
+            self.mean = torch.empty(c.B * c.S, device=dev)
+            self.rstd = torch.empty(c.B * c.S, device=dev)
+
+        def block(self):
+            c = self.c
+            taa.attn_encoder_fwd(self.q, self.k, self.v, c.scale, None, out=self.out, residual=self.res,
+                                 residual_out=self.rout, gamma=self.g, beta=self.b, eps=c.eps, ln_out=self.ln,
+                                 ln_mean=self.mean, ln_rstd=self.rstd)
+
+        def attention(self):
+            taa.attn_encoder_fwd(self.q, self.k, self.v, self.c.scale, None, out=self.out, want_ln=False)
+
+    which = {"vjepa2": "vjepa2_encoder_block_s2048", "dinov3": "dinov3_encoder_block_s789"}
+    run_enc = [k for k in encs if args.only == "all" or which.get(args.only) == k]
+    run_dec = args.only in ("all", "decode")
+    run_pre = args.only in ("all", "prefill")
+    if args.only == "next":
+        args.steps = args.warmup = 0
+    e_dev = {k: EncDev(encs[k]) for k in run_enc}
 
     d_q, d_k, d_v, d_m = (t.to(dev) for t in (dec.q, dec.k, dec.v, dec.mask))
     d_out = torch.empty_like(d_q)
@@ -460,36 +705,33 @@ def main():
     p_ws = torch.empty(taa.attn_prefill_paged_expanded_workspace_size(pre.Hkv, pre.L_act, pre.D), dtype=torch.uint8,
                        device=dev)
     # 512 MiB written before every decode call (outside its timer), so its
-    # ~134 MB of K/V come from HBM and not from the 256 MB Infinity Cache
+    # ~134 MB of K/V come from HBM and not from the 256 MB Infinity Cache.
+    # The encoder blocks and the prefill are timed warm (compute-bound: their
+    # inputs are re-read from L2/MALL many times within one call anyway).
     flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
     torch.cuda.synchronize()
 
-    t_enc, t_dec, t_pre = Timer(), Timer(), Timer()
-    run_enc = args.only in ("all", "encoder")
-    run_dec = args.only in ("all", "decode")
-    run_pre = args.only in ("all", "prefill")
-    if args.only == "next":
-        args.steps = args.warmup = 0
+    t_enc = {k: Timer() for k in run_enc}
+    t_dec, t_pre = Timer(), Timer()
 
     def step(timed: bool):
-        if run_enc:
-            s = t_enc.start() if timed else None
-            taa.attn_encoder_fwd(e_q, e_k, e_v, enc.scale, None, out=e_out, residual=e_res, residual_out=e_rout,
-                                 gamma=e_g, beta=e_b, eps=enc.eps, ln_out=e_ln, ln_mean=e_mean, ln_rstd=e_rstd)
+        for k in run_enc:
+            s_ = t_enc[k].start() if timed else None
+            e_dev[k].block()
             if timed:
-                t_enc.stop(s)
+                t_enc[k].stop(s_)
         if run_dec:
             flush.zero_()
-            s = t_dec.start() if timed else None
+            s_ = t_dec.start() if timed else None
             taa.attn_decode_gqa(d_q, d_k, d_v, d_m, dec.scale, dec.G, out=d_out, workspace=d_ws)
             if timed:
-                t_dec.stop(s)
+                t_dec.stop(s_)
         if run_pre:
-            s = t_pre.start() if timed else None
+            s_ = t_pre.start() if timed else None
             taa.attn_prefill_paged_expanded(p_q, p_k, p_v, pre.k_scale, pre.v_scale, p_bt, pre.L_act, pre.scale,
                                             pre.G, out=p_out, workspace=p_ws)
             if timed:
-                t_pre.stop(s)
+                t_pre.stop(s_)
 
     _log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -503,65 +745,109 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps if args.steps else 0.0
 
-    f_enc = acc.encoder_flops(enc.B, enc.H, enc.S, enc.S, enc.D)
     lens = dec.lens.tolist()
     f_dec = 4 * sum(lens) * dec.Hq * dec.D  # each query head attends len_b keys of its batch row
     f_pre = acc.prefill_flops(pre.Lq, pre.Hq, pre.L_act, pre.D)
     b_dec = acc.decode_bytes(lens, dec.Hkv, dec.Hq, dec.S_ctx, dec.D)
-    total_flops = (f_enc if run_enc else 0) + (f_dec if run_dec else 0) + (f_pre if run_pre else 0)
+    f_enc = {k: acc.encoder_flops(c.B, c.H, c.S, c.S, c.D) for k, c in encs.items()}
+    total_flops = sum(f_enc[k] for k in run_enc) + (f_dec if run_dec else 0) + (f_pre if run_pre else 0)
 
     parts = {}
 
-    def summ(ms):
-        return {"mean_ms": statistics.fmean(ms), "median_ms": statistics.median(ms), "min_ms": min(ms),
-                "max_ms": max(ms)}
+    def gpu_timed(fn, n):
+        """Per-call GPU time of fn: a spin kernel (about 60 us) holds the stream
+        while the host enqueues the start event, the call and the end event, so
+        each event window holds the call's kernels only, not the host's
+        enqueue time (which exceeds a 20 us kernel)."""
+        t = Timer()
+        for _ in range(n):
+            torch.cuda._sleep(150_000)
+            s_ = t.start()
+            fn()
+            t.stop(s_)
+        torch.cuda.synchronize()
+        return t.ms()
 
-    if run_enc:
-        ms = t_enc.ms()
-        tf = f_enc / (statistics.fmean(ms) * 1e-3) / 1e12
-        parts["encoder_block"] = {**summ(ms), "tflops": tf, "frac_bf16_peak": tf / acc.PEAK_BF16_TFLOPS,
-                                  "flops": f_enc, "kernels": "attention+residual, res_ln"}
-    if run_dec:
+    # the encoder blocks and their attention alone (epilogue pointers null),
+    # timed after the step loop, warm; in the step itself a block's events
+    # also cover the host's enqueue time
+    for k in run_enc:
+        if not args.steps:
+            break
+        e = e_dev[k]
+        for _ in range(3):
+            e.attention()
+        ms_b = gpu_timed(e.block, args.steps)
+        ms_a = gpu_timed(e.attention, args.steps)
+        c = encs[k]
+        tf_b = f_enc[k] / (statistics.fmean(ms_b) * 1e-3) / 1e12
+        tf_a = f_enc[k] / (statistics.fmean(ms_a) * 1e-3) / 1e12
+        scores = c.B * c.H * c.S * c.S
+        bound_us = acc.softmax_valu_bound_us(scores)
+        parts[k] = {
+            **_stats(ms_b), "tflops": tf_b, "frac_bf16_peak": tf_b / acc.PEAK_BF16_TFLOPS, "flops": f_enc[k],
+            "kernels": "attention + fp32 residual epilogue, res_ln (LayerNorm over H*D)",
+            "shape": {"B": c.B, "H": c.H, "S": c.S, "D": c.D, "hidden": c.H * c.D},
+            "attention_only": {**_stats(ms_a), "tflops": tf_a, "frac_bf16_peak": tf_a / acc.PEAK_BF16_TFLOPS},
+            "epilogue_and_ln_ms": statistics.fmean(ms_b) - statistics.fmean(ms_a),
+            "in_step_events_mean_ms": statistics.fmean(t_enc[k].ms()),
+            "timing": "per call, HIP events behind a spin kernel (GPU time of the call's kernels), warm",
+            "mfma_bound_us": f_enc[k] / acc.PEAK_BF16_TFLOPS / 1e6,
+            "valu_bound": {"us": bound_us, "scores": scores,
+                           "per_score": f"{acc.SOFTMAX_EXP_PER_SCORE:g} exp2 (16 cycles per wave64) + "
+                                        f"{acc.SOFTMAX_FULL_RATE_PER_SCORE:g} full-rate VALU ops (4 cycles): FMA, "
+                                        "half a max3, half a bf16 pack, half a dot2 row sum",
+                           "attention_frac_of_bound": bound_us / (statistics.fmean(ms_a) * 1e3)},
+        }
+    if run_dec and args.steps:
         ms = t_dec.ms()
         gbs = b_dec / (statistics.fmean(ms) * 1e-3) / 1e9
-        parts["decode"] = {**summ(ms), "gbps": gbs, "frac_hbm_peak": gbs / acc.PEAK_HBM_GBPS, "bytes": b_dec,
-                           "dense_equiv_gbps": acc.decode_dense_bytes(dec.B, dec.Hkv, dec.Hq, dec.S_ctx, dec.D)
-                           / (statistics.fmean(ms) * 1e-3) / 1e9, "kernels": "split-K, combine"}
-    if run_pre:
+        parts["gemma_gqa_decode_d256_ctx4096"] = {
+            **_stats(ms), "gbps": gbs, "frac_hbm_peak": gbs / acc.PEAK_HBM_GBPS, "bytes": b_dec,
+            "dense_equiv_gbps": acc.decode_dense_bytes(dec.B, dec.Hkv, dec.Hq, dec.S_ctx, dec.D)
+            / (statistics.fmean(ms) * 1e-3) / 1e9, "kernels": "split-K, combine",
+            "timing": "512 MiB written before each call (outside its events): K/V come from HBM"}
+    if run_pre and args.steps:
         ms = t_pre.ms()
         tf = f_pre / (statistics.fmean(ms) * 1e-3) / 1e12
-        parts["prefill"] = {**summ(ms), "tflops": tf, "frac_bf16_peak": tf / acc.PEAK_BF16_TFLOPS, "flops": f_pre,
-                            "tflops_at_131072_convention": acc.prefill_flops(pre.Lq, pre.Hq, 131072, pre.D)
-                            / (statistics.fmean(ms) * 1e-3) / 1e12,
-                            "kernels": "tile images (fp8 history -> bf16), key loop"}
+        parts["paged_fp8_prefill_q4096_hist120000"] = {
+            **_stats(ms), "tflops": tf, "frac_bf16_peak": tf / acc.PEAK_BF16_TFLOPS, "flops": f_pre,
+            "tflops_at_131072_convention": acc.prefill_flops(pre.Lq, pre.Hq, 131072, pre.D)
+            / (statistics.fmean(ms) * 1e-3) / 1e12,
+            "kernels": "tile images (fp8 history -> bf16), key loop"}
 
     roofline = None
-    if run_pre:
-        p = parts["prefill"]
+    if run_pre and args.steps:
+        p = parts["paged_fp8_prefill_q4096_hist120000"]
         # one prefill call = the tile-image pass + the key loop; both count
         # toward its time (achieved) and its HBM bytes (traffic)
         t_img, t_loop = measured_traffic("prefill_tile_images_kernel"), measured_traffic("prefill_paged_kernel")
+        # algorithmic bytes: q and out bf16, the live fp8 history K/V once
+        alg = 2 * pre.Hq * pre.Lq * pre.D * 2 + 2 * pre.Hkv * pre.L_act * pre.D
+        traffic = t_img + t_loop if t_img is not None and t_loop is not None else None
         roofline = {"bound": "mfma", "achieved": p["tflops"], "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": p["tflops"] / acc.PEAK_BF16_TFLOPS,
-                    "traffic": t_img + t_loop if t_img is not None and t_loop is not None else None,
+                    "frac": p["tflops"] / acc.PEAK_BF16_TFLOPS, "traffic": traffic,
+                    "algorithmic_bytes": alg, "traffic_over_algorithmic": traffic / alg if traffic else None,
                     "kernel": "prefill_tile_images_kernel + prefill_paged_kernel",
                     "kernel_source_hash": kernel_source_hash()}
-    elif run_enc:
-        p = parts["encoder_block"]
+    elif run_enc and args.steps:
+        p = parts[run_enc[0]]
         roofline = {"bound": "mfma", "achieved": p["tflops"], "peak": acc.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": p["frac_bf16_peak"], "traffic": None, "kernel": "encoder_fwd_kernel+res_ln_kernel"}
-    elif run_dec:
-        p = parts["decode"]
+    elif run_dec and args.steps:
+        p = parts["gemma_gqa_decode_d256_ctx4096"]
         roofline = {"bound": "hbm", "achieved": p["gbps"], "peak": acc.PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": p["frac_hbm_peak"], "traffic": None, "kernel": "decode_split_kernel+decode_combine_kernel"}
 
     if args.only in ("all", "next") and not args.no_next:
+        _log("[bench] workload variants")
         parts["next"] = time_next_workloads(taa, dev, flush, (pre, p_q, p_k, p_v, p_bt))
 
     cpu = None
-    if args.cpu_rows > 0 and run_pre:
-        _log(f"[bench] cpu baseline: oracle on {args.cpu_rows} prefill tokens")
-        cpu = cpu_baseline(pre, args.cpu_rows)
+    if args.cpu_rows > 0 and args.only == "all":
+        _log(f"[bench] cpu baseline: oracle on workloads 1-4 and {args.cpu_rows} prefill tokens")
+        cases = {"tiny_sdpa_s128_block": W.encoder_tiny(), **encs, "gemma_gqa_decode_d256_ctx4096": dec}
+        cpu = cpu_baseline(cases, pre, args.cpu_rows)
 
     line = {
         "metric": "attn TFLOP/s & % MFMA peak (encoder/prefill); decode GB/s & % HBM peak",
@@ -577,9 +863,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes of the pages' workloads, no weights or datasets)",
         "config": {
-            "workload": "vjepa2_encoder_block_s2048 + gemma_gqa_decode_d256_ctx4096 + paged_fp8_prefill_q4096_hist120000"
-            if args.only == "all" else args.only,
-            "encoder": {"B": enc.B, "H": enc.H, "S": enc.S, "D": enc.D, "residual_ln_hidden": enc.H * enc.D},
+            "workload": "vjepa2_encoder_block_s2048 + dinov3_encoder_block_s789 + gemma_gqa_decode_d256_ctx4096 + "
+                        "paged_fp8_prefill_q4096_hist120000" if args.only == "all" else args.only,
+            "encoders": {k: {"B": c.B, "H": c.H, "S": c.S, "D": c.D, "residual_ln_hidden": c.H * c.D}
+                         for k, c in encs.items()},
             "decode": {"B": dec.B, "Hq": dec.Hq, "Hkv": dec.Hkv, "S_ctx": dec.S_ctx, "D": dec.D, "sum_len": sum(lens)},
             "prefill": {"Lq": pre.Lq, "Hq": pre.Hq, "Hkv": pre.Hkv, "D": pre.D, "block_size": pre.block_size,
                         "actual_history_len": pre.L_act, "kv": "fp8_e4m3fn"},

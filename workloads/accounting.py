@@ -63,3 +63,28 @@ def vit_encoder_flops(layers: int, tokens: int, hidden: int, mlp: int, patch_in:
     per_layer = (2 * tokens * hidden * 3 * hidden + 2 * tokens * hidden * hidden
                  + 2 * 2 * tokens * hidden * mlp + 4 * tokens * tokens * hidden)
     return layers * per_layer + 2 * tokens * patch_in * hidden
+
+
+# The softmax's VALU work, the encoder's second roofline at head_dim 64.
+# 256 CUs x 4 SIMDs issue at 2.4 GHz; a wave64 VALU instruction occupies its
+# SIMD's VALU 4 cycles at full rate and 16 cycles for a transcendental
+# (v_exp_f32 runs at a quarter of the rate).
+SIMDS = 256 * 4
+CLOCK_GHZ = 2.4
+# Per score, at the least: one exp2 and, at full rate, the scale-and-subtract
+# FMA (1), the row max (half an op: a max3 folds two scores), the bf16 pack of
+# P (half: two scores per pack) and the row sum (half: a dot2 of two packed
+# scores).
+SOFTMAX_EXP_PER_SCORE = 1.0
+SOFTMAX_FULL_RATE_PER_SCORE = 2.5
+
+
+def softmax_valu_cycles(n_scores: int, exp_per_score: float = SOFTMAX_EXP_PER_SCORE,
+                        full_rate_per_score: float = SOFTMAX_FULL_RATE_PER_SCORE) -> float:
+    """SIMD-cycles of VALU issue the online softmax needs for n_scores scores."""
+    return n_scores / 64 * (16 * exp_per_score + 4 * full_rate_per_score)
+
+
+def softmax_valu_bound_us(n_scores: int, **kw) -> float:
+    """Shortest time the whole chip's VALUs need for that softmax work (us)."""
+    return softmax_valu_cycles(n_scores, **kw) / SIMDS / (CLOCK_GHZ * 1e3)
