@@ -132,7 +132,7 @@ def test_decode_window_range_changes_on_device(gpu_lib):
     case = W.decode_gemma(99, 2, 4, 2, 1536, lens=[1536, 1536])
     d = lambda t: t.to(DEV)
     q, k, v = d(case.q), d(case.k), d(case.v)
-    ws = torch.empty(taa.attn_decode_gqa_window_workspace_size(2, 4, 1536, 256, 256), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(taa.attn_decode_gqa_window_workspace_size(2, 4, 1536, 256, 256), dtype=torch.uint8, device=DEV)
     kb, ke = _i32([0, 0]), _i32([256, 256])
     outs = []
     for rng in (([10, 1000], [266, 1200]), ([1280, 77], [1536, 300])):
@@ -144,3 +144,27 @@ def test_decode_window_range_changes_on_device(gpu_lib):
     for o, (b_, e_) in outs:
         ref = oracle.decode_window(case.q, case.k, case.v, case.scale, None, b_, e_, 256)
         assert_close(o, ref, f"device range {b_}-{e_}")
+
+
+def test_one_workspace_for_decodes_of_different_shapes(gpu_lib):
+    """The workspace's arrival counters sit at a fixed place: calls of
+    different shapes (larger, smaller, larger again; plain and windowed)
+    share one zero-filled workspace and each matches the oracle."""
+    taa = gpu_lib
+    big = W.decode_gemma(1530, B=8, Hq=16, Hkv=8, S_ctx=2048)
+    small = W.decode_gemma(1531, B=2, Hq=8, Hkv=2, S_ctx=700, lens=[700, 3])
+    n = max(taa.attn_decode_gqa_workspace_size(c.B, c.Hq, c.S_ctx, c.D) for c in (big, small))
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    d = lambda t: t.to(DEV)
+    for case in (big, small, big):
+        _say(f"[decode] shared workspace: B={case.B} Hq={case.Hq} Hkv={case.Hkv} S_ctx={case.S_ctx}")
+        out = taa.attn_decode_gqa(d(case.q), d(case.k), d(case.v), d(case.mask), case.scale, case.G, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(out, oracle.sdpa(case.q, case.k, case.v, case.scale, case.mask), f"shared ws {case.name}")
+    beg, end = [0, 200], [700, 650]
+    kb, ke = (torch.tensor(x, dtype=torch.int32, device=DEV) for x in (beg, end))
+    out = taa.attn_decode_gqa_window(d(small.q), d(small.k), d(small.v), None, kb, ke, 300, small.scale, small.G,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(out, oracle.decode_window(small.q, small.k, small.v, small.scale, None, beg, end, 300),
+                 "shared ws window")

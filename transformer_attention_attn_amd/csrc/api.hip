@@ -73,7 +73,7 @@ int decode_common(const void *q, const void *k, const void *v, const float *attn
                              : attn_decode_gqa_workspace_size(B, Hq, S_ctx, D);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_INVALID_ARG;
-  if (n_chunks > 0x7fffffffLL || Hkv > 65535 || B > 65535 || Hq > 65535) return ATTN_ERR_UNSUPPORTED;
+  if (n_chunks * Hkv * B > 0x7fffffffLL || Hq > 65535) return ATTN_ERR_UNSUPPORTED;  // one-dimensional grid
 
   DecodeLaunch L;
   memset(&L, 0, sizeof L);

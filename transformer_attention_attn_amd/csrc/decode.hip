@@ -8,8 +8,9 @@
 // re-streaming the whole cache is bandwidth-starved and that the KV stream
 // should be sharded over many programs, and that sliding-window layers need
 // only the most recent window of keys.  Here every (batch, KV head, chunk of
-// 64 keys) is its own workgroup, the G query heads of a KV head share the
-// one pass over its K/V, and a second kernel merges the chunk partials.  With
+// 64 keys) is its own workgroup (the highest chunks dispatched first), the
+// G query heads of a KV head share the one pass over its K/V, and a second
+// kernel merges the chunk partials.  With
 // a key range the grid spans only the chunks the widest range can touch,
 // counted from each sequence's own first key (a windowed gather: keys before
 // the window are never fetched and get no workgroup).  The introduction of
@@ -117,10 +118,13 @@ __device__ __forceinline__ DecRange dec_range(const DecodeLaunch &a, int b) {
 // The accumulator of one query head: the lane's D/64 output columns.
 template <int D> struct DecAcc { float x[D / 64]; };
 
-template <int D> constexpr int dec_waves_per_eu() { return D == 256 ? 5 : 2; }
+// Register budget (waves per SIMD): at head_dim 256, 5 waves fit one or two
+// query heads per KV head; four heads need the 4-wave budget (5 spills 20
+// bytes per lane).
+template <int D, int G> constexpr int dec_waves_per_eu() { return D == 256 ? (G >= 4 ? 4 : 5) : 2; }
 
 template <int D, int G>
-__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<D>())))
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<D, G>())))
 void decode_split_kernel(DecodeLaunch a) {
   constexpr int KW = kDecKW, NW = kDecWaves, NG = kDecNG, WK = NG * KW;  // WK: keys per wave
   constexpr int CPL = D / 64;                                             // output columns per lane
@@ -138,7 +142,14 @@ void decode_split_kernel(DecodeLaunch a) {
   auto sc = reinterpret_cast<float(*)[G][KW]>(smem + QS_B);
   auto red_o = reinterpret_cast<float(*)[G][D]>(smem + (ALIAS ? 0 : QS_B + SC_B));
 
-  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // One-dimensional grid, chunk-major with the last chunks first: the chunks
+  // that most sequences leave empty (the highest) are dispatched first and
+  // exit early, and the final workgroups are the all-live first chunks of
+  // every (batch, KV head), which finish together.  A timeline of the
+  // workgroups showed the (batch-major) order ending in a long tail of the
+  // last batch's chunks.
+  const int np = a.Hkv * a.B, lin = blockIdx.x;
+  const int chunk = a.n_chunks - 1 - lin / np, kvh = (lin % np) % a.Hkv, b = (lin % np) / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const DecRange R = dec_range(a, b);
   const float *mrow = a.mask ? a.mask + (int64_t)b * a.S_ctx : nullptr;
@@ -344,7 +355,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeLaunch a) {
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeLaunch &a, hipStream_t stream) {
-  const dim3 grid(a.n_chunks, a.Hkv, a.B), block(64 * kDecWaves);
+  const dim3 grid(a.n_chunks * a.Hkv * a.B), block(64 * kDecWaves);
   switch (a.G) {
     case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, block, 0, stream, a); break;
