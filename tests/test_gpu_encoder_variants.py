@@ -107,3 +107,40 @@ def test_rows_independent_of_other_rows(gpu_lib):
     b = gpu_lib.attn_encoder_fwd(d(q2), d(case.k), d(case.v), case.scale, None, want_ln=False)["out"]
     torch.cuda.synchronize()
     assert torch.equal(a[:, :, 0::2], b[:, :, 0::2])
+
+
+def test_key_row_strides_give_identical_bits(gpu_lib):
+    """bf16 K/V rows are copied global -> LDS by direct loads, one 16-byte
+    piece per lane at an offset built from the key's row stride (K
+    chunk-major, V rows with their halves swapped on key bit 1).  The same
+    values in rows of another stride (head-major, padded 72-wide rows,
+    token-major [B,S,H,D] memory) must give the same bits, including the
+    ragged last tiles, and match the oracle."""
+    B, H, S, D = 2, 4, 789, 64
+    case = W.encoder_custom(805, B, H, S, D)
+    q = case.q.to(DEV)
+
+    def strided(t, width):  # the same values in rows of `width` elements
+        buf = torch.zeros(B, H, S, width, dtype=t.dtype)
+        buf[..., :D] = t
+        return buf.to(DEV)[..., :D]
+
+    def token_major(t):  # [B, S, H, D] memory, viewed as [B, H, S, D]
+        return t.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+
+    layouts = {
+        "contiguous": (case.k.to(DEV), case.v.to(DEV)),
+        "72-wide rows": (strided(case.k, 72), strided(case.v, 72)),
+        "token-major": (token_major(case.k), token_major(case.v)),
+        "mixed": (token_major(case.k), strided(case.v, 72)),
+    }
+    outs = {}
+    for name, (k, v) in layouts.items():
+        _say(f"[encoder-variant] key row strides: {name} k.stride={k.stride()} v.stride={v.stride()}")
+        r = gpu_lib.attn_encoder_fwd(q, k, v, case.scale, None, lse=torch.empty(B, H, S, device=DEV), want_ln=False)
+        torch.cuda.synchronize()
+        outs[name] = (r["out"].cpu(), r["lse"].cpu())
+    for name, (o, l) in outs.items():
+        assert torch.equal(o, outs["contiguous"][0]) and torch.equal(l, outs["contiguous"][1]), f"{name} differs"
+    ref = oracle.encoder_block(case.q, case.k, case.v, case.scale, case.residual, case.gamma, case.beta, case.eps)
+    assert_close(outs["contiguous"][0], ref["attn"], "strided key rows: attention")

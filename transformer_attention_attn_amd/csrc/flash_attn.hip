@@ -75,7 +75,7 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 
 template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int OCC_, bool VFIRST_ = false, int QL_ = 0,
-          bool PVPRIO_ = false, bool DMA_ = false>
+          bool PVPRIO_ = false, bool DMA_ = false, bool EDMA_ = false>
 struct Geo {
   static constexpr int D = D_, BN = BN_, NT = NT_, RG = RG_, NSPLIT = NSPLIT_;
   static constexpr int GRP = GRP_;  // LDS fragments read ahead of the MFMAs that use them
@@ -106,9 +106,15 @@ struct Geo {
   // bank groups.  Three buffers per operand let a tile's copy run two
   // iterations ahead of its use.
   static constexpr bool DMA = DMA_;
-  static constexpr int NBUF = DMA ? 3 : 2;
-  static constexpr int KTILE = DMA ? BN * D * 2 : BN * KROW;
-  static constexpr int VTILE = DMA ? BN * D * 2 : BN * D * 2 + (BN >> VSH) * 64;
+  // EDMA: the caller's bf16 K and V rows copied global -> LDS by the same
+  // direct loads (no image pass): K chunk-major as above, V row-major with
+  // the two 64-byte halves of a row swapped when key bit 1 is set
+  // (v_frag_edma), which stands in for the padding a direct load cannot make.
+  static constexpr bool EDMA = EDMA_;
+  static constexpr bool LINEAR = DMA || EDMA;  // tiles land unpadded, K chunk-major
+  static constexpr int NBUF = LINEAR ? 3 : 2;
+  static constexpr int KTILE = LINEAR ? BN * D * 2 : BN * KROW;
+  static constexpr int VTILE = LINEAR ? BN * D * 2 : BN * D * 2 + (BN >> VSH) * 64;
   static constexpr int KSLOT = NSPLIT * KTILE;                    // one K buffer: every split's tile
   static constexpr int VSLOT = NSPLIT * VTILE + NSPLIT * BN * 4;  // one V buffer, then the tiles' staged key mask
   static constexpr int KB = BN / 32;  // 32-key blocks per tile
@@ -135,15 +141,17 @@ struct Geo {
   static_assert(QL >= 0 && QL <= SD, "Q fragments in LDS");
   static_assert(!DMA || (NSPLIT == 1 && BN == 32 && KTILE % 1024 == 0 && VTILE % 1024 == 0),
                 "tile images: one key split, 32-key tiles, 1 KB pieces");
+  static_assert(!EDMA || (!DMA && D == 64 && BN == 32 && QL == 0 && KSLOT % (1024 * WAVES) == 0),
+                "direct encoder tiles: 128-byte rows, 32-key tiles, whole rounds of 1 KB pieces");
   static_assert(LDS <= 160 * 1024, "LDS budget (gfx950: 160 KiB per workgroup)");
 
-  static __device__ __forceinline__ int k_row(int key) { static_assert(!DMA, "padded K rows"); return key * KROW; }
+  static __device__ __forceinline__ int k_row(int key) { static_assert(!LINEAR, "padded K rows"); return key * KROW; }
   // byte offset of this lane's first QK fragment (key lane%32, chunk lane/32)
   // and of fragment (32-key block kb, k-step sd) relative to it
   static __device__ __forceinline__ int k_lane(int lane) {
-    return DMA ? (lane & 31) * 16 + (lane >> 5) * BN * 16 : (lane & 31) * KROW + 16 * (lane >> 5);
+    return LINEAR ? (lane & 31) * 16 + (lane >> 5) * BN * 16 : (lane & 31) * KROW + 16 * (lane >> 5);
   }
-  static constexpr int k_frag(int kb, int sd) { return DMA ? kb * 512 + sd * 2 * BN * 16 : kb * 32 * KROW + 32 * sd; }
+  static constexpr int k_frag(int kb, int sd) { return LINEAR ? kb * 512 + sd * 2 * BN * 16 : kb * 32 * KROW + 32 * sd; }
   static __device__ __forceinline__ int v_row(int key) { return key * (D * 2) + (key >> VSH) * 64; }
   // DMA: the V^T chunk of (d, k-step kk, lane half h) holds, as elements
   // j = 0..7, the keys 16kk + 8(j/4) + 4h + j%4 (the key order of P's B
@@ -434,6 +442,63 @@ struct TileImgSrc {
   }
   __device__ __forceinline__ void copy_v(char *dst, int t, int wave, int lane) const {
     copy(tile(t), dst, G::KTILE, VP, wave, lane);
+  }
+};
+
+// The encoder's K and V tiles copied global -> LDS by direct loads (G::EDMA;
+// bf16 rows whose base and stride are multiples of 16 bytes, checked on the
+// host).  An iteration's NSPLIT tiles of each operand are KSLOT / 1 KB pieces
+// and wave w copies pieces w, w + WAVES, ...; piece p belongs to split p / PT,
+// keys of that split's tile:
+//   K: lane L takes chunk c = 2 (p % PT) + L / 32 (d = 8c .. 8c + 7) of key
+//      L % 32, which lands at c * 512 + key * 16 (chunk-major);
+//   V: lane L lands at byte 16 L of the piece, key 8 (p % PT) + L / 8,
+//      physical chunk L % 8, and takes the key's logical chunk
+//      (L % 8) ^ (4 * key bit 1) (the half swap v_frag_edma undoes).
+// Each iteration's keys form one buffer range (as EncSrc's), so keys past
+// n_keys read as zeros.
+template <class G>
+struct EncDmaSrc {
+  static constexpr int PT = G::KTILE / 1024;            // pieces per split tile
+  static constexpr int PW = G::KSLOT / 1024 / G::WAVES;  // pieces per wave and operand
+  static constexpr int KEYS = G::NSPLIT * G::BN;
+  static constexpr bool kNoScalarLoads = true;
+  const char *kb, *vb;     // this (b,h)'s K and V base
+  int64_t kstep, vstep;    // bytes per iteration
+  uint32_t krow, vrow;     // bytes between consecutive keys
+  int n_keys;
+  uint32_t koff[PW], voff[PW];  // this lane's source offsets inside an iteration's keys
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      const int p = wave + j * G::WAVES, sp = p / PT, pp = p % PT;
+      const int ck = 2 * pp + (lane >> 5), kk = lane & 31;
+      koff[j] = (uint32_t)(sp * G::BN + kk) * krow + ck * 16;
+      const int kv = 8 * pp + (lane >> 3), cv = (lane & 7) ^ (((kv >> 1) & 1) << 2);
+      voff[j] = (uint32_t)(sp * G::BN + kv) * vrow + cv * 16;
+    }
+  }
+  __device__ __forceinline__ uint32_t records(int it, uint32_t row) const {
+    const int full = n_keys / KEYS;
+    const uint32_t n = it < full ? (uint32_t)KEYS : it == full ? (uint32_t)(n_keys % KEYS) : 0u;
+    return n * row;
+  }
+  // wait until at most this wave's copies of one tile step are in flight
+  static __device__ __forceinline__ void wait_step(int) { wait_vm<2 * PW>(); }
+  __device__ __forceinline__ void copy_k(char *dst, int it, int wave, int) const {
+    const auto r = make_rsrc(kb + it * kstep, records(it, krow));
+#pragma unroll
+    for (int j = 0; j < PW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + (wave + j * G::WAVES) * 1024),
+                                               16, koff[j], 0, 0, 0);
+  }
+  __device__ __forceinline__ void copy_v(char *dst, int it, int wave, int) const {
+    const auto r = make_rsrc(vb + it * vstep, records(it, vrow));
+#pragma unroll
+    for (int j = 0; j < PW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + (wave + j * G::WAVES) * 1024),
+                                               16, voff[j], 0, 0, 0);
   }
 };
 
@@ -793,6 +858,22 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
 // multiples of 4, so v_row(base + j) = v_row(base) + v_row(j).  Over tile
 // images (G::DMA) V^T already holds those keys in that order: one 16-byte
 // read at vt_off.
+// PV A fragment q of a directly copied V tile (G::EDMA): the same rows and
+// columns as the staged read above, at their row-major, half-swapped place:
+// logical 16-byte chunk c of row r sits at r*128 + 16*(c ^ 4*((r >> 1) & 1)).
+// The row offsets of the fragments (8t + 16kk + 32kb) keep bit 1, so the swap
+// is fixed per lane.  In each half-wave the four rows j = 0..3 then fall in
+// four different quarters of the 64 banks.
+template <class G>
+__device__ __forceinline__ u32x4_t v_frag_edma(const char *vt, int lane, int q) {
+  const int h = lane >> 5, j = (lane >> 2) & 3, m = lane & 3, g2 = (lane >> 4) & 1;
+  const int mt = q % G::MT, kk = (q / G::MT) % 2, kb = q / (2 * G::MT);
+  const char *p = vt + (4 * h + j) * 128 + ((mt ^ ((j >> 1) & 1)) << 6) + (2 * g2 + (m >> 1)) * 16 + (m & 1) * 8 +
+                  (kb * 32 + kk * 16) * 128;
+  const u32x2_t a0 = lds_read_tr16(p), a1 = lds_read_tr16(p + 8 * 128);
+  return u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+}
+
 template <class G, bool HAS_MASK, class Work>
 __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f32x16_t (&s)[G::NT][G::KB],
                                         float c, const char *vt, int lane, Work &&work) {
@@ -814,6 +895,8 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
     const int mt = q % G::MT, kk = (q / G::MT) % 2, kb = q / (2 * G::MT);
     if constexpr (G::DMA) {
       fb[q] = *reinterpret_cast<const u32x4_t *>(vt + vto + G::vt_off(32 * mt, kk, 0));
+    } else if constexpr (G::EDMA) {
+      fb[q] = v_frag_edma<G>(vt, lane, q);
     } else {
       const char *p = vbase + G::v_row(kb * 32 + kk * 16) + 64 * mt;
       const u32x2_t a0 = lds_read_tr16(p), a1 = lds_read_tr16(p + G::v_row(8));
@@ -958,7 +1041,9 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
   }
 }
 
-// The key loop over tile images (G::DMA, one key split).  Three K buffers
+// The key loop over tiles copied by direct loads: tile images (G::DMA, one
+// key split) or the encoder's own rows (G::EDMA, each wave reading its key
+// split's tile of every buffer).  Three K buffers
 // (kA, kB, kC) and three V buffers: at step `it` they hold K(it), K(it+1),
 // K(it+2) and V(it), V(it+1), V(it+2) in an order that rotates with it % 3.
 // Phase A reads K(it+1), phase B reads V(it), and the step copies K(it+3)
@@ -972,8 +1057,8 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
 // never aliases the LDS reads that follow it; otherwise it would wait for
 // every copy before each LDS read.  Same phases, schedule and masks as
 // flash_loop.
-template <class G, class Mask>
-__device__ __forceinline__ void dma_loop_body(WaveState<G> &ws, const TileImgSrc<G> &src,
+template <class G, class Src, class Mask>
+__device__ __forceinline__ void dma_loop_body(WaveState<G> &ws, const Src &src,
                                               const u32x4_t (&qf)[G::NT][G::SD], char *__restrict__ kA,
                                               char *__restrict__ kB, char *__restrict__ kC, char *__restrict__ vA,
                                               char *__restrict__ vB, char *__restrict__ vC,
@@ -988,9 +1073,11 @@ __device__ __forceinline__ void dma_loop_body(WaveState<G> &ws, const TileImgSrc
   wait_vm<0>();
   lds_barrier();
 
+  // key split of this wave (its tile of each iteration: sp * KTILE, sp * VTILE)
+  const int sp = G::NSPLIT > 1 ? wave / G::RG : 0;
   f32x16_t s[G::NT][G::KB], s2[G::NT][G::KB];
-  qk_tile<G>(s, qf, qa, kA, lane);
-  mk.template apply<G>(s, 0, lane);
+  qk_tile<G>(s, qf, qa, kA + sp * G::KTILE, lane);
+  mk.template apply<G>(s, sp * G::BN, lane);
   lds_barrier();  // K(0) read by every wave before K(3) replaces it
 
   // kr: K(it+1), read; kw: K(it)'s buffer, receives K(it+3); vr: V(it), read;
@@ -999,20 +1086,20 @@ __device__ __forceinline__ void dma_loop_body(WaveState<G> &ws, const TileImgSrc
                   char *__restrict__ vw, f32x16_t (&S)[G::NT][G::KB], f32x16_t (&SN)[G::NT][G::KB]) {
     PCarry<G> pc;
     float alpha[G::NT];
-    const bool any = phase_a<G, false>(ws, pc, SN, S, alpha, qf, qa, kr, nullptr, c, lane);
+    const bool any = phase_a<G, false>(ws, pc, SN, S, alpha, qf, qa, kr + sp * G::KTILE, nullptr, c, lane);
     if (any) {
 #pragma unroll
       for (int nt = 0; nt < G::NT; ++nt)
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] *= alpha[nt];
     }
-    phase_b<G, false>(ws, pc, S, c, vr, lane, [&](int k) {
+    phase_b<G, false>(ws, pc, S, c, vr + sp * G::VTILE, lane, [&](int k) {
       if (k == 0) src.copy_k(kw, it + 3, wave, lane);
       if (k == 1) src.copy_v(vw, it + 2, wave, lane);
     });
-    TileImgSrc<G>::wait_step(wave);  // the step before's copies have landed
+    Src::wait_step(wave);  // the step before's copies have landed
     lds_barrier();
-    mk.template apply<G>(SN, (it + 1) * G::BN, lane);
+    mk.template apply<G>(SN, ((it + 1) * G::NSPLIT + sp) * G::BN, lane);
   };
   for (int it = 0; it < n_iter; it += 6) {
     step(it, kB, kA, vA, vC, s, s2);
@@ -1031,14 +1118,14 @@ __device__ __forceinline__ void dma_loop_body(WaveState<G> &ws, const TileImgSrc
   lds_barrier();
 }
 
-template <class G, class Mask>
-__device__ __forceinline__ void flash_loop_dma(WaveState<G> &ws, const TileImgSrc<G> &src,
+template <class G, class Src, class Mask>
+__device__ __forceinline__ void flash_loop_dma(WaveState<G> &ws, const Src &src,
                                                const u32x4_t (&qf)[G::NT][G::SD], char *smem, float c, const Mask &mk,
                                                bool fresh, unsigned tid) {
-  static_assert(G::DMA && G::NSPLIT == 1, "tile images: one key split");
+  static_assert(G::LINEAR && (G::EDMA || G::NSPLIT == 1), "tile images: one key split");
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
-  const int n_iter = (src.n_keys + G::BN - 1) / G::BN;
+  const int n_iter = ((src.n_keys + G::BN - 1) / G::BN + G::NSPLIT - 1) / G::NSPLIT;
   if (fresh) {
 #pragma unroll
     for (int nt = 0; nt < G::NT; ++nt) {
@@ -1187,7 +1274,21 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   src.mask = HAS_MASK ? a.mask + b * a.mask_sb : nullptr;
 
   WaveState<G> ws;
-  flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c, TailMask{a.Skv}, true, threadIdx.x);
+  if constexpr (G::EDMA) {
+    static_assert(!F32IN && !HAS_MASK, "direct copies: bf16 rows, no additive mask");
+    EncDmaSrc<G> ds;
+    ds.kb = src.kb;
+    ds.vb = src.vb;
+    ds.krow = src.krow;
+    ds.vrow = src.vrow;
+    ds.kstep = src.kstep;
+    ds.vstep = src.vstep;
+    ds.n_keys = a.Skv;
+    ds.init(__builtin_amdgcn_readfirstlane(wave), lane);
+    flash_loop_dma<G>(ws, ds, qf, smem, a.c, TailMask{a.Skv}, true, threadIdx.x);
+  } else {
+    flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c, TailMask{a.Skv}, true, threadIdx.x);
+  }
 
   // The residual rows are read before the split merge, so their latency
   // overlaps it.
@@ -1464,9 +1565,11 @@ __global__ __launch_bounds__(256) void prefill_tile_images_kernel(PrefillLaunch 
 
 // ------------------------------------------------------------------ launchers
 
-using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true>;      // BM 128, 8 waves: 4 row groups x 2 key splits, 32-key tiles, 4 waves/SIMD
-using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: mask values held in registers, 2 waves/SIMD
-using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: twice the staging registers per tile
+// BM 128, 8 waves: 4 row groups x 2 key splits, 32-key tiles, 4 waves/SIMD; bf16 K/V copied global -> LDS by
+// direct loads (the boundary requires 16-byte aligned bases and strides that are multiples of 8 elements)
+using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true, 0, false, false, true>;
+using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: register-staged tiles and mask values, 2 waves/SIMD
+using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: register-staged (converted) tiles
 using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 3, true>;  // BM 256, 8 waves of 32 rows, 2 waves per SIMD, 3 Q fragments in LDS, PV priority
 using PrefImgGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 0, false, true>;  // the same over bf16 tile images copied by DMA (no staging registers: Q fits in registers; no PV priority)
 using PrefCurImgGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 4, false, true>;  // current tokens over their images: the causal state needs 4 Q fragments in LDS to stay out of scratch
