@@ -402,6 +402,9 @@ def _launches(rows):
         e = by_id.setdefault(d, {"family": f, "grid": _grid(r), "kernel": r["Kernel_Name"], "row": r, "value": 0.0})
         if "Counter_Value" in r:
             e["value"] += float(r["Counter_Value"])
+            if r.get("Counter_Name"):
+                c = e.setdefault("counters", {})
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     ordered = [by_id[d] for d in sorted(by_id)]
     ours = [e for e in ordered if e["family"] != "copyBuffer"]
     for i, e in enumerate(ours):
@@ -427,6 +430,20 @@ cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/WRITE_SIZE -o
 cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/FETCH_SIZE_copy -o copy -- python3 <repo>/bench.py --copy-calibration
 cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/WRITE_SIZE_copy -o copy -- python3 <repo>/bench.py --copy-calibration
 python3 <repo>/bench.py --summarize <out>      # writes profiles/traffic.json and these summaries"""
+
+# Two counter passes over the same bench step (each within the per-block limits
+# of one rocprofv3 pass: at most 8 SQ and 2 GRBM counters).
+PMC_PASSES = {
+    "pmc1": "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+            "SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY SQ_INSTS_VALU GRBM_GUI_ACTIVE",
+    "pmc2": "SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_ACTIVE_INST_ANY "
+            "SQ_INSTS_SALU SQ_INSTS_VALU_CVT GRBM_GUI_ACTIVE",
+}
+PMC_COMMANDS = "\n".join(f"cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <out>/{d} -o run -- python3 "
+                         "<repo>/bench.py --steps 2 --warmup 1 --cpu-rows 0 --no-next" for d, c in PMC_PASSES.items())
+NEXT_COMMAND = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace_next -o next -- "
+                "python3 <repo>/bench.py --only next --cpu-rows 0")
+PCP_COMMAND = "python3 <repo>/bench.py --pcp-shapes > <out>/pcp.md"
 
 
 def summarize(prof_dir: str) -> None:
@@ -501,6 +518,119 @@ def summarize(prof_dir: str) -> None:
     bench_path = os.path.join(prof_dir, "bench.json")
     if os.path.exists(bench_path):
         _write_profiles(json.load(open(bench_path)), kernels, cal)
+    _write_pmc_profile(prof_dir, kernels)
+    _write_next_profile(prof_dir)
+    _write_pcp_profile(prof_dir)
+
+
+def _hash_line():
+    return (f"Measured on one MI355X (gfx950, 256 CUs) in the same lease as the other summaries, kernel code hash "
+            f"`{kernel_source_hash()}` (comments and layout ignored; `bench.py` -> `kernel_source_hash()`).")
+
+
+def _write_pmc_profile(prof_dir, kernels):
+    """profiles/pmc_instruction_mix__bench_step.md from the two counter passes
+    (<dir>/pmc1, <dir>/pmc2) and the kernel trace's durations (kernels)."""
+    import csv
+    import glob
+
+    merged, order = {}, []
+    for d in PMC_PASSES:
+        hits = sorted(glob.glob(os.path.join(prof_dir, d, "*counter_collection.csv")))
+        if not hits:
+            return
+        for e in _launches(list(csv.DictReader(open(hits[0])))):
+            if e["family"] == "copyBuffer":
+                continue
+            key = (e["role"], e["grid"])
+            if key not in merged:
+                merged[key] = {}
+                order.append(key)
+            for c, v in e.get("counters", {}).items():
+                merged[key].setdefault(c, []).append(v)
+    dur = {(e["role"], str(e["grid_work_items"])): e["avg_duration_ns"] for e in kernels.values()}
+    names = {(e["role"], str(e["grid_work_items"])): e["kernel"] for e in kernels.values()}
+    L = ["# Instruction mix and MFMA occupancy of the bench step (rocprofv3 counters)", "", _hash_line(), "",
+         "Commands (repository root copy `<repo>`, output dir `<out>`; two passes, each within the per-block counter "
+         "limits; the durations come from the kernel trace of the same lease):", "", "```", PMC_COMMANDS, "```", "",
+         "Per launch (mean over the launches of each kernel and grid), wave-level instruction counts. "
+         "`SQ_INSTS_VALU` counts the MFMA instructions too; the VALU column is `SQ_INSTS_VALU - SQ_INSTS_MFMA`. "
+         "MFMA busy: `SQ_VALU_MFMA_BUSY_CYCLES` (cycles the matrix cores are busy, summed over the SIMDs) over "
+         "the SIMD cycles available while the kernel runs (`GRBM_GUI_ACTIVE`, summed over the 8 XCDs, / 8 x 1024 "
+         "SIMDs); clock: `GRBM_GUI_ACTIVE` / 8 over the traced duration.", "",
+         "| kernel (role, grid) | MFMA insts | VALU insts | VALU / MFMA | exp2 (trans) / MFMA | cvt / MFMA | "
+         "LDS insts / MFMA | LDS bank conflicts | wait-any / wave cycles | MFMA busy | clock (GHz) |",
+         "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key in order:
+        c = {k: statistics.fmean(v) for k, v in merged[key].items()}
+        mf, va = c.get("SQ_INSTS_MFMA", 0.0), c.get("SQ_INSTS_VALU", 0.0) - c.get("SQ_INSTS_MFMA", 0.0)
+        per = (lambda x: f"{x / mf:.2f}") if mf else (lambda x: "-")
+        gui, t = c.get("GRBM_GUI_ACTIVE"), dur.get(key)
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui / 8 * 1024) if gui else None
+        clk = gui / 8 / t if gui and t else None
+        wa = c.get("SQ_WAIT_INST_ANY", 0.0) / c["SQ_WAVE_CYCLES"] if c.get("SQ_WAVE_CYCLES") else None
+        L.append(f"| `{key[0]}` ({key[1]}) | {mf:.4g} | {va:.4g} | {per(va)} | {per(c.get('SQ_INSTS_VALU_TRANS_F32', 0))} | "
+                 f"{per(c.get('SQ_INSTS_VALU_CVT', 0))} | {per(c.get('SQ_INSTS_LDS', 0))} | "
+                 f"{c.get('SQ_LDS_BANK_CONFLICT', 0):.3g} | {'-' if wa is None else f'{wa:.2f}'} | "
+                 f"{'-' if busy is None else f'{100 * busy:.0f}%'} | {'-' if clk is None else f'{clk:.2f}'} |")
+    L += ["", "Full kernel names:", ""]
+    L += [f"- `{k[0]}` ({k[1]}): `{names.get(k, '?')}`" for k in order]
+    L += ["", "Raw counter means per launch:", "", "| kernel (role, grid) | " + " | ".join(
+        sorted({n for k in order for n in merged[k]})) + " |"]
+    cols = sorted({n for k in order for n in merged[k]})
+    L.append("|---|" + "---|" * len(cols))
+    for key in order:
+        L.append(f"| `{key[0]}` ({key[1]}) | " + " | ".join(
+            f"{statistics.fmean(merged[key][n]):.4g}" if n in merged[key] else "-" for n in cols) + " |")
+    with open(os.path.join(ROOT, "profiles", "pmc_instruction_mix__bench_step.md"), "w") as f:
+        f.write("\n".join(L) + "\n")
+    print("wrote profiles/pmc_instruction_mix__bench_step.md")
+
+
+def _write_next_profile(prof_dir):
+    """profiles/next_workloads__kernel_trace.md from <dir>/trace_next (one call
+    of time_next_workloads under the kernel trace)."""
+    import csv
+    import glob
+
+    hits = sorted(glob.glob(os.path.join(prof_dir, "trace_next", "*kernel_trace.csv")))
+    if not hits:
+        return
+    by = {}
+    for r in csv.DictReader(open(hits[0])):
+        by.setdefault(r["Kernel_Name"], []).append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3)
+    L = ["# Workload variants reported under `parts.next` (kernel trace)", "", _hash_line(), "",
+         "Command (repository root copy `<repo>`, output dir `<out>`):", "", "```", NEXT_COMMAND, "```", "",
+         "One call of `time_next_workloads` (each workload: warm-up calls, then timed calls): the V-JEPA2 64-frame "
+         "clip (8192 tokens, attention alone); a gte-base batch right-padded to 512 tokens (mask, residual, "
+         "LayerNorm); decode at head_dim 512 and over a 1024-key sliding window at head_dim 256; V-JEPA2 and DINOv3 "
+         "attention with RoPE (`rope_k_kernel` rotates K once); the paged prefill with causal current tokens. "
+         "Kernels by total time:", "",
+         "| kernel | calls | avg (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        L.append(f"| `{name}` | {len(v)} | {statistics.fmean(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    with open(os.path.join(ROOT, "profiles", "next_workloads__kernel_trace.md"), "w") as f:
+        f.write("\n".join(L) + "\n")
+    print("wrote profiles/next_workloads__kernel_trace.md")
+
+
+def _write_pcp_profile(prof_dir):
+    """profiles/prefill_pcp_q_scaling__hist8192.md from <dir>/pcp.md (the
+    --pcp-shapes table of the same lease)."""
+    path = os.path.join(prof_dir, "pcp.md")
+    if not os.path.exists(path):
+        return
+    table = [l.rstrip("\n") for l in open(path) if l.startswith("|")]
+    L = ["# Paged prefill at the PCP page's Q-scaling shapes (32 Q / 2 KV heads, D 256, 8192 history keys)", "",
+         _hash_line(), "", "Command (repository root copy `<repo>`, output dir `<out>`):", "", "```", PCP_COMMAND,
+         "```", "",
+         "Each entry point is timed over 10 back-to-back calls after 3 warm-up calls, with HIP events on the stream "
+         "the library launches on; inputs are seeded synthetic tensors of the shapes, 512-token blocks under a "
+         "permuted block table.  FLOPs are 4 * Lq * 32 * 8192 * 256 (QK^T + PV).  The page's column is its own "
+         "table, on four Trainium2 chips: another machine, context only.", ""] + table
+    with open(os.path.join(ROOT, "profiles", "prefill_pcp_q_scaling__hist8192.md"), "w") as f:
+        f.write("\n".join(L) + "\n")
+    print("wrote profiles/prefill_pcp_q_scaling__hist8192.md")
 
 
 def _kernel_rows(ks):

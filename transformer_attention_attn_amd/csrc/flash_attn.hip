@@ -116,7 +116,8 @@ struct Geo {
   static constexpr int KTILE = LINEAR ? BN * D * 2 : BN * KROW;
   static constexpr int VTILE = LINEAR ? BN * D * 2 : BN * D * 2 + (BN >> VSH) * 64;
   static constexpr int KSLOT = NSPLIT * KTILE;                    // one K buffer: every split's tile
-  static constexpr int VSLOT = NSPLIT * VTILE + NSPLIT * BN * 4;  // one V buffer, then the tiles' staged key mask
+  // one V buffer, then the tiles' staged key mask (none over direct copies)
+  static constexpr int VSLOT = NSPLIT * VTILE + (EDMA ? 0 : NSPLIT * BN * 4);
   static constexpr int KB = BN / 32;  // 32-key blocks per tile
   static constexpr int SD = D / 16;   // k-steps of the QK^T contraction
   static constexpr int MT = D / 32;   // d tiles of O^T
@@ -134,7 +135,11 @@ struct Geo {
   // the VALU-bound encoder gains nothing).
   static constexpr bool PVPRIO = PVPRIO_;
   static constexpr int QOFF = NBUF * (KSLOT + VSLOT) > MERGE ? NBUF * (KSLOT + VSLOT) : MERGE;
-  static constexpr int LDS = QOFF + QL * NT * THREADS * 16;  // K/V double buffers (or merge space), Q slots
+  // EDMA: the tile's fp32 residual rows (BM x D), copied to LDS with the first
+  // K/V tiles and read by the epilogue (ResRows); apart from buffers and merge
+  // space.  At D = 64 the whole geometry takes 80 KiB: two workgroups per CU.
+  static constexpr int RES = EDMA ? BM * D * 4 : 0;
+  static constexpr int LDS = QOFF + QL * NT * THREADS * 16 + RES;  // buffers (or merge space), Q slots, residual
   // softmax VALU instructions issued between consecutive QK MFMA groups
   static constexpr int VPM = (NT * (7 * BN / 4 + 8) + NFQ - 1) / NFQ;
   static_assert(D % 64 == 0 && BN % 32 == 0 && (VSH == 0 || D == 64), "tile shape");
@@ -499,6 +504,34 @@ struct EncDmaSrc {
     for (int j = 0; j < PW; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + (wave + j * G::WAVES) * 1024),
                                                16, voff[j], 0, 0, 0);
+  }
+};
+
+// The fp32 residual rows of an encoder tile (BM rows x D columns of the
+// token-major [B, Sq, H*D] stream) copied global -> LDS by direct loads
+// (G::EDMA): 1 KB pieces of 4 rows, wave w copying pieces w, w + WAVES, ...
+// Row r's 16-byte chunk c lands at r*D*4 + 16*(c ^ (r % 16)), so that the
+// epilogue's reads (32 consecutive rows, one chunk) spread over the banks.
+// Rows past the tile's nrows fall outside the buffer range and read as zeros;
+// every offset is in the lane's VGPR, where the range check sees it.
+template <class G>
+struct ResRows {
+  static __device__ __forceinline__ void copy(const float *tile, int nrows, int hidden, char *dst, int wave,
+                                              int lane) {
+    static_assert(G::D * 4 == 256 && (4 * G::WAVES) % 16 == 0 && (G::BM / 4) % G::WAVES == 0, "residual pieces");
+    const uint32_t stride = (uint32_t)hidden * 4;
+    const auto r = make_rsrc(tile, nrows > 0 ? (uint32_t)(nrows - 1) * stride + G::D * 4 : 0u);
+    const int row = 4 * wave + (lane >> 4);  // row of piece `wave`; later pieces add 4 * WAVES rows
+    const uint32_t off = (uint32_t)row * stride + 16 * ((lane & 15) ^ (row & 15));
+#pragma unroll
+    for (int j = 0; j < G::BM / 4 / G::WAVES; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void *)(dst + (wave + j * G::WAVES) * 1024), 16,
+          off + (uint32_t)(j * 4 * G::WAVES) * stride, 0, 0, 0);
+  }
+  // columns d0 .. d0 + 3 (d0 a multiple of 4) of tile row `row`, as copy left them
+  static __device__ __forceinline__ f32x4_t read(const char *src, int row, int d0) {
+    return *reinterpret_cast<const f32x4_t *>(src + row * (G::D * 4) + 16 * ((d0 >> 2) ^ (row & 15)));
   }
 };
 
@@ -1276,6 +1309,9 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   WaveState<G> ws;
   if constexpr (G::EDMA) {
     static_assert(!F32IN && !HAS_MASK, "direct copies: bf16 rows, no additive mask");
+    if (a.res_out)  // the residual rows land with the first tiles (the loop's first wait covers them)
+      ResRows<G>::copy(a.res + ((int64_t)b * a.Sq + row0) * (a.H * G::D) + h * G::D, nrow, a.H * G::D,
+                  smem + G::LDS - G::RES, __builtin_amdgcn_readfirstlane(wave), lane);
     EncDmaSrc<G> ds;
     ds.kb = src.kb;
     ds.vb = src.vb;
@@ -1294,7 +1330,7 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   // overlaps it.
   const int HD = a.H * G::D;
   f32x4_t resv[G::NT][G::MT][4];
-  if (a.res_out && sp == 0) {
+  if (!G::EDMA && a.res_out && sp == 0) {
 #pragma unroll
     for (int nt = 0; nt < G::NT; ++nt) {
       const int row = qt * G::BM + (rg * G::NT + nt) * 32 + l32;
@@ -1309,6 +1345,15 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   }
   merge_splits<G>(ws, smem);
   if (sp != 0) return;
+  if (G::EDMA && a.res_out) {  // residual rows from LDS (ResRows; merge_splits uses other bytes)
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          resv[nt][mt][r4] = ResRows<G>::read(smem + G::LDS - G::RES, (rg * G::NT + nt) * 32 + l32, mt * 32 + r4 * 8 + 4 * hh);
+  }
 
 #pragma unroll
   for (int nt = 0; nt < G::NT; ++nt) {
