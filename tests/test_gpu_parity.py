@@ -85,6 +85,34 @@ def test_encoder_small_cases(gpu_lib, B, H, S, lens, fp32):
     _enc_check(gpu_lib, case, f"custom B{B} H{H} S{S} mask={lens} fp32={fp32}")
 
 
+@pytest.mark.parametrize("B,H,Sq,Skv", [
+    (1, 2, 100, 1),     # one key; a single, short row tile
+    (2, 1, 129, 31),    # fewer keys than one tile; two row tiles, the second of one row
+    (1, 3, 64, 65),     # one key past a whole key step
+    (2, 2, 300, 129),   # both ragged
+])
+def test_encoder_cross_lengths_block(gpu_lib, B, H, Sq, Skv):
+    """S_q != S_kv, bf16, no mask (the tiles copied global -> LDS directly,
+    the residual rows with them), the whole block checked: the key tail and
+    the last row tile's missing rows come from the loads' range checks."""
+    g = torch.Generator().manual_seed(9000 + Sq + Skv)
+    bf = lambda *s: torch.randn(*s, generator=g).to(torch.bfloat16)
+    D = 64
+    q, k, v = bf(B, H, Sq, D), bf(B, H, Skv, D), bf(B, H, Skv, D)
+    res = torch.randn(B, Sq, H * D, generator=g)
+    gamma, beta = torch.rand(H * D, generator=g) + 0.5, torch.randn(H * D, generator=g) * 0.3
+    _say(f"[encoder] cross lengths B={B} H={H} Sq={Sq} Skv={Skv}")
+    r = gpu_lib.attn_encoder_fwd(q.to(DEV), k.to(DEV), v.to(DEV), 0.125, None, residual=res.to(DEV),
+                                 gamma=gamma.to(DEV), beta=beta.to(DEV), eps=1e-6, want_ln=True)
+    torch.cuda.synchronize()
+    ref = oracle.encoder_block(q, k, v, 0.125, res, gamma, beta, 1e-6)
+    what = f"cross Sq={Sq} Skv={Skv}"
+    assert_close(r["out"], ref["attn"], f"{what} attention")
+    assert_close(r["residual_out"], ref["res_out"], f"{what} residual_out")
+    assert_close(r["ln_out"], ref["ln_out"], f"{what} ln_out")
+    assert_ln_stats(r["residual_out"], r["ln_mean"], r["ln_rstd"], gamma, beta, 1e-6, what)
+
+
 def test_encoder_token_major_output_and_lse(gpu_lib):
     case = W.encoder_custom(5, 2, 4, 300, masked_lens=[300, 211])
     _say("[encoder] token-major out + lse")
