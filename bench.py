@@ -439,6 +439,7 @@ PMC_PASSES = {
     "pmc2": "SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_ACTIVE_INST_ANY "
             "SQ_INSTS_SALU SQ_INSTS_VALU_CVT GRBM_GUI_ACTIVE",
 }
+N_SE = 32  # shader engines of the MI355X (4 per XCD)
 PMC_COMMANDS = "\n".join(f"cd /tmp && rocprofv3 --pmc {c} --output-format csv -d <out>/{d} -o run -- python3 "
                          "<repo>/bench.py --steps 2 --warmup 1 --cpu-rows 0 --no-next" for d, c in PMC_PASSES.items())
 NEXT_COMMAND = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace_next -o next -- "
@@ -555,9 +556,12 @@ def _write_pmc_profile(prof_dir, kernels):
          "limits; the durations come from the kernel trace of the same lease):", "", "```", PMC_COMMANDS, "```", "",
          "Per launch (mean over the launches of each kernel and grid), wave-level instruction counts. "
          "`SQ_INSTS_VALU` counts the MFMA instructions too; the VALU column is `SQ_INSTS_VALU - SQ_INSTS_MFMA`. "
-         "MFMA busy: `SQ_VALU_MFMA_BUSY_CYCLES` (cycles the matrix cores are busy, summed over the SIMDs) over "
-         "the SIMD cycles available while the kernel runs (`GRBM_GUI_ACTIVE`, summed over the 8 XCDs, / 8 x 1024 "
-         "SIMDs); clock: `GRBM_GUI_ACTIVE` / 8 over the traced duration.", "",
+         "MFMA busy: `SQ_VALU_MFMA_BUSY_CYCLES` (cycles the matrix cores are busy, summed over the 1024 SIMDs) over "
+         f"the SIMD cycles of the kernel's active time, `SQ_BUSY_CYCLES` / {N_SE} x 1024 (`SQ_BUSY_CYCLES` sums the "
+         f"{N_SE} shader engines: over the 12 ms prefill it reads about 30.5 x `GRBM_GUI_ACTIVE` / 8, i.e. {N_SE} "
+         "engines busy ~95% of the time; `GRBM_GUI_ACTIVE` itself also counts each dispatch's idle overhead under "
+         f"counter collection, which dominates a 5-30 us kernel).  Clock: `SQ_BUSY_CYCLES` / {N_SE} over the traced "
+         "duration.", "",
          "| kernel (role, grid) | MFMA insts | VALU insts | VALU / MFMA | exp2 (trans) / MFMA | cvt / MFMA | "
          "LDS insts / MFMA | LDS bank conflicts | wait-any / wave cycles | MFMA busy | clock (GHz) |",
          "|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -565,9 +569,9 @@ def _write_pmc_profile(prof_dir, kernels):
         c = {k: statistics.fmean(v) for k, v in merged[key].items()}
         mf, va = c.get("SQ_INSTS_MFMA", 0.0), c.get("SQ_INSTS_VALU", 0.0) - c.get("SQ_INSTS_MFMA", 0.0)
         per = (lambda x: f"{x / mf:.2f}") if mf else (lambda x: "-")
-        gui, t = c.get("GRBM_GUI_ACTIVE"), dur.get(key)
-        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui / 8 * 1024) if gui else None
-        clk = gui / 8 / t if gui and t else None
+        sq, t = c.get("SQ_BUSY_CYCLES"), dur.get(key)
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (sq / N_SE * 1024) if sq else None
+        clk = sq / N_SE / t if sq and t else None
         wa = c.get("SQ_WAIT_INST_ANY", 0.0) / c["SQ_WAVE_CYCLES"] if c.get("SQ_WAVE_CYCLES") else None
         L.append(f"| `{key[0]}` ({key[1]}) | {mf:.4g} | {va:.4g} | {per(va)} | {per(c.get('SQ_INSTS_VALU_TRANS_F32', 0))} | "
                  f"{per(c.get('SQ_INSTS_VALU_CVT', 0))} | {per(c.get('SQ_INSTS_LDS', 0))} | "
