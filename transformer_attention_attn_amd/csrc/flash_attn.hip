@@ -1309,7 +1309,9 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   WaveState<G> ws;
   if constexpr (G::EDMA) {
     static_assert(!F32IN && !HAS_MASK, "direct copies: bf16 rows, no additive mask");
-    if (a.res_out)  // the residual rows land with the first tiles (the loop's first wait covers them)
+    // the residual rows land with the first tiles: the loop's first wait covers them (S_kv >= 1 is
+    // checked at the boundary, so the loop always runs)
+    if (a.res_out)
       ResRows<G>::copy(a.res + ((int64_t)b * a.Sq + row0) * (a.H * G::D) + h * G::D, nrow, a.H * G::D,
                   smem + G::LDS - G::RES, __builtin_amdgcn_readfirstlane(wave), lane);
     EncDmaSrc<G> ds;
