@@ -138,3 +138,42 @@ def test_encoder_rope_block_in_a_graph(gpu_lib):
     _say("[graph] RoPE pass + encoder attention + residual/LayerNorm")
     _replays_match(call, out, eager)
     assert torch.equal(ln, eager_ln)
+
+
+def test_encoder_block_direct_copies_in_a_graph(gpu_lib):
+    """The bf16 block without a mask (K, V and the residual rows copied global
+    -> LDS directly) then the LayerNorm pass, DINOv3's ragged shape: every
+    output of every replay equals the eager call's."""
+    taa = gpu_lib
+    case = W.encoder_dinov3()
+    d = lambda t: t.to(DEV)
+    q, k, v, res, gam, bet = d(case.q), d(case.k), d(case.v), d(case.residual), d(case.gamma), d(case.beta)
+    out = torch.empty_like(q)
+    res_out = torch.empty_like(res)
+    ln = torch.empty(case.B, case.S, case.H * case.D, dtype=torch.bfloat16, device=DEV)
+    mean = torch.empty(case.B * case.S, device=DEV)
+    rstd = torch.empty(case.B * case.S, device=DEV)
+    call = lambda: taa.attn_encoder_fwd(q, k, v, case.scale, None, out=out, residual=res, residual_out=res_out,
+                                        gamma=gam, beta=bet, eps=case.eps, ln_out=ln, ln_mean=mean, ln_rstd=rstd)
+    call()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (out, res_out, ln, mean, rstd)]
+    _say("[graph] encoder block over direct copies + LayerNorm (DINOv3 shape)")
+    outs, names = (out, res_out, ln, mean, rstd), ("out", "residual_out", "ln_out", "mean", "rstd")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for i in range(3):
+        for t in outs:
+            t.zero_()  # eager work between the replays; every output must be rewritten
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e, name in zip(outs, eager, names):
+            assert torch.equal(t, e), f"replay {i}: {name} differs from the eager call"
