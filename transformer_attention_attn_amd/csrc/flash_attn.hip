@@ -75,7 +75,7 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 
 template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int OCC_, bool VFIRST_ = false, int QL_ = 0,
-          bool PVPRIO_ = false, bool DMA_ = false, bool EDMA_ = false>
+          bool PVPRIO_ = false, bool DMA_ = false, bool EDMA_ = false, bool RARE_ALPHA_ = false>
 struct Geo {
   static constexpr int D = D_, BN = BN_, NT = NT_, RG = RG_, NSPLIT = NSPLIT_;
   static constexpr int GRP = GRP_;  // LDS fragments read ahead of the MFMAs that use them
@@ -112,6 +112,13 @@ struct Geo {
   // (v_frag_edma), which stands in for the padding a direct load cannot make.
   static constexpr bool EDMA = EDMA_;
   static constexpr bool LINEAR = DMA || EDMA;  // tiles land unpadded, K chunk-major
+  // RARE_ALPHA: phase A hands out the rescale exponent and the caller takes
+  // its exp2 on the rare path where some row's reference moved, instead of
+  // one exp2 per row and tile on the common path; the tile's row sum then
+  // starts from zero and joins l at the end of the step.  Carrying both
+  // across the phases costs registers (kept off where the key loop would
+  // spill).
+  static constexpr bool RARE_ALPHA = RARE_ALPHA_;
   static constexpr int NBUF = LINEAR ? 3 : 2;
   static constexpr int KTILE = LINEAR ? BN * D * 2 : BN * KROW;
   static constexpr int VTILE = LINEAR ? BN * D * 2 : BN * D * 2 + (BN >> VSH) * 64;
@@ -740,11 +747,14 @@ __device__ __forceinline__ u32x4_t p_frag(const PCarry<G> &pc, int nt, int kb, i
 // > 0.  With a mask, mk (LDS) holds this tile's additive mask in log2 units,
 // -inf for removed keys.  Computes the first half of P (the keys the first
 // PV MFMAs consume), updates m, and returns whether any row's reference max
-// moved (then O must be multiplied by alpha before PV).
+// moved: then O must be multiplied by alpha before PV.  la is alpha (1 for the
+// rows that keep their reference), or with G::RARE_ALPHA its log2 (old
+// reference - new, 0 for those rows): the caller takes the exp2 on that rare
+// path, and rescales l there too.
 //
 // Slot f issues QK MFMA f and the K read GRP fragments ahead, and a slice of
 // the softmax (before or after the MFMA, G::VFIRST): slot 0 the row max, slot
-// 1 the cross-lane max, the rescale decision and alpha, later slots the exp2
+// 1 the cross-lane max, the rescale decision and la, later slots the exp2
 // / bf16 pack / row sum of P pairs.
 // sched_barrier(0) and the pins hold that order, so this wave's MFMAs run
 // under its own VALU work; the second half of P is left to phase B, which
@@ -755,10 +765,12 @@ __device__ __forceinline__ u32x4_t p_frag(const PCarry<G> &pc, int nt, int kb, i
 // rescale (a VALU pass over every accumulator, skipped unless some row of the
 // wave moved) is rare.  Exact: the final O/l uses one
 // consistent reference per row.  The row sum is taken on the packed bf16 P
-// (v_dot2_f32_bf16), so it normalises exactly the values multiplied into V.
+// (v_dot2_f32_bf16), so it normalises exactly the values multiplied into V;
+// with G::RARE_ALPHA the tile's sum starts from zero (pc.lsum) and joins l at
+// the end of phase B; otherwise it starts from l * alpha.
 template <class G, bool HAS_MASK>
 __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_t (&sn)[G::NT][G::KB],
-                                        f32x16_t (&s)[G::NT][G::KB], float (&alpha)[G::NT],
+                                        f32x16_t (&s)[G::NT][G::KB], float (&la)[G::NT],
                                         const u32x4_t (&qf)[G::NT][G::SD], const char *qa, const char *kt,
                                         const float *mk, float c, int lane) {
   constexpr int RA = G::GRP < G::NFQ ? G::GRP : G::NFQ;
@@ -860,13 +872,15 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
         // with no live key yet keeps m = -inf; its exponents use the lowest float
         // instead (-kFloatMax), which gives p = 0 for its -inf scores without a NaN.
         const float m_new = grow_row[nt] ? mx[nt] : ws.m[nt];
-        alpha[nt] = grow_row[nt] ? fast_exp2(ws.m[nt] - mx[nt]) : 1.0f;
+        // la: log2 of the rescale factor (G::RARE_ALPHA) or the factor itself
+        if constexpr (G::RARE_ALPHA) la[nt] = grow_row[nt] ? ws.m[nt] - mx[nt] : 0.0f;
+        else la[nt] = grow_row[nt] ? fast_exp2(ws.m[nt] - mx[nt]) : 1.0f;
         ws.m[nt] = m_new;
         pc.m_use[nt] = fmaxf(m_new, -kFloatMax);
-        pc.lsum[nt] = ws.l[nt] * alpha[nt];
+        pc.lsum[nt] = G::RARE_ALPHA ? 0.0f : ws.l[nt] * la[nt];
         pin_out(pc.m_use[nt]);
         pin_out(pc.lsum[nt]);
-        pin_out(alpha[nt]);
+        pin_out(la[nt]);
       }
     } else if constexpr (SPA > 0) {
       if ((f - 2) % SPA == 0 && (f - 2) / SPA < NP) p_pairs<G, HAS_MASK>(pc, s, 0, (f - 2) / SPA, (f - 2) / SPA + 1, c);
@@ -970,7 +984,7 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
     if (G::VFIRST) pv_slot(q);
   }
 #pragma unroll
-  for (int nt = 0; nt < G::NT; ++nt) ws.l[nt] = pc.lsum[nt];
+  for (int nt = 0; nt < G::NT; ++nt) ws.l[nt] = G::RARE_ALPHA ? ws.l[nt] + pc.lsum[nt] : pc.lsum[nt];
 }
 
 // ------------------------------------------------------------------ core loop
@@ -1039,15 +1053,18 @@ __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, con
     char *const vcur = vbuf + cur * G::VSLOT, *const vnext = vbuf + (cur ^ 1) * G::VSLOT;
 
     PCarry<G> pc;
-    float alpha[G::NT];
+    float la[G::NT];
     const bool any =
-        phase_a<G, HAS_MASK>(ws, pc, SN, S, alpha, qf, qa, knext + sp * G::KTILE,
+        phase_a<G, HAS_MASK>(ws, pc, SN, S, la, qf, qa, knext + sp * G::KTILE,
                              reinterpret_cast<const float *>(vcur + G::NSPLIT * G::VTILE) + sp * G::BN, c, lane);
-    if (any) {
+    if (any) {  // rare: the rows whose reference moved rescale O (and l) (alpha = 1 for the others)
 #pragma unroll
-      for (int nt = 0; nt < G::NT; ++nt)
+      for (int nt = 0; nt < G::NT; ++nt) {
+        const float alpha = G::RARE_ALPHA ? fast_exp2(la[nt]) : la[nt];
+        if constexpr (G::RARE_ALPHA) ws.l[nt] *= alpha;
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] *= alpha[nt];
+        for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] *= alpha;
+      }
     }
 
     // PV(it); stage K(it+2) and V(it+1); issue K(it+3) and V(it+2)
@@ -1118,13 +1135,16 @@ __device__ __forceinline__ void dma_loop_body(WaveState<G> &ws, const Src &src,
   auto step = [&](int it, char *__restrict__ kr, char *__restrict__ kw, char *__restrict__ vr,
                   char *__restrict__ vw, f32x16_t (&S)[G::NT][G::KB], f32x16_t (&SN)[G::NT][G::KB]) {
     PCarry<G> pc;
-    float alpha[G::NT];
-    const bool any = phase_a<G, false>(ws, pc, SN, S, alpha, qf, qa, kr + sp * G::KTILE, nullptr, c, lane);
-    if (any) {
+    float la[G::NT];
+    const bool any = phase_a<G, false>(ws, pc, SN, S, la, qf, qa, kr + sp * G::KTILE, nullptr, c, lane);
+    if (any) {  // rare: the rows whose reference moved rescale O (and l) (alpha = 1 for the others)
 #pragma unroll
-      for (int nt = 0; nt < G::NT; ++nt)
+      for (int nt = 0; nt < G::NT; ++nt) {
+        const float alpha = G::RARE_ALPHA ? fast_exp2(la[nt]) : la[nt];
+        if constexpr (G::RARE_ALPHA) ws.l[nt] *= alpha;
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] *= alpha[nt];
+        for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] *= alpha;
+      }
     }
     phase_b<G, false>(ws, pc, S, c, vr + sp * G::VTILE, lane, [&](int k) {
       if (k == 0) src.copy_k(kw, it + 3, wave, lane);
@@ -1614,7 +1634,7 @@ __global__ __launch_bounds__(256) void prefill_tile_images_kernel(PrefillLaunch 
 
 // BM 128, 8 waves: 4 row groups x 2 key splits, 32-key tiles, 4 waves/SIMD; bf16 K/V copied global -> LDS by
 // direct loads (the boundary requires 16-byte aligned bases and strides that are multiples of 8 elements)
-using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true, 0, false, false, true>;
+using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true, 0, false, false, true, true>;
 using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: register-staged tiles and mask values, 2 waves/SIMD
 using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: register-staged (converted) tiles
 using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 3, true>;  // BM 256, 8 waves of 32 rows, 2 waves per SIMD, 3 Q fragments in LDS, PV priority
