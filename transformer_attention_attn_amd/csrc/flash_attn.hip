@@ -555,6 +555,10 @@ template <class G>
 struct WaveState {
   f32x16_t o[G::NT][G::MT];
   float m[G::NT], l[G::NT];  // m: running reference max, log2 units
+  // G::RARE_ALPHA: the exponents' reference (m, or the lowest float while m =
+  // -inf) and the raw tile max above which m moves ((m + kTau) / c, -inf while
+  // m = -inf), both changed only when m does
+  float mu[G::RARE_ALPHA ? G::NT : 1], thr[G::RARE_ALPHA ? G::NT : 1];
 };
 
 // max / sum of a value with its partner lane (lane ^ 32) in one VALU op
@@ -857,30 +861,55 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
 #pragma unroll
       for (int nt = 0; nt < G::NT; ++nt) {
         const float m2 = pair_max(mx[nt]);
-        mx[nt] = HAS_MASK ? m2 : m2 * c;  // -inf * c = -inf (c > 0)
-        grow_row[nt] = mx[nt] > ws.m[nt] + kTau;
+        if constexpr (G::RARE_ALPHA) {
+          static_assert(!HAS_MASK, "raw-unit threshold: scores without an additive mask");
+          mx[nt] = m2;  // raw units; scaled on the rare path
+          grow_row[nt] = m2 > ws.thr[nt];
+        } else {
+          mx[nt] = HAS_MASK ? m2 : m2 * c;  // -inf * c = -inf (c > 0)
+          grow_row[nt] = mx[nt] > ws.m[nt] + kTau;
+        }
         grow |= grow_row[nt];
       }
       any = __ballot(grow) != 0;
+      // per row: a row's reference moves only on its own scores, so its
+      // result never depends on the other rows of the wave (alpha = 1 leaves
+      // the rows that keep theirs bit-identical).  A growing row's tile max
+      // exceeds its old reference, so it is the new one, and is finite:
+      // exp2(m - mx) is 0 for a first live tile (m = -inf).  A row with no
+      // live key yet keeps m = -inf; its exponents use the lowest float
+      // instead (-kFloatMax), which gives p = 0 for its -inf scores without a NaN.
+      if constexpr (G::RARE_ALPHA) {
+        if (any) {  // rare: the rows whose reference moves
 #pragma unroll
-      for (int nt = 0; nt < G::NT; ++nt) {
-        // per row: a row's reference moves only on its own scores, so its
-        // result never depends on the other rows of the wave (alpha = 1
-        // leaves the rows that keep theirs bit-identical).  A growing row's
-        // tile max exceeds its old reference, so it is the new one, and is
-        // finite: exp2(m - mx) is 0 for a first live tile (m = -inf).  A row
-        // with no live key yet keeps m = -inf; its exponents use the lowest float
-        // instead (-kFloatMax), which gives p = 0 for its -inf scores without a NaN.
-        const float m_new = grow_row[nt] ? mx[nt] : ws.m[nt];
-        // la: log2 of the rescale factor (G::RARE_ALPHA) or the factor itself
-        if constexpr (G::RARE_ALPHA) la[nt] = grow_row[nt] ? ws.m[nt] - mx[nt] : 0.0f;
-        else la[nt] = grow_row[nt] ? fast_exp2(ws.m[nt] - mx[nt]) : 1.0f;
-        ws.m[nt] = m_new;
-        pc.m_use[nt] = fmaxf(m_new, -kFloatMax);
-        pc.lsum[nt] = G::RARE_ALPHA ? 0.0f : ws.l[nt] * la[nt];
-        pin_out(pc.m_use[nt]);
-        pin_out(pc.lsum[nt]);
-        pin_out(la[nt]);
+          for (int nt = 0; nt < G::NT; ++nt) {
+            const float mxc = mx[nt] * c;
+            const float m_new = grow_row[nt] ? mxc : ws.m[nt];
+            la[nt] = grow_row[nt] ? ws.m[nt] - mxc : 0.0f;
+            ws.m[nt] = m_new;
+            ws.mu[nt] = fmaxf(m_new, -kFloatMax);
+            ws.thr[nt] = grow_row[nt] ? (m_new + kTau) * (1.0f / c) : ws.thr[nt];
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt) {
+          pc.m_use[nt] = ws.mu[nt];
+          pc.lsum[nt] = 0.0f;
+          pin_out(pc.m_use[nt]);
+          pin_out(pc.lsum[nt]);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt) {
+          const float m_new = grow_row[nt] ? mx[nt] : ws.m[nt];
+          la[nt] = grow_row[nt] ? fast_exp2(ws.m[nt] - mx[nt]) : 1.0f;
+          ws.m[nt] = m_new;
+          pc.m_use[nt] = fmaxf(m_new, -kFloatMax);
+          pc.lsum[nt] = ws.l[nt] * la[nt];
+          pin_out(pc.m_use[nt]);
+          pin_out(pc.lsum[nt]);
+          pin_out(la[nt]);
+        }
       }
     } else if constexpr (SPA > 0) {
       if ((f - 2) % SPA == 0 && (f - 2) / SPA < NP) p_pairs<G, HAS_MASK>(pc, s, 0, (f - 2) / SPA, (f - 2) / SPA + 1, c);
@@ -1003,6 +1032,7 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
 template <class G, bool HAS_MASK, class Src, class Mask>
 __device__ __forceinline__ void flash_loop(WaveState<G> &ws, const Src &src, const u32x4_t (&qf)[G::NT][G::SD],
                                            char *smem, float c, const Mask &mk, bool fresh, unsigned tid) {
+  static_assert(!G::RARE_ALPHA, "the rare-path rescale state is set up by flash_loop_dma");
   const int lane = tid & 63;
   const int sp = __builtin_amdgcn_readfirstlane((int)(tid >> 6)) / G::RG;
   const int n_tiles = (src.n_keys + G::BN - 1) / G::BN;
@@ -1186,6 +1216,13 @@ __device__ __forceinline__ void flash_loop_dma(WaveState<G> &ws, const Src &src,
       ws.l[nt] = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] = f32x16_t{};
+    }
+  }
+  if constexpr (G::RARE_ALPHA) {  // from m (fresh: -inf, so any live key moves it)
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) {
+      ws.mu[nt] = fmaxf(ws.m[nt], -kFloatMax);
+      ws.thr[nt] = ws.m[nt] == -INFINITY ? -INFINITY : (ws.m[nt] + kTau) * (1.0f / c);
     }
   }
   if (n_iter <= 0) return;
