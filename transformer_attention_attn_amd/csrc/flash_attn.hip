@@ -53,6 +53,7 @@
 namespace mi355 {
 
 constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
+constexpr float kSumTrig = 256.0f;      // 2^kTau: a half-tile row sum above it may need a new reference
 constexpr float kFloatMax = __FLT_MAX__;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer resource word 3 (gfx9 family: 32-bit data format, no swizzle)
 
@@ -75,7 +76,8 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 
 template <int D_, int BN_, int NT_, int RG_, int NSPLIT_, int GRP_, int OCC_, bool VFIRST_ = false, int QL_ = 0,
-          bool PVPRIO_ = false, bool DMA_ = false, bool EDMA_ = false, bool RARE_ALPHA_ = false>
+          bool PVPRIO_ = false, bool DMA_ = false, bool EDMA_ = false, bool RARE_ALPHA_ = false,
+          bool LAZYSUM_ = false>
 struct Geo {
   static constexpr int D = D_, BN = BN_, NT = NT_, RG = RG_, NSPLIT = NSPLIT_;
   static constexpr int GRP = GRP_;  // LDS fragments read ahead of the MFMAs that use them
@@ -119,6 +121,14 @@ struct Geo {
   // across the phases costs registers (kept off where the key loop would
   // spill).
   static constexpr bool RARE_ALPHA = RARE_ALPHA_;
+  // LAZYSUM (with RARE_ALPHA): no row max on the common path.  While a row's
+  // reference holds, every p = 2^(s c - m) is at most 2^kTau, so a half
+  // tile's row sum (which the dot2s take anyway) above 2^kTau is a
+  // conservative sign that it may have to move: only then is the tile max
+  // taken, the reference moved and the half's P recomputed (same bits for
+  // the rows that keep their reference).  Phase A checks the first half
+  // before the PV MFMAs use it, phase B the second half before its MFMAs.
+  static constexpr bool LAZYSUM = LAZYSUM_;
   static constexpr int NBUF = LINEAR ? 3 : 2;
   static constexpr int KTILE = LINEAR ? BN * D * 2 : BN * KROW;
   static constexpr int VTILE = LINEAR ? BN * D * 2 : BN * D * 2 + (BN >> VSH) * 64;
@@ -746,6 +756,36 @@ __device__ __forceinline__ u32x4_t p_frag(const PCarry<G> &pc, int nt, int kb, i
   return u32x4_t{pc.w[nt][kb][4 * kk], pc.w[nt][kb][4 * kk + 1], pc.w[nt][kb][4 * kk + 2], pc.w[nt][kb][4 * kk + 3]};
 }
 
+// LAZYSUM: the rows whose half-tile sum went past 2^kTau (own lane or its
+// partner) take the tile's max and move their reference when it exceeds the
+// old one by more than kTau (the raw-unit threshold).  Returns per row
+// whether it moved and the old reference (for the rescale); updates m, the
+// exponents' reference and the threshold.
+template <class G>
+__device__ __forceinline__ bool lazy_redecide(WaveState<G> &ws, const f32x16_t (&s)[G::NT][G::KB],
+                                              const bool (&trig)[G::NT], float c, bool (&grow)[G::NT],
+                                              float (&m_old)[G::NT]) {
+  bool any = false;
+#pragma unroll
+  for (int nt = 0; nt < G::NT; ++nt) {
+    const bool row_trig = pair_max(trig[nt] ? 1.0f : 0.0f) > 0.0f;
+    float mx = s[nt][0][0];
+#pragma unroll
+    for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = __builtin_fmaxf(mx, s[nt][kb][v]);
+    mx = pair_max(mx);
+    grow[nt] = row_trig && mx > ws.thr[nt];
+    m_old[nt] = ws.m[nt];
+    const float m_new = grow[nt] ? mx * c : ws.m[nt];
+    ws.m[nt] = m_new;
+    ws.mu[nt] = fmaxf(m_new, -kFloatMax);
+    ws.thr[nt] = grow[nt] ? (m_new + kTau) * (1.0f / c) : ws.thr[nt];
+    any |= grow[nt];
+  }
+  return __ballot(any) != 0;
+}
+
 // Phase A of one tile step: S(next) = K(next) Q^T on MFMA, interleaved with
 // the online softmax of S (this tile) on the VALU.  c = softmax_scale*log2(e)
 // > 0.  With a mask, mk (LDS) holds this tile's additive mask in log2 units,
@@ -786,6 +826,16 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
   // its MFMA; otherwise PPS consecutive pairs per slot.
   constexpr int SPA = SLOTS >= NP && NP > 1 ? (SLOTS - 1) / (NP - 1) : 0;
   static_assert(SLOTS >= 1, "QK slots");
+  // LAZYSUM: the first half's pairs over all NFQ slots, PPA per slot
+  constexpr int PPA = (NP + G::NFQ - 1) / G::NFQ;
+  static_assert(!G::LAZYSUM || (G::RARE_ALPHA && G::VFIRST && !HAS_MASK), "lazy sum: rare rescale, VALU first");
+  if constexpr (G::LAZYSUM) {
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) {
+      pc.m_use[nt] = ws.mu[nt];
+      pc.lsum[nt] = 0.0f;
+    }
+  }
   const int h = lane >> 5;
   const char *kbase = kt + G::k_lane(lane);
 
@@ -829,7 +879,9 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
 #pragma unroll
   for (int f = 0; f < G::NFQ; ++f) {
     if (!G::VFIRST) qk_slot(f);
-    if (f == 0) {
+    if constexpr (G::LAZYSUM) {
+      if (f * PPA < NP) p_pairs<G, HAS_MASK>(pc, s, 0, f * PPA, (f + 1) * PPA < NP ? (f + 1) * PPA : NP, c);
+    } else if (f == 0) {
       // scores into log2 units (mask path) and the in-lane row max
 #pragma unroll
       for (int nt = 0; nt < G::NT; ++nt) {
@@ -920,6 +972,26 @@ __device__ __forceinline__ bool phase_a(WaveState<G> &ws, PCarry<G> &pc, f32x16_
     __builtin_amdgcn_sched_barrier(0);
     if (G::VFIRST) qk_slot(f);
   }
+  if constexpr (G::LAZYSUM) {
+    bool trig[G::NT], t = false;
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) {
+      trig[nt] = pc.lsum[nt] > kSumTrig;
+      t |= trig[nt];
+    }
+    if (__ballot(t) != 0) {  // rare
+      bool grow[G::NT];
+      float m_old[G::NT];
+      any = lazy_redecide<G>(ws, s, trig, c, grow, m_old);
+#pragma unroll
+      for (int nt = 0; nt < G::NT; ++nt) {
+        la[nt] = grow[nt] ? m_old[nt] - ws.m[nt] : 0.0f;
+        pc.m_use[nt] = ws.mu[nt];
+        pc.lsum[nt] = 0.0f;
+      }
+      p_pairs<G, HAS_MASK>(pc, s, 0, 0, NP, c);  // the first half again (same bits where the reference held)
+    }
+  }
   return any;
 }
 
@@ -983,6 +1055,7 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
 #pragma unroll
   for (int q = 0; q < RA; ++q) read(q);
   __builtin_amdgcn_sched_barrier(0);
+  static_assert(!G::LAZYSUM || PSLOTS <= G::MT, "lazy sum: the second half is complete before its MFMAs");
   auto pv_slot = [&](int q) {
     const int mt = q % G::MT, kk = (q / G::MT) % 2, kb = q / (2 * G::MT);
     pin_in(fb[q]);
@@ -998,6 +1071,38 @@ __device__ __forceinline__ void phase_b(WaveState<G> &ws, PCarry<G> &pc, const f
 #pragma unroll
   for (int q = 0; q < G::NFV; ++q) {
     if (!G::VFIRST) pv_slot(q);
+    if constexpr (G::LAZYSUM) {
+      if (q == G::MT) {  // the second half, before the first MFMA that uses it
+        bool trig[G::NT], t = false;
+#pragma unroll
+        for (int nt = 0; nt < G::NT; ++nt) {
+          trig[nt] = pc.lsum[nt] > kSumTrig;  // both halves so far: conservative
+          t |= trig[nt];
+        }
+        if (__ballot(t) != 0) {  // rare: O already holds the first half's products
+          bool grow[G::NT];
+          float m_old[G::NT];
+          lazy_redecide<G>(ws, s, trig, c, grow, m_old);
+          const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+#pragma unroll
+          for (int nt = 0; nt < G::NT; ++nt) {
+            const float alpha = grow[nt] ? fast_exp2(m_old[nt] - ws.m[nt]) : 1.0f;
+            ws.l[nt] *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt) ws.o[nt][mt] *= alpha;
+            float t1 = 0.0f;  // the first half's sum, in phase A's order
+#pragma unroll
+            for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+              for (int i8 = 0; i8 < 4; ++i8)
+                t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pc.w[nt][kb][i8]), ones, t1, false);
+            pc.lsum[nt] = t1 * alpha;
+            pc.m_use[nt] = ws.mu[nt];
+          }
+          p_pairs<G, HAS_MASK>(pc, s, 1, 0, NP, c);  // the second half again
+        }
+      }
+    }
     if constexpr (SPB > 0) {
       if (q % SPB == 0 && q / SPB < NP) p_pairs<G, HAS_MASK>(pc, s, 1, q / SPB, q / SPB + 1, c);
       else if (q >= G::MT && (q - G::MT) % WS == 0 && (q - G::MT) / WS <= 2) work((q - G::MT) / WS);
@@ -1158,6 +1263,24 @@ __device__ __forceinline__ void dma_loop_body(WaveState<G> &ws, const Src &src,
   f32x16_t s[G::NT][G::KB], s2[G::NT][G::KB];
   qk_tile<G>(s, qf, qa, kA + sp * G::KTILE, lane);
   mk.template apply<G>(s, sp * G::BN, lane);
+  if constexpr (G::LAZYSUM) {
+    // a row without a reference takes the first tile's max as its own, so
+    // the first step does not have to leave the common path to set it
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt) {
+      float mx = s[nt][0][0];
+#pragma unroll
+      for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = __builtin_fmaxf(mx, s[nt][kb][v]);
+      mx = pair_max(mx);
+      if (ws.m[nt] == -INFINITY && mx > -INFINITY) {
+        ws.m[nt] = mx * c;
+        ws.mu[nt] = ws.m[nt];
+        ws.thr[nt] = (ws.m[nt] + kTau) * (1.0f / c);
+      }
+    }
+  }
   lds_barrier();  // K(0) read by every wave before K(3) replaces it
 
   // kr: K(it+1), read; kw: K(it)'s buffer, receives K(it+3); vr: V(it), read;
@@ -1671,7 +1794,7 @@ __global__ __launch_bounds__(256) void prefill_tile_images_kernel(PrefillLaunch 
 
 // BM 128, 8 waves: 4 row groups x 2 key splits, 32-key tiles, 4 waves/SIMD; bf16 K/V copied global -> LDS by
 // direct loads (the boundary requires 16-byte aligned bases and strides that are multiples of 8 elements)
-using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true, 0, false, false, true, true>;
+using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true, 0, false, false, true, true, true>;
 using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: register-staged tiles and mask values, 2 waves/SIMD
 using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: register-staged (converted) tiles
 using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 3, true>;  // BM 256, 8 waves of 32 rows, 2 waves per SIMD, 3 Q fragments in LDS, PV priority
