@@ -90,6 +90,8 @@ def test_encoder_small_cases(gpu_lib, B, H, S, lens, fp32):
     (2, 1, 129, 31),    # fewer keys than one tile; two row tiles, the second of one row
     (1, 3, 64, 65),     # one key past a whole key step
     (2, 2, 300, 129),   # both ragged
+    (1, 4, 200, 1600),  # long enough for 64-key tiles; ragged last tile
+    (2, 3, 130, 2000),  # 64-key tiles, both ragged
 ])
 def test_encoder_cross_lengths_block(gpu_lib, B, H, Sq, Skv):
     """S_q != S_kv, bf16, no mask (the tiles copied global -> LDS directly,

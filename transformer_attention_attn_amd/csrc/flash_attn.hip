@@ -163,8 +163,8 @@ struct Geo {
   static_assert(QL >= 0 && QL <= SD, "Q fragments in LDS");
   static_assert(!DMA || (NSPLIT == 1 && BN == 32 && KTILE % 1024 == 0 && VTILE % 1024 == 0),
                 "tile images: one key split, 32-key tiles, 1 KB pieces");
-  static_assert(!EDMA || (!DMA && D == 64 && BN == 32 && QL == 0 && KSLOT % (1024 * WAVES) == 0),
-                "direct encoder tiles: 128-byte rows, 32-key tiles, whole rounds of 1 KB pieces");
+  static_assert(!EDMA || (!DMA && D == 64 && BN % 32 == 0 && QL == 0 && KSLOT % (1024 * WAVES) == 0),
+                "direct encoder tiles: 128-byte rows, 32-key blocks, whole rounds of 1 KB pieces");
   static_assert(LDS <= 160 * 1024, "LDS budget (gfx950: 160 KiB per workgroup)");
 
   static __device__ __forceinline__ int k_row(int key) { static_assert(!LINEAR, "padded K rows"); return key * KROW; }
@@ -472,8 +472,9 @@ struct TileImgSrc {
 // host).  An iteration's NSPLIT tiles of each operand are KSLOT / 1 KB pieces
 // and wave w copies pieces w, w + WAVES, ...; piece p belongs to split p / PT,
 // keys of that split's tile:
-//   K: lane L takes chunk c = 2 (p % PT) + L / 32 (d = 8c .. 8c + 7) of key
-//      L % 32, which lands at c * 512 + key * 16 (chunk-major);
+//   K: lane L takes element u = 64 (p % PT) + L of the tile's chunk-major
+//      order, chunk c = u / BN (d = 8c .. 8c + 7) of key u % BN, which lands
+//      at c * BN * 16 + key * 16;
 //   V: lane L lands at byte 16 L of the piece, key 8 (p % PT) + L / 8,
 //      physical chunk L % 8, and takes the key's logical chunk
 //      (L % 8) ^ (4 * key bit 1) (the half swap v_frag_edma undoes).
@@ -495,7 +496,7 @@ struct EncDmaSrc {
 #pragma unroll
     for (int j = 0; j < PW; ++j) {
       const int p = wave + j * G::WAVES, sp = p / PT, pp = p % PT;
-      const int ck = 2 * pp + (lane >> 5), kk = lane & 31;
+      const int u = 64 * pp + lane, ck = u / G::BN, kk = u % G::BN;
       koff[j] = (uint32_t)(sp * G::BN + kk) * krow + ck * 16;
       const int kv = 8 * pp + (lane >> 3), cv = (lane & 7) ^ (((kv >> 1) & 1) << 2);
       voff[j] = (uint32_t)(sp * G::BN + kv) * vrow + cv * 16;
@@ -1795,6 +1796,9 @@ __global__ __launch_bounds__(256) void prefill_tile_images_kernel(PrefillLaunch 
 // BM 128, 8 waves: 4 row groups x 2 key splits, 32-key tiles, 4 waves/SIMD; bf16 K/V copied global -> LDS by
 // direct loads (the boundary requires 16-byte aligned bases and strides that are multiples of 8 elements)
 using EncGeo = Geo<64, 32, 1, 4, 2, 4, 4, true, 0, false, false, true, true, true>;
+// the same with 64-key tiles (half the barriers and per-tile work per key) at the 2-wave register budget and
+// 128 KiB of LDS: for grids of at most one workgroup per CU, where neither limit costs occupancy
+using EncGeo64 = Geo<64, 64, 1, 4, 2, 4, 2, true, 0, false, false, true, true, true>;
 using EncGeoMask = Geo<64, 32, 1, 4, 2, 4, 2, true>;  // masked: register-staged tiles and mask values, 2 waves/SIMD
 using EncGeoF32 = Geo<64, 32, 1, 4, 2, 4, 2, true>;   // fp32 inputs: register-staged (converted) tiles
 using PrefGeo = Geo<256, 32, 1, 8, 1, 2, 2, false, 3, true>;  // BM 256, 8 waves of 32 rows, 2 waves per SIMD, 3 Q fragments in LDS, PV priority
@@ -1814,6 +1818,19 @@ hipError_t launch_lds(K kernel, dim3 grid, const A &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+static int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 // ROPE here rotates the Q rows as they are loaded; K arrives rotated (the
 // RoPE pass of rope.hip).
 template <int ROPE>
@@ -1821,8 +1838,12 @@ static hipError_t launch_encoder_r(const EncoderLaunch &a, bool f32_in, dim3 gri
   if (f32_in)
     return a.mask ? launch_lds<EncGeoF32>(encoder_fwd_kernel<EncGeoF32, true, true, ROPE>, grid, a, stream)
                   : launch_lds<EncGeoF32>(encoder_fwd_kernel<EncGeoF32, true, false, ROPE>, grid, a, stream);
-  return a.mask ? launch_lds<EncGeoMask>(encoder_fwd_kernel<EncGeoMask, false, true, ROPE>, grid, a, stream)
-                : launch_lds<EncGeo>(encoder_fwd_kernel<EncGeo, false, false, ROPE>, grid, a, stream);
+  if (a.mask) return launch_lds<EncGeoMask>(encoder_fwd_kernel<EncGeoMask, false, true, ROPE>, grid, a, stream);
+  // 64-key tiles from 1536 keys on (measured at 256 workgroups of 2048 query rows: 1.3% slower at 1024
+  // keys, even at 1280, 1-4% faster from 1536 to 4096)
+  if ((int)grid.x <= cu_count() && a.Skv >= 1536)
+    return launch_lds<EncGeo64>(encoder_fwd_kernel<EncGeo64, false, false, ROPE>, grid, a, stream);
+  return launch_lds<EncGeo>(encoder_fwd_kernel<EncGeo, false, false, ROPE>, grid, a, stream);
 }
 
 hipError_t launch_encoder(const EncoderLaunch &a, bool f32_in, hipStream_t stream) {
@@ -1830,6 +1851,7 @@ hipError_t launch_encoder(const EncoderLaunch &a, bool f32_in, hipStream_t strea
   const dim3 grid(n_qt * a.H * a.B);
   static_assert(EncGeo::BM == EncGeoF32::BM && EncGeo::THREADS == EncGeoF32::THREADS, "same launch shape");
   static_assert(EncGeo::BM == EncGeoMask::BM && EncGeo::THREADS == EncGeoMask::THREADS, "same launch shape");
+  static_assert(EncGeo::BM == EncGeo64::BM && EncGeo::THREADS == EncGeo64::THREADS, "same launch shape");
   switch (a.rope) {
     case 0: return launch_encoder_r<0>(a, f32_in, grid, stream);
     case 1: return launch_encoder_r<1>(a, f32_in, grid, stream);
