@@ -180,21 +180,7 @@ void decode_split_kernel(DecodeLaunch a) {
   }
   const uint64_t live = (live_chunk >> (wave * WK)) & ((WK == 64) ? ~0ull : ((1ull << WK) - 1));
 
-  // The G query rows (G * 2D bytes) are copied into this wave's LDS slice:
-  // the q^T B-operand fragments are read from there right before their
-  // MFMAs, which keeps them out of the registers.
   const int gq = lane & 15, quad = lane >> 4;
-  {
-    const auto rq = dec_rsrc(a.q + ((int64_t)b * a.Hq + (int64_t)kvh * G) * D, G * D * 2);
-#pragma unroll
-    for (int i = 0; i < (G * D * 2 + 1023) / 1024; ++i) {
-      const uint32_t off = (lane + 64 * i) * 16;
-      if (off < G * D * 2)
-        *reinterpret_cast<u32x4_t *>(reinterpret_cast<char *>(&qs[wave][0][0]) + off) =
-            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    }
-  }
-
   float m[G], l[G];
   DecAcc<D> o[G];
 #pragma unroll
@@ -209,8 +195,24 @@ void decode_split_kernel(DecodeLaunch a) {
     const int64_t row0 = ((int64_t)b * a.Hkv + kvh) * a.S_ctx + key0;
     const uint32_t span = (uint32_t)max(min(WK, R.end - key0), 0) * (D * 2);
     const auto rk = dec_rsrc(a.k + row0 * D, span), rv = dec_rsrc(a.v + row0 * D, span);
+    // The G query rows (G * 2D bytes) go into this wave's LDS slice: the
+    // q^T B-operand fragments are read from there right before their MFMAs,
+    // which keeps them out of the registers.  q's loads are issued first and
+    // written to LDS after the first group's K/V loads are issued, so the
+    // K/V stream does not wait for q's round trip.
+    constexpr int QL = (G * D * 2 + 1023) / 1024;  // 16-byte q loads per lane
+    const auto rq = dec_rsrc(a.q + ((int64_t)b * a.Hq + (int64_t)kvh * G) * D, G * D * 2);
+    u32x4_t qv[QL];
+#pragma unroll
+    for (int i = 0; i < QL; ++i)  // offsets past the G rows read zeros and are not written
+      qv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (lane + 64 * i) * 16, 0, 0));
     DecStage<D> st[NG < 2 ? 1 : 2];
     dec_load<D>(st[0], rk, rv, live, 0, lane);
+#pragma unroll
+    for (int i = 0; i < QL; ++i) {
+      const uint32_t off = (lane + 64 * i) * 16;
+      if (off < G * D * 2) *reinterpret_cast<u32x4_t *>(reinterpret_cast<char *>(&qs[wave][0][0]) + off) = qv[i];
+    }
 
 #pragma unroll
     for (int grp = 0; grp < NG; ++grp) {
@@ -319,7 +321,8 @@ void decode_split_kernel(DecodeLaunch a) {
 // 64 chunks per round.  Lane c reads chunk c's statistics; the max and the
 // weighted sum of l are wave reductions; every lane issues its column's loads
 // for all 64 chunks at once and weights them with the chunk weight broadcast
-// from lane c.  Dead chunks (m_c = -inf, partial never written) and chunks
+// from lane c.  Dead chunks (m_c = -inf, partial never written) get an
+// out-of-range offset, so their partials are never fetched; they and chunks
 // whose weight underflows are selected away, not branched around.  The chunk
 // order is fixed, so the result is deterministic.
 template <int D>
@@ -327,16 +330,22 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeLaunch a) {
   const int slice = blockIdx.x, hq = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
   const int64_t p0 = ((int64_t)b * a.Hq + hq) * a.n_chunks;
   const int d = slice * 64 + lane;
+  const auto ro = dec_rsrc(a.ws_o + p0 * D, (uint32_t)a.n_chunks * D * 4);  // this head's chunk partials
   float M = -INFINITY, L = 0.0f, acc = 0.0f;
   for (int c0 = 0; c0 < a.n_chunks; c0 += 64) {
     const int nc = min(64, a.n_chunks - c0);
     const int64_t pc = p0 + c0 + (lane < nc ? lane : 0);
     const f32x2_t ml = *reinterpret_cast<const f32x2_t *>(a.ws_ml + pc * 2);
     const float mc = lane < nc ? ml[0] : -INFINITY;
+    const uint64_t alive = __ballot(mc != -INFINITY);  // bit i: chunk c0 + i has a partial
     float oc[64];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) oc[i] = a.ws_o[(p0 + c0 + (i < nc ? i : 0)) * D + d];
-    const float Mb = fmaxf(M, wave_max(mc));
+    for (int i = 0; i < 64; ++i)
+      oc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             ro, ((alive >> i) & 1) ? (uint32_t)((c0 + i) * D + d) * 4 : kOOB, 0, 0));
+    float mcp = mc;
+    asm volatile("" : "+v"(mcp));  // the reductions below run while the loads are in flight
+    const float Mb = fmaxf(M, wave_max(mcp));
     const float Mu = Mb == -INFINITY ? 0.0f : Mb;
     const float w = mc == -INFINITY ? 0.0f : fast_exp2(mc - Mu);
     const float rs = M == -INFINITY ? 0.0f : fast_exp2(M - Mu);  // rescale of the running sums
