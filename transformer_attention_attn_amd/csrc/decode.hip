@@ -147,9 +147,14 @@ void decode_split_kernel(DecodeLaunch a) {
   // exit early, and the final workgroups are the all-live first chunks of
   // every (batch, KV head), which finish together.  A timeline of the
   // workgroups showed the (batch-major) order ending in a long tail of the
-  // last batch's chunks.
-  const int np = a.Hkv * a.B, lin = blockIdx.x;
-  const int chunk = a.n_chunks - 1 - lin / np, kvh = (lin % np) % a.Hkv, b = (lin % np) / a.Hkv;
+  // last batch's chunks.  At head_dim 512 (3 waves per SIMD, so fewer
+  // workgroups resident, each with twice the bytes) the chunk order
+  // alternates between the highest and the lowest remaining chunk instead,
+  // so the K/V stream starts with the first workgroups (measured faster
+  // there, slower at 256).
+  const int np = a.Hkv * a.B, lin = blockIdx.x, j = lin / np;
+  const int chunk = (D == 512 && (j & 1)) ? j / 2 : a.n_chunks - 1 - (D == 512 ? j / 2 : j);
+  const int kvh = (lin % np) % a.Hkv, b = (lin % np) / a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const DecRange R = dec_range(a, b);
   const float *mrow = a.mask ? a.mask + (int64_t)b * a.S_ctx : nullptr;
