@@ -911,8 +911,10 @@ def main():
         e = e_dev[k]
         for _ in range(3):
             e.attention()
-        ms_b = gpu_timed(e.block, args.steps)
-        ms_a = gpu_timed(e.attention, args.steps)
+        # at least 50 calls each (~0.1 ms apiece): the mean of a few 20-40 us
+        # calls moves by several percent with one slow call
+        ms_b = gpu_timed(e.block, max(args.steps, 50))
+        ms_a = gpu_timed(e.attention, max(args.steps, 50))
         c = encs[k]
         tf_b = f_enc[k] / (statistics.fmean(ms_b) * 1e-3) / 1e12
         tf_a = f_enc[k] / (statistics.fmean(ms_a) * 1e-3) / 1e12
