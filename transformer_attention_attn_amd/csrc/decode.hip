@@ -26,6 +26,9 @@
 //   mask : additive, in log2 units; keys it removes are never fetched (their
 //          buffer offsets fall out of range), a wave with no live key skips
 //          the loads;
+//   softmax: in the MFMA's score layout, one head per 16-lane column (four
+//          exp2 per lane; the group's max and sum over the head's four
+//          lanes), P to LDS;
 //   PV   : on the VALU, each lane owning D/64 of the D output columns, V read
 //          with 2D contiguous bytes per key per wave;
 //   merge: the 4 wave partials combine through LDS; the chunk partial
@@ -56,6 +59,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dec_rsrc(const void *base, uin
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p), hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0,
                                            (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Max and sum over the four lanes l % 16 + 16 q of a 16-lane column (lane ^ 16,
+// then lane ^ 32); all four receive the same bits.
+__device__ __forceinline__ float dec_quad_max(float x) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+__device__ __forceinline__ float dec_quad_sum(float x) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 // Per-lane V slice: D/64 bf16 columns of one key (4 -> 8 bytes, 8 -> 16).
@@ -118,10 +136,10 @@ __device__ __forceinline__ DecRange dec_range(const DecodeLaunch &a, int b) {
 // The accumulator of one query head: the lane's D/64 output columns.
 template <int D> struct DecAcc { float x[D / 64]; };
 
-// Register budget (waves per SIMD): at head_dim 256, 5 waves fit one or two
-// query heads per KV head; four heads need the 4-wave budget (5 spills 20
-// bytes per lane).
-template <int D, int G> constexpr int dec_waves_per_eu() { return D == 256 ? (G >= 4 ? 4 : 5) : 2; }
+// Register budget (waves per SIMD): at head_dim 256, 5 waves fit up to four
+// query heads per KV head (at most 96 VGPRs, no scratch); eight take the
+// 4-wave budget.
+template <int D, int G> constexpr int dec_waves_per_eu() { return D == 256 ? (G >= 8 ? 4 : 5) : 2; }
 
 template <int D, int G>
 __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(dec_waves_per_eu<D, G>())))
@@ -186,15 +204,15 @@ void decode_split_kernel(DecodeLaunch a) {
   const uint64_t live = (live_chunk >> (wave * WK)) & ((WK == 64) ? ~0ull : ((1ull << WK) - 1));
 
   const int gq = lane & 15, quad = lane >> 4;
-  float m[G], l[G];
+  // Softmax state of the lane's head (lane % 16, in the score layout of the
+  // QK MFMA; the same in all four lanes of a head) and the G heads' partial
+  // outputs over the lane's columns.
+  float m_l = -INFINITY, l_l = 0.0f;
   DecAcc<D> o[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.0f;
+  for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) o[g].x[c] = 0.0f;
-  }
 
   if (live != 0) {
     const int64_t row0 = ((int64_t)b * a.Hkv + kvh) * a.S_ctx + key0;
@@ -239,48 +257,54 @@ void decode_split_kernel(DecodeLaunch a) {
         const u32x4_t qv = *reinterpret_cast<const u32x4_t *>(qrow + 64 * s);
         s4 = mfma16(as_bf16x8(cs.k[s]), as_bf16x8(gq < G ? qv : u32x4_t{0, 0, 0, 0}), s4);
       }
-      // lane l holds S^T[key = 4*(l/16) + i][head g = l%16]: scale, mask, to LDS
+      // lane l holds S^T[key = 4*(l/16) + i][head g = l%16]: scale and mask,
+      // then the online softmax of head l%16 in this layout (four exp2 per
+      // lane; the group max and sum run over the head's four lanes), and P
+      // to LDS for the PV
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float mv = __shfl(mk_lane, wave * WK + grp * KW + 4 * quad + i);
         s4[i] = mv == -INFINITY ? -INFINITY : __builtin_fmaf(s4[i], a.c, mv);
       }
-      if (gq < G) *reinterpret_cast<f32x4_t *>(&sc[wave][gq][4 * quad]) = s4;
+      const float mg = dec_quad_max(fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3])));
+      const float m_new = fmaxf(m_l, mg);
+      const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m_l - m_new);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // a head with no live key yet: p = 0
+      m_l = m_new;
+      f32x4_t p4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p4[i] = fast_exp2(s4[i] - m_use);
+      l_l = l_l * alpha + dec_quad_sum((p4[0] + p4[1]) + (p4[2] + p4[3]));
+      if (gq < G) *reinterpret_cast<f32x4_t *>(&sc[wave][gq][4 * quad]) = p4;
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
       __builtin_amdgcn_wave_barrier();
-      // online softmax over the group for each head, PV on the VALU
+      // PV on the VALU for each head, after its rescale (alpha of head g from lane g)
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        // two passes over the scores in LDS (max, then exp2): fewer live registers
-        float mg = -INFINITY;
-#pragma unroll
-        for (int q4 = 0; q4 < KW / 4; ++q4) {
-          const f32x4_t t = *reinterpret_cast<const f32x4_t *>(&sc[wave][g][4 * q4]);
-          mg = fmaxf(mg, fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])));
-        }
-        const float m_new = fmaxf(m[g], mg);
-        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m[g] - m_new);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        m[g] = m_new;
-        float ls = l[g] * alpha;
+        const float ag = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), g));
         DecAcc<D> acc;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc.x[c] = o[g].x[c] * alpha;
+        for (int c = 0; c < CPL; ++c) acc.x[c] = o[g].x[c] * ag;
 #pragma unroll
         for (int j = 0; j < KW; ++j) {
-          const float pj = fast_exp2(sc[wave][g][j] - m_use);
-          ls += pj;
+          const float pj = sc[wave][g][j];
 #pragma unroll
           for (int w = 0; w < CPL / 2; ++w) {
             acc.x[2 * w] += pj * bf16_lo(cs.v[j][w]);
             acc.x[2 * w + 1] += pj * bf16_hi(cs.v[j][w]);
           }
         }
-        l[g] = ls;
         o[g] = acc;
       }
       __builtin_amdgcn_wave_barrier();  // sc is rewritten by the next group
     }
+  }
+
+  float m[G], l[G];  // per head, from the head's lane
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m_l), g));
+    l[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_l), g));
   }
 
   // Merge the wave partials (fixed order) and write the chunk partial.
