@@ -147,18 +147,18 @@ void decode_split_kernel(DecodeLaunch a) {
   constexpr int KW = kDecKW, NW = kDecWaves, NG = kDecNG, WK = NG * KW;  // WK: keys per wave
   constexpr int CPL = D / 64;                                             // output columns per lane
   static_assert(WK <= 64, "one liveness bit per lane");
-  // LDS: each wave's copy of the G query rows and its score tile (used in
+  // LDS: each wave's copy of the G query rows and its tile of P (used in
   // the key loop), then the wave partials of the merge.  When the three
   // together would cap occupancy the merge buffer reuses the first two,
   // behind one more barrier.
-  constexpr int QS_B = NW * G * D * 2, SC_B = NW * G * KW * 4, RO_B = NW * G * D * 4;
-  constexpr bool ALIAS = QS_B + SC_B + RO_B > 48 * 1024;
-  constexpr int SMEM_B = ALIAS ? (QS_B + SC_B > RO_B ? QS_B + SC_B : RO_B) : QS_B + SC_B + RO_B;
+  constexpr int QS_B = NW * G * D * 2, PL_B = NW * G * KW * 4, RO_B = NW * G * D * 4;
+  constexpr bool ALIAS = QS_B + PL_B + RO_B > 48 * 1024;
+  constexpr int SMEM_B = ALIAS ? (QS_B + PL_B > RO_B ? QS_B + PL_B : RO_B) : QS_B + PL_B + RO_B;
   __shared__ __attribute__((aligned(16))) char smem[SMEM_B];
   __shared__ float red_ml[NW][G][2];
   auto qs = reinterpret_cast<__bf16(*)[G][D]>(smem);
-  auto sc = reinterpret_cast<float(*)[G][KW]>(smem + QS_B);
-  auto red_o = reinterpret_cast<float(*)[G][D]>(smem + (ALIAS ? 0 : QS_B + SC_B));
+  auto pl = reinterpret_cast<float(*)[G][KW]>(smem + QS_B);
+  auto red_o = reinterpret_cast<float(*)[G][D]>(smem + (ALIAS ? 0 : QS_B + PL_B));
 
   // One-dimensional grid, chunk-major with the last chunks first: the chunks
   // that most sequences leave empty (the highest) are dispatched first and
@@ -275,7 +275,7 @@ void decode_split_kernel(DecodeLaunch a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) p4[i] = fast_exp2(s4[i] - m_use);
       l_l = l_l * alpha + dec_quad_sum((p4[0] + p4[1]) + (p4[2] + p4[3]));
-      if (gq < G) *reinterpret_cast<f32x4_t *>(&sc[wave][gq][4 * quad]) = p4;
+      if (gq < G) *reinterpret_cast<f32x4_t *>(&pl[wave][gq][4 * quad]) = p4;
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
       __builtin_amdgcn_wave_barrier();
       // PV on the VALU for each head, after its rescale (alpha of head g from lane g)
@@ -287,7 +287,7 @@ void decode_split_kernel(DecodeLaunch a) {
         for (int c = 0; c < CPL; ++c) acc.x[c] = o[g].x[c] * ag;
 #pragma unroll
         for (int j = 0; j < KW; ++j) {
-          const float pj = sc[wave][g][j];
+          const float pj = pl[wave][g][j];
 #pragma unroll
           for (int w = 0; w < CPL / 2; ++w) {
             acc.x[2 * w] += pj * bf16_lo(cs.v[j][w]);
@@ -296,7 +296,7 @@ void decode_split_kernel(DecodeLaunch a) {
         }
         o[g] = acc;
       }
-      __builtin_amdgcn_wave_barrier();  // sc is rewritten by the next group
+      __builtin_amdgcn_wave_barrier();  // pl is rewritten by the next group
     }
   }
 
@@ -308,7 +308,7 @@ void decode_split_kernel(DecodeLaunch a) {
   }
 
   // Merge the wave partials (fixed order) and write the chunk partial.
-  if (ALIAS) __syncthreads();  // every wave is done with its q copy and scores
+  if (ALIAS) __syncthreads();  // every wave is done with its q copy and P tile
 #pragma unroll
   for (int g = 0; g < G; ++g) {
 #pragma unroll
