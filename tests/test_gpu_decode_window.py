@@ -168,3 +168,30 @@ def test_one_workspace_for_decodes_of_different_shapes(gpu_lib):
     torch.cuda.synchronize()
     assert_close(out, oracle.decode_window(small.q, small.k, small.v, small.scale, None, beg, end, 300),
                  "shared ws window")
+
+
+@pytest.mark.parametrize("D", [256, 512])
+@pytest.mark.parametrize("scale", [8.0, -1.5, 0.0])
+def test_decode_softmax_scales(gpu_lib, D, scale):
+    """Sharp (scores of tens of log2 units, the running max moves between key
+    groups and waves), negative and zero (uniform weights) softmax scales at
+    two and four query heads per KV head, ragged lengths."""
+    for B, Hq, Hkv, S, lens in ((3, 16, 8, 1500, [1500, 700, 65]), (2, 16, 4, 900, [900, 33])):
+        case = W.decode_gemma(70 + S, B, Hq, Hkv, S, D=D, lens=lens)
+        case.scale = scale
+        _say(f"[decode] D={D} scale={scale} G={Hq // Hkv} B={B} S_ctx={S} lens={lens}")
+        assert_close(_full(gpu_lib, case), oracle.sdpa(case.q, case.k, case.v, case.scale, case.mask),
+                     f"d{D} scale {scale}")
+
+
+def test_decode_finite_additive_mask(gpu_lib):
+    """An additive mask with finite entries (uniform in [-6, 0]) besides the
+    -inf of removed keys, at both head sizes."""
+    for D in (256, 512):
+        case = W.decode_gemma(81, 2, 16, 8, 1200, D=D, lens=[1200, 517])
+        g = torch.Generator().manual_seed(82)
+        finite = -6.0 * torch.rand(case.mask.shape, generator=g)
+        case.mask = torch.where(torch.isinf(case.mask), case.mask, finite)
+        _say(f"[decode] D={D} finite additive mask, lens=[1200, 517]")
+        assert_close(_full(gpu_lib, case), oracle.sdpa(case.q, case.k, case.v, case.scale, case.mask),
+                     f"d{D} finite mask")
