@@ -1,6 +1,10 @@
 // Tiled online-softmax ("flash") attention forward for gfx950.
 //
-// One key loop (flash_loop) serves three kernels:
+// Two key loops serve three kernels: flash_loop stages K/V tiles through
+// registers (fp32 or masked encoder inputs, the prefill without a
+// workspace); flash_loop_dma copies them straight into LDS with direct
+// global -> LDS loads (the bf16 encoder, the prefill over bf16 tile images).
+// The kernels:
 //   * the non-causal encoder (q/k/v [B,H,S,D] bf16 or fp32, optional additive
 //     key mask, optional RoPE on the Q rows, fused residual-add epilogue);
 //   * the history-only GQA prefill over a paged FP8 (e4m3fn) KV cache, whose
@@ -27,7 +31,9 @@
 // Per key tile (BN keys), per wave:
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys on M, query rows on N), so
 //   every lane owns one query row (lane % 32) and 16 keys per 32-key block;
-//   row max: in-lane max + one v_permlane32_swap with the partner lane;
+//   row max: in-lane max + one v_permlane32_swap with the partner lane (the
+//   bf16 encoder skips it while a row's half-tile sums stay below 2^kTau:
+//   Geo::LAZYSUM);
 //   P = exp2(S*c - m) with the scale folded into one FMA (c > 0, log2 units),
 //   packed to bf16 straight into the B operand of O^T += V^T P^T (d on M,
 //   rows on N): P never leaves registers; the row sum is taken on the packed
