@@ -183,8 +183,9 @@ def cpu_baseline(cases, pre, n_rows: int, reps: int = 3):
 def time_next_workloads(taa, dev, flush, pre_dev, reps: int = 20):
     """Workload variants beyond the step (reported, not part of `value`):
     the 64-frame V-JEPA 2 clip (8192 tokens), a gte-base batch right-padded to
-    512 tokens with ragged real lengths (additive key mask), both timed as
-    back-to-back launches between two HIP events after 3 warm-up calls; and
+    512 tokens with ragged real lengths (as an additive key mask, and as key
+    lengths), all timed as back-to-back launches between two HIP events after
+    3 warm-up calls; and
     the decode at head_dim 512 (global layers) and over a 1024-key sliding
     window at head_dim 256, each call timed alone after the cache flush; and
     the paged prefill with causal attention among the 4096 current tokens
@@ -236,6 +237,14 @@ def time_next_workloads(taa, dev, flush, pre_dev, reps: int = 20):
     out["gte_base_padded_L512_b8_block"] = {"ms": ms, "lens": lens, "dense_equiv_tflops": dense / (ms * 1e-3) / 1e12,
                                             "live_key_tflops": live / (ms * 1e-3) / 1e12,
                                             "kernels": "attention+mask+residual, res_ln"}
+    # the same batch with its right padding given as key lengths: same result,
+    # the padded key tiles are never read
+    kl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ms = timed(lambda: taa.attn_encoder_fwd(q, k, v, c.scale, None, key_len=kl, residual=res, gamma=gam, beta=bet,
+                                            eps=c.eps))
+    out["gte_base_padded_L512_b8_block_key_len"] = {
+        "ms": ms, "lens": lens, "dense_equiv_tflops": dense / (ms * 1e-3) / 1e12,
+        "live_key_tflops": live / (ms * 1e-3) / 1e12, "kernels": "attention+residual over the live keys, res_ln"}
 
     c = W.decode_gemma(1005, D=512)
     q, k, v, m = c.q.to(dev), c.k.to(dev), c.v.to(dev), c.mask.to(dev)
@@ -607,7 +616,7 @@ def _write_next_profile(prof_dir):
          "Command (repository root copy `<repo>`, output dir `<out>`):", "", "```", NEXT_COMMAND, "```", "",
          "One call of `time_next_workloads` (each workload: warm-up calls, then timed calls): the V-JEPA2 64-frame "
          "clip (8192 tokens, attention alone); a gte-base batch right-padded to 512 tokens (mask, residual, "
-         "LayerNorm); decode at head_dim 512 and over a 1024-key sliding window at head_dim 256; V-JEPA2 and DINOv3 "
+         "LayerNorm; then the same with key lengths); decode at head_dim 512 and over a 1024-key sliding window at head_dim 256; V-JEPA2 and DINOv3 "
          "attention with RoPE (`rope_k_kernel` rotates K once); the paged prefill with causal current tokens. "
          "Kernels by total time:", "",
          "| kernel | calls | avg (us) | min (us) | max (us) |", "|---|---|---|---|---|"]

@@ -101,6 +101,14 @@ ATTN_API int attn_version(void);
  * mask_stride_b: a stride of at least S_kv (rows do not overlap), or 0 for one
  * row [1,1,1,S_kv] shared by the whole batch; a negative stride, or one in
  * 1..S_kv-1 with B > 1, is ATTN_ERR_INVALID_ARG.
+ * key_len is nullable int32 [B] in device memory, 4-byte aligned: the right
+ * padding of gte-encoder-neuron-kernels, "Constraints" (a 0/1 attention
+ * mask over right-padded rows) and vit-encoder-neuron-kernels, "Attribution
+ * and license" (padded-key skipping) as lengths.  Batch row b attends keys
+ * 0 .. key_len[b]-1 (clamped to [0, S_kv]); the result is that of an
+ * additive mask of 0 on those keys and -inf on the rest, but key tiles past
+ * the length are never read.  A row with no key gets o = 0 and lse = -inf.
+ * key_len together with mask is ATTN_ERR_INVALID_ARG.
  *
  * Fused RoPE prologue (rope != ATTN_ROPE_NONE; vit-encoder-neuron-kernels,
  * "Kernels": the rotate-half and interleaved pairings; V-JEPA2 ViT-L Encoder
@@ -144,6 +152,7 @@ typedef struct {
   attn_rope_t rope;
   void *rope_workspace;
   size_t rope_workspace_bytes;
+  const int32_t *key_len;
 } attn_encoder_args_t;
 
 ATTN_API int attn_encoder_fwd(const attn_encoder_args_t *args, hipStream_t stream);

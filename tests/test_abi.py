@@ -56,7 +56,7 @@ def test_status_strings(lib):
     for s in range(5):
         assert taa.attn_status_string(s).startswith(("ATTN_OK", "ATTN_ERR"))
     assert taa.attn_status_string(99) == "unknown attn status"
-    assert taa.attn_version() == 10300
+    assert taa.attn_version() == 10400
 
 
 def _enc(**kw):
@@ -102,6 +102,8 @@ def _enc(**kw):
     (dict(rope=2, rope_cos=FAKE, rope_sin=FAKE, rope_workspace=FAKE + 16, rope_workspace_bytes=1 << 30),
      taa.ATTN_ERR_INVALID_ARG),                                                             # 256-byte alignment
     (dict(softmax_scale=float("nan")), taa.ATTN_ERR_INVALID_ARG),
+    (dict(key_len=FAKE, mask=FAKE), taa.ATTN_ERR_INVALID_ARG),   # key lengths replace the mask
+    (dict(key_len=FAKE + 2), taa.ATTN_ERR_INVALID_ARG),          # 4-byte alignment
     (dict(out_dtype=taa.ATTN_FP8_E4M3FN), taa.ATTN_ERR_UNSUPPORTED),
 ])
 def test_encoder_validation(lib, kw, expect):

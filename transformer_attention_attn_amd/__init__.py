@@ -56,6 +56,7 @@ class EncoderArgs(ctypes.Structure):
         ("rope_cos", ctypes.c_void_p), ("rope_sin", ctypes.c_void_p), ("rope_stride_b", ctypes.c_int64),
         ("rope", ctypes.c_int),
         ("rope_workspace", ctypes.c_void_p), ("rope_workspace_bytes", ctypes.c_size_t),
+        ("key_len", ctypes.c_void_p),
     ]
 
 
@@ -178,10 +179,12 @@ def attn_encoder_fwd(q, k, v, softmax_scale: float, mask=None, *, out=None, out_
                      want_out: bool = True, lse=None, residual=None, residual_out=None, gamma=None, beta=None,
                      eps: float = 1e-6, ln_out=None, ln_dtype=torch.bfloat16, want_ln: bool | None = None,
                      ln_mean=None, ln_rstd=None, rope=None, rope_cos=None, rope_sin=None, rope_workspace=None,
-                     stream=None):
+                     key_len=None, stream=None):
     """Non-causal SDPA over q/k/v [B,H,S,D] (bf16 or fp32, any strides with a
     unit d stride), optional additive key mask [B,1,1,S_kv] fp32 (or
-    [1,1,1,S_kv], one row for the whole batch), optional fused residual add
+    [1,1,1,S_kv], one row for the whole batch) or, instead of a mask, right
+    padding as key lengths (key_len: int32 [B]; batch row b attends keys
+    0 .. key_len[b]-1 and the rest are never read), optional fused residual add
     (+ LayerNorm) into the fp32 residual stream [B,S,H*D].
     rope: None, "half" or "interleaved", with fp32 tables rope_cos/rope_sin
     [rows, D/2] (shared by the batch) or [B, rows, D/2]; rope_workspace
@@ -213,6 +216,11 @@ def attn_encoder_fwd(q, k, v, softmax_scale: float, mask=None, *, out=None, out_
     if mask is not None and (mask.dtype != torch.float32 or mask.dim() != 4 or tuple(mask.shape[1:]) != (1, 1, Skv)
                              or mask.shape[0] not in (1, B) or mask.stride(-1) != 1):
         raise ValueError("mask must be fp32 [B,1,1,S_kv] or [1,1,1,S_kv] with a unit last stride")
+    if key_len is not None:
+        if mask is not None:
+            raise ValueError("key_len replaces the mask: pass one of them")
+        if key_len.dtype != torch.int32 or tuple(key_len.shape) != (B,) or not key_len.is_contiguous():
+            raise ValueError("key_len must be a contiguous int32 [B] tensor")
     if rope not in _ROPE:
         raise ValueError(f"rope must be one of {list(_ROPE)}")
     if rope is not None:
@@ -225,7 +233,7 @@ def attn_encoder_fwd(q, k, v, softmax_scale: float, mask=None, *, out=None, out_
         if rope_cos.shape != rope_sin.shape:
             raise ValueError("rope_cos and rope_sin must have one shape")
     _need_cuda(q, k, v, mask, out, lse, residual, residual_out, gamma, beta, ln_out, ln_mean, ln_rstd,
-               rope_cos, rope_sin, rope_workspace)
+               rope_cos, rope_sin, rope_workspace, key_len)
     res = {}
     with _alloc_ctx(stream):
         if want_out and out is None:
@@ -265,6 +273,7 @@ def attn_encoder_fwd(q, k, v, softmax_scale: float, mask=None, *, out=None, out_
             a.ln_dtype = _DT.get(ln_out.dtype, -1)
         a.ln_mean = None if ln_mean is None else ln_mean.data_ptr()
         a.ln_rstd = None if ln_rstd is None else ln_rstd.data_ptr()
+        a.key_len = None if key_len is None else key_len.data_ptr()
         a.rope = _ROPE[rope]
         if rope is not None:
             a.rope_cos, a.rope_sin = rope_cos.data_ptr(), rope_sin.data_ptr()

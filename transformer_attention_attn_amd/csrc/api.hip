@@ -202,7 +202,7 @@ const char *attn_status_string(int status) {
   }
 }
 
-int attn_version(void) { return 10300; }
+int attn_version(void) { return 10400; }
 
 size_t attn_encoder_rope_workspace_size(int B, int H, int S_kv, int D, attn_dtype_t in_dtype) {
   if (B <= 0 || H <= 0 || S_kv <= 0 || D <= 0) return 0;
@@ -241,6 +241,7 @@ int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
   if (a->mask && (a->mask_stride_b < 0 || (a->B > 1 && a->mask_stride_b != 0 && a->mask_stride_b < a->S_kv)))
     return ATTN_ERR_INVALID_ARG;
   if (a->mask && (reinterpret_cast<uintptr_t>(a->mask) & 3u)) return ATTN_ERR_INVALID_ARG;
+  if (a->key_len && (a->mask || (reinterpret_cast<uintptr_t>(a->key_len) & 3u))) return ATTN_ERR_INVALID_ARG;
   const int64_t hidden = (int64_t)a->H * a->D;
   if (a->ln_out) {
     if (a->ln_dtype != ATTN_BF16 && a->ln_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
@@ -273,6 +274,7 @@ int attn_encoder_fwd(const attn_encoder_args_t *a, hipStream_t stream) {
   }
   L.mask = a->mask;
   L.mask_sb = a->mask_stride_b;
+  L.key_len = a->key_len;
   L.B = a->B;
   L.H = a->H;
   L.Sq = a->S_q;

@@ -1355,7 +1355,10 @@ __device__ __forceinline__ void flash_loop_dma(WaveState<G> &ws, const Src &src,
       ws.thr[nt] = ws.m[nt] == -INFINITY ? -INFINITY : (ws.m[nt] + kTau) * (1.0f / c);
     }
   }
-  if (n_iter <= 0) return;
+  if (n_iter <= 0) {  // no key: copies issued before the loop (the encoder's residual rows) land first
+    wait_vm<0>();
+    return;
+  }
   char *const vbuf = smem + 3 * G::KSLOT;
   dma_loop_body<G>(ws, src, qf, smem, smem + G::KSLOT, smem + 2 * G::KSLOT, vbuf, vbuf + G::VSLOT,
                    vbuf + 2 * G::VSLOT, smem + G::QOFF + tid * 16, c, mk, lane, wave, n_iter);
@@ -1483,6 +1486,9 @@ void encoder_fwd_kernel(EncoderLaunch a) {
     for (int sd = 0; sd < G::SD; ++sd) qf[nt][sd] = neg_bf16x8(pack8(f[sd]), qsign);
   }
 
+  // keys of this batch row: all S_kv, or its right-padded length
+  const int n_keys =
+      a.key_len ? __builtin_amdgcn_readfirstlane(min(max(a.key_len[b], 0), a.Skv)) : a.Skv;
   EncSrc<G, F32IN, HAS_MASK> src;
   src.kb = reinterpret_cast<const char *>(a.k) + (b * a.ks[0] + h * a.ks[1]) * ES;
   src.vb = reinterpret_cast<const char *>(a.v) + (b * a.vs[0] + h * a.vs[1]) * ES;
@@ -1490,14 +1496,14 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   src.vrow = (uint32_t)(a.vs[2] * ES);
   src.kstep = (int64_t)G::NSPLIT * G::BN * a.ks[2] * ES;
   src.vstep = (int64_t)G::NSPLIT * G::BN * a.vs[2] * ES;
-  src.n_keys = a.Skv;
+  src.n_keys = n_keys;
   src.mask = HAS_MASK ? a.mask + b * a.mask_sb : nullptr;
 
   WaveState<G> ws;
   if constexpr (G::EDMA) {
     static_assert(!F32IN && !HAS_MASK, "direct copies: bf16 rows, no additive mask");
-    // the residual rows land with the first tiles: the loop's first wait covers them (S_kv >= 1 is
-    // checked at the boundary, so the loop always runs)
+    // the residual rows land with the first tiles: the loop's first wait covers them (with no key
+    // the loop does not run and waits for them itself)
     if (a.res_out)
       ResRows<G>::copy(a.res + ((int64_t)b * a.Sq + row0) * (a.H * G::D) + h * G::D, nrow, a.H * G::D,
                   smem + G::LDS - G::RES, __builtin_amdgcn_readfirstlane(wave), lane);
@@ -1508,11 +1514,11 @@ void encoder_fwd_kernel(EncoderLaunch a) {
     ds.vrow = src.vrow;
     ds.kstep = src.kstep;
     ds.vstep = src.vstep;
-    ds.n_keys = a.Skv;
+    ds.n_keys = n_keys;
     ds.init(__builtin_amdgcn_readfirstlane(wave), lane);
-    flash_loop_dma<G>(ws, ds, qf, smem, a.c, TailMask{a.Skv}, true, threadIdx.x);
+    flash_loop_dma<G>(ws, ds, qf, smem, a.c, TailMask{n_keys}, true, threadIdx.x);
   } else {
-    flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c, TailMask{a.Skv}, true, threadIdx.x);
+    flash_loop<G, HAS_MASK>(ws, src, qf, smem, a.c, TailMask{n_keys}, true, threadIdx.x);
   }
 
   // The residual rows are read before the split merge, so their latency

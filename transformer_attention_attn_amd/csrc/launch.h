@@ -24,6 +24,7 @@ struct EncoderLaunch {
   const float *rope_cos, *rope_sin;  // RoPE tables [rows, D/2] fp32 (rope != 0; q rows only, K comes rotated)
   int64_t rope_sb;              // table batch stride in floats (0: shared)
   int rope;                     // 0 none, 1 rotate-half pairing, 2 interleaved pairing
+  const int *key_len;           // nullable [B]: batch row b attends keys 0 .. key_len[b]-1 (clamped)
 };
 
 // K rotation pass of the encoder's RoPE: k [B,H,S,D] strided -> out [B,H,S,D]
