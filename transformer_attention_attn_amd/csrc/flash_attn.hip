@@ -553,9 +553,11 @@ struct ResRows {
           r, (__attribute__((address_space(3))) void *)(dst + (wave + j * G::WAVES) * 1024), 16,
           off + (uint32_t)(j * 4 * G::WAVES) * stride, 0, 0, 0);
   }
-  // columns d0 .. d0 + 3 (d0 a multiple of 4) of tile row `row`, as copy left them
+  // byte offset of columns d0 .. d0 + 3 (d0 a multiple of 4) of tile row `row`
+  static __device__ __forceinline__ int offset(int row, int d0) { return row * (G::D * 4) + 16 * ((d0 >> 2) ^ (row & 15)); }
+  // those columns as copy left them
   static __device__ __forceinline__ f32x4_t read(const char *src, int row, int d0) {
-    return *reinterpret_cast<const f32x4_t *>(src + row * (G::D * 4) + 16 * ((d0 >> 2) ^ (row & 15)));
+    return *reinterpret_cast<const f32x4_t *>(src + offset(row, d0));
   }
 };
 
@@ -1575,10 +1577,33 @@ void encoder_fwd_kernel(EncoderLaunch a) {
           }
         }
         if (a.res_out) {
-          const int64_t off = ((int64_t)b * a.Sq + row) * HD + h * G::D + d0;
-          *reinterpret_cast<f32x4_t *>(a.res_out + off) = resv[nt][mt][r4] + val;
+          if constexpr (G::EDMA) {  // back into the row's LDS copy; stored by whole rows below
+            *reinterpret_cast<f32x4_t *>(smem + G::LDS - G::RES + ResRows<G>::offset((rg * G::NT + nt) * 32 + l32, d0)) =
+                resv[nt][mt][r4] + val;
+          } else {
+            const int64_t off = ((int64_t)b * a.Sq + row) * HD + h * G::D + d0;
+            *reinterpret_cast<f32x4_t *>(a.res_out + off) = resv[nt][mt][r4] + val;
+          }
         }
       }
+  }
+  if constexpr (G::EDMA) {
+    if (a.res_out) {
+      // this wave's rows of residual_out, four whole 256-byte rows per store
+      // (a lane per 16 bytes) instead of 32-byte pieces of 32 rows, and
+      // non-temporal: measured 1-3% faster per block than either alone
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes above are done
+      __builtin_amdgcn_wave_barrier();
+      const char *rl = smem + G::LDS - G::RES;
+#pragma unroll
+      for (int i = 0; i < G::NT * 32 / 4; ++i) {
+        const int r = rg * G::NT * 32 + 4 * i + (lane >> 4), c = lane & 15, row = qt * G::BM + r;
+        if (row < a.Sq)
+          __builtin_nontemporal_store(
+              *reinterpret_cast<const f32x4_t *>(rl + ResRows<G>::offset(r, 4 * c)),
+              reinterpret_cast<f32x4_t *>(a.res_out + ((int64_t)b * a.Sq + row) * HD + h * G::D + 4 * c));
+      }
+    }
   }
 }
 
