@@ -109,3 +109,24 @@ def test_identity_tables_give_the_unrotated_bits(gpu_lib, pairing):
     torch.cuda.synchronize()
     for key in ("out", "residual_out", "ln_out"):
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+def test_rope_with_key_lengths(gpu_lib, pairing):
+    """RoPE with the right padding as key lengths (the direct-copy path over
+    the rotated K): the oracle with the equivalent additive mask."""
+    lens = [300, 77]
+    case = W.encoder_custom(970, 2, 3, 300, masked_lens=lens)
+    c, s = _tables(np.arange(300) * 1.5, 64, ntk_factor=2.0)
+    d = lambda t: None if t is None else t.to(DEV)
+    _say(f"[encoder-rope] {pairing} with key lengths {lens}")
+    r = gpu_lib.attn_encoder_fwd(d(case.q), d(case.k), d(case.v), case.scale, None,
+                                 key_len=torch.tensor(lens, dtype=torch.int32, device=DEV),
+                                 residual=d(case.residual), gamma=d(case.gamma), beta=d(case.beta), eps=case.eps,
+                                 rope=pairing, rope_cos=d(c), rope_sin=d(s))
+    torch.cuda.synchronize()
+    ref = oracle.encoder_block_rope(case.q, case.k, case.v, case.scale, case.residual, case.gamma, case.beta,
+                                    case.eps, case.mask, c, s, pairing)
+    assert_close(r["out"], ref["attn"], f"rope {pairing} key lengths attention")
+    assert_close(r["residual_out"], ref["res_out"], f"rope {pairing} key lengths residual_out")
+    assert_close(r["ln_out"], ref["ln_out"], f"rope {pairing} key lengths ln_out")
