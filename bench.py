@@ -700,8 +700,13 @@ def _write_profiles(line, kernels, cal):
                   f"{p['min_ms'] * 1e3:.1f} | {p['p90_ms'] * 1e3:.1f} | {p['tflops']:.0f} | {100 * p['frac_bf16_peak']:.1f} |",
                   f"| attention alone | {p['attention_only']['mean_ms'] * 1e3:.1f} | {p['attention_only']['median_ms'] * 1e3:.1f} | "
                   f"{p['attention_only']['min_ms'] * 1e3:.1f} | {p['attention_only']['p90_ms'] * 1e3:.1f} | "
-                  f"{p['attention_only']['tflops']:.0f} | {100 * p['attention_only']['frac_bf16_peak']:.1f} |", "",
-                  "## Kernel trace", ""] + _kernel_rows(ks) + [""]
+                  f"{p['attention_only']['tflops']:.0f} | {100 * p['attention_only']['frac_bf16_peak']:.1f} |", ""]
+            if "back_to_back_ms" in p:
+                L += [f"Back to back (50 calls between two events, per call): block {p['back_to_back_ms'] * 1e3:.1f} us "
+                      f"({100 * p['back_to_back_frac_bf16_peak']:.1f}% of the bf16 peak), attention alone "
+                      f"{p['attention_only']['back_to_back_ms'] * 1e3:.1f} us "
+                      f"({100 * p['attention_only']['back_to_back_frac_bf16_peak']:.1f}%).", ""]
+            L += ["## Kernel trace", ""] + _kernel_rows(ks) + [""]
             L += [f"Algorithmic work: {p['flops'] / 1e9:.2f} GFLOP of attention (QK^T + PV); MFMA bound at the "
                   f"bf16 peak {p['mfma_bound_us']:.2f} us; softmax VALU bound {p['valu_bound']['us']:.2f} us "
                   f"({p['valu_bound']['per_score']}).  From the trace: block {t_blk:.1f} us = "
@@ -924,6 +929,21 @@ def main():
         # calls moves by several percent with one slow call
         ms_b = gpu_timed(e.block, max(args.steps, 50))
         ms_a = gpu_timed(e.attention, max(args.steps, 50))
+
+        def back_to_back(fn, n=50):
+            """Mean GPU time per call of n calls enqueued back to back between
+            two events (as in a model's layer loop: each launch overlaps the
+            previous call's tail)."""
+            torch.cuda._sleep(150_000)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        bb_b, bb_a = back_to_back(e.block), back_to_back(e.attention)
         c = encs[k]
         tf_b = f_enc[k] / (statistics.fmean(ms_b) * 1e-3) / 1e12
         tf_a = f_enc[k] / (statistics.fmean(ms_a) * 1e-3) / 1e12
@@ -933,10 +953,15 @@ def main():
             **_stats(ms_b), "tflops": tf_b, "frac_bf16_peak": tf_b / acc.PEAK_BF16_TFLOPS, "flops": f_enc[k],
             "kernels": "attention + fp32 residual epilogue, res_ln (LayerNorm over H*D)",
             "shape": {"B": c.B, "H": c.H, "S": c.S, "D": c.D, "hidden": c.H * c.D},
-            "attention_only": {**_stats(ms_a), "tflops": tf_a, "frac_bf16_peak": tf_a / acc.PEAK_BF16_TFLOPS},
+            "attention_only": {**_stats(ms_a), "tflops": tf_a, "frac_bf16_peak": tf_a / acc.PEAK_BF16_TFLOPS,
+                               "back_to_back_ms": bb_a,
+                               "back_to_back_frac_bf16_peak": f_enc[k] / (bb_a * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS},
+            "back_to_back_ms": bb_b,
+            "back_to_back_frac_bf16_peak": f_enc[k] / (bb_b * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS,
             "epilogue_and_ln_ms": statistics.fmean(ms_b) - statistics.fmean(ms_a),
             "in_step_events_mean_ms": statistics.fmean(t_enc[k].ms()),
-            "timing": "per call, HIP events behind a spin kernel (GPU time of the call's kernels), warm",
+            "timing": "per call, HIP events behind a spin kernel (GPU time of the call's kernels), warm; "
+                      "back_to_back_*: 50 calls between two events, per call",
             "mfma_bound_us": f_enc[k] / acc.PEAK_BF16_TFLOPS / 1e6,
             "valu_bound": {"us": bound_us, "scores": scores,
                            "per_score": f"{acc.SOFTMAX_EXP_PER_SCORE:g} exp2 (16 cycles per wave64) + "
