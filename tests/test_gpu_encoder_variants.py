@@ -144,3 +144,21 @@ def test_key_row_strides_give_identical_bits(gpu_lib):
         assert torch.equal(o, outs["contiguous"][0]) and torch.equal(l, outs["contiguous"][1]), f"{name} differs"
     ref = oracle.encoder_block(case.q, case.k, case.v, case.scale, case.residual, case.gamma, case.beta, case.eps)
     assert_close(outs["contiguous"][0], ref["attn"], "strided key rows: attention")
+
+
+@pytest.mark.parametrize("fp32,masked", [(False, False), (True, False), (False, True)])
+def test_residual_in_place(gpu_lib, fp32, masked):
+    """residual_out may alias residual (the header allows it): the in-place
+    block gives the bits of the out-of-place one, on the direct-copy path and
+    on the register-staged paths (fp32 inputs, an additive mask)."""
+    case = W.encoder_custom(990, 2, 4, 333, masked_lens=[333, 120] if masked else None, fp32_inputs=fp32)
+    d = lambda t: None if t is None else t.to(DEV)
+    _say(f"[encoder-variant] residual in place fp32={fp32} masked={masked}")
+    ref = _run_block(gpu_lib, case)
+    res = case.residual.to(DEV).clone()
+    r = gpu_lib.attn_encoder_fwd(d(case.q), d(case.k), d(case.v), case.scale, d(case.mask), residual=res,
+                                 residual_out=res, gamma=d(case.gamma), beta=d(case.beta), eps=case.eps)
+    torch.cuda.synchronize()
+    assert r["residual_out"].data_ptr() == res.data_ptr()
+    for key in ("out", "residual_out", "ln_out", "ln_mean", "ln_rstd"):
+        assert torch.equal(r[key], ref[key]), key
