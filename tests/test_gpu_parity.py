@@ -342,3 +342,28 @@ def test_prefill_poisoned_tail_ignored(gpu_lib):
         case.v_cache[bt[i]] = nan
     out2 = _pre_run(gpu_lib, case)
     assert torch.equal(out1, out2)
+
+
+@pytest.mark.parametrize("token_major", [False, True])
+def test_encoder_fp32_outputs(gpu_lib, token_major):
+    """out and ln_out in fp32 (out_dtype / ln_dtype ATTN_F32), the attention
+    output head-major or token-major by strides."""
+    case = W.encoder_custom(21, 2, 4, 300, masked_lens=None)
+    d = lambda t: None if t is None else t.to(DEV)
+    B, H, S, D = case.B, case.H, case.S, case.D
+    out = (torch.empty(B, S, H, D, device=DEV).permute(0, 2, 1, 3) if token_major
+           else torch.empty(B, H, S, D, device=DEV))
+    _say(f"[encoder] fp32 out and ln_out, token_major={token_major}")
+    r = gpu_lib.attn_encoder_fwd(d(case.q), d(case.k), d(case.v), case.scale, None, out=out,
+                                 residual=d(case.residual), gamma=d(case.gamma), beta=d(case.beta), eps=case.eps,
+                                 ln_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert r["out"].dtype == torch.float32 and r["ln_out"].dtype == torch.float32
+    ref = oracle.encoder_block(case.q, case.k, case.v, case.scale, case.residual, case.gamma, case.beta, case.eps)
+    assert_close(r["out"], ref["attn"], "fp32 out")
+    assert_close(r["residual_out"], ref["res_out"], "fp32 out residual_out")
+    assert_close(r["ln_out"], ref["ln_out"], "fp32 ln_out")
+    # the fp32 output is the attention before its bf16 rounding: the bf16 call's output is its rounding
+    rb = gpu_lib.attn_encoder_fwd(d(case.q), d(case.k), d(case.v), case.scale, None, want_ln=False)
+    torch.cuda.synchronize()
+    assert torch.equal(rb["out"], r["out"].to(torch.bfloat16))
