@@ -177,3 +177,38 @@ def test_encoder_block_direct_copies_in_a_graph(gpu_lib):
         torch.cuda.synchronize()
         for t, e, name in zip(outs, eager, names):
             assert torch.equal(t, e), f"replay {i}: {name} differs from the eager call"
+
+
+def test_encoder_key_lengths_in_a_graph(gpu_lib):
+    """Right padding as key lengths (a device int32 array read by the kernel):
+    the lengths changed between replays change the replayed result exactly as
+    they change the eager one."""
+    taa = gpu_lib
+    case = W.encoder_custom(1100, 4, 12, 512)
+    d = lambda t: t.to(DEV)
+    q, k, v = d(case.q), d(case.k), d(case.v)
+    out = torch.empty_like(q)
+    kl = torch.tensor([512, 300, 17, 0], dtype=torch.int32, device=DEV)
+    call = lambda: taa.attn_encoder_fwd(q, k, v, case.scale, None, key_len=kl, out=out, want_ln=False)
+    call()
+    torch.cuda.synchronize()
+    _say("[graph] encoder with key lengths, lengths changed between replays")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for lens in ([512, 300, 17, 0], [1, 2, 3, 512], [256, 256, 256, 256]):
+        kl.copy_(torch.tensor(lens, dtype=torch.int32))
+        call()
+        torch.cuda.synchronize()
+        eager = out.clone()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay with lengths {lens} differs from the eager call"
