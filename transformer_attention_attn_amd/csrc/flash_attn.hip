@@ -554,7 +554,9 @@ struct ResRows {
           off + (uint32_t)(j * 4 * G::WAVES) * stride, 0, 0, 0);
   }
   // byte offset of columns d0 .. d0 + 3 (d0 a multiple of 4) of tile row `row`
-  static __device__ __forceinline__ int offset(int row, int d0) { return row * (G::D * 4) + 16 * ((d0 >> 2) ^ (row & 15)); }
+  static __device__ __forceinline__ int offset(int row, int d0) {
+    return row * (G::D * 4) + 16 * ((d0 >> 2) ^ (row & 15));
+  }
   // those columns as copy left them
   static __device__ __forceinline__ f32x4_t read(const char *src, int row, int d0) {
     return *reinterpret_cast<const f32x4_t *>(src + offset(row, d0));
@@ -1578,8 +1580,8 @@ void encoder_fwd_kernel(EncoderLaunch a) {
         }
         if (a.res_out) {
           if constexpr (G::EDMA) {  // back into the row's LDS copy; stored by whole rows below
-            *reinterpret_cast<f32x4_t *>(smem + G::LDS - G::RES + ResRows<G>::offset((rg * G::NT + nt) * 32 + l32, d0)) =
-                resv[nt][mt][r4] + val;
+            const int lr = (rg * G::NT + nt) * 32 + l32;
+            *reinterpret_cast<f32x4_t *>(smem + G::LDS - G::RES + ResRows<G>::offset(lr, d0)) = resv[nt][mt][r4] + val;
           } else {
             const int64_t off = ((int64_t)b * a.Sq + row) * HD + h * G::D + d0;
             *reinterpret_cast<f32x4_t *>(a.res_out + off) = resv[nt][mt][r4] + val;
