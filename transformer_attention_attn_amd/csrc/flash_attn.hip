@@ -1266,7 +1266,9 @@ __device__ __forceinline__ void dma_loop_body(WaveState<G> &ws, const Src &src,
   src.copy_v(vB, 1, wave, lane);
   src.copy_k(kC, 2, wave, lane);
   q_to_lds<G>(qf, qa);  // own Q slots: after the tile copies are on their way
-  wait_vm<0>();
+  // K(0), V(0) and K(1) are read before the first step's copies are waited
+  // for; V(1) and K(2), the last two issued, may still be in flight
+  Src::wait_step(wave);
   lds_barrier();
 
   // key split of this wave (its tile of each iteration: sp * KTILE, sp * VTILE)
