@@ -1453,8 +1453,24 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   const uint32_t qrow = (uint32_t)(a.qs[2] * ES);
   const int row0 = qt * G::BM, nrow = min(a.Sq - row0, G::BM);
   const auto rq = make_rsrc(qb + (int64_t)row0 * a.qs[2] * ES, (uint32_t)(nrow - 1) * qrow + G::D * ES);
+  // bf16 rows without a rotation are the fragments as loaded: no VALU work
+  // touches them before the first MFMA, so no wait on these loads holds up
+  // the tile copies issued after them (the sign of q, for a negative scale,
+  // is applied on a branch of its own)
+  constexpr bool RAW = !F32IN && ROPE == 0;
 #pragma unroll
-  for (int nt = 0; nt < G::NT; ++nt) {
+  for (int nt = 0; nt < G::NT && RAW; ++nt)
+#pragma unroll
+    for (int sd = 0; sd < G::SD; ++sd)
+      qf[nt][sd] = buf_load16(rq, (uint32_t)((rg * G::NT + nt) * 32 + l32) * qrow + (16 * sd + 8 * hh) * ES);
+  if (RAW && a.q_neg) {
+#pragma unroll
+    for (int nt = 0; nt < G::NT; ++nt)
+#pragma unroll
+      for (int sd = 0; sd < G::SD; ++sd) qf[nt][sd] = neg_bf16x8(qf[nt][sd], qsign);
+  }
+#pragma unroll
+  for (int nt = 0; nt < G::NT && !RAW; ++nt) {
     const int lrow = (rg * G::NT + nt) * 32 + l32, row = row0 + lrow;
     float f[G::SD][8];
 #pragma unroll
