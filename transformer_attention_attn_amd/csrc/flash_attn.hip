@@ -1448,15 +1448,15 @@ void encoder_fwd_kernel(EncoderLaunch a) {
   const char *qb = reinterpret_cast<const char *>(a.q) + (b * a.qs[0] + h * a.qs[1]) * ES;
   // This tile's rows as one buffer range ending with the last row's data
   // (row stride < 2^24 bytes, checked on the host, so offsets fit 32 bits):
-  // rows past Sq read as zeros without a branch, and no wait on these loads
-  // comes before the first K/V tiles are requested.
+  // rows past Sq read as zeros without a branch.
   const uint32_t qrow = (uint32_t)(a.qs[2] * ES);
   const int row0 = qt * G::BM, nrow = min(a.Sq - row0, G::BM);
   const auto rq = make_rsrc(qb + (int64_t)row0 * a.qs[2] * ES, (uint32_t)(nrow - 1) * qrow + G::D * ES);
   // bf16 rows without a rotation are the fragments as loaded: no VALU work
-  // touches them before the first MFMA, so no wait on these loads holds up
-  // the tile copies issued after them (the sign of q, for a negative scale,
-  // is applied on a branch of its own)
+  // touches them before the first MFMA, so no wait on these loads comes
+  // before the tile copies are issued (the sign of q, for a negative scale,
+  // is applied on a branch of its own).  fp32 rows are rounded and rotated
+  // rows rotated here, which waits for them.
   constexpr bool RAW = !F32IN && ROPE == 0;
 #pragma unroll
   for (int nt = 0; nt < G::NT && RAW; ++nt)
