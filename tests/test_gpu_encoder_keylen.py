@@ -70,6 +70,7 @@ def _check(r, case, lens, what, with_res=True):
     (4, 12, 512, [6, 512, 300, 129]),    # gte-base at L 512: ragged, one unpadded
     (3, 2, 200, [0, 1, 200]),            # no key, one key, all keys
     (2, 2, 96, [500, -3]),               # clamped to S_kv and to 0
+    (3, 2, 192, [64, 65, 128]),          # one, two and exactly two key steps (64 keys per step)
 ])
 def test_keylen_bf16_block(gpu_lib, B, H, S, lens):
     case = W.encoder_custom(900 + S, B, H, S, masked_lens=None)
@@ -77,12 +78,16 @@ def test_keylen_bf16_block(gpu_lib, B, H, S, lens):
     _check(_run(gpu_lib, case, lens), case, lens, f"bf16 S={S}")
 
 
-def test_keylen_64key_tiles(gpu_lib):
+@pytest.mark.parametrize("B,H,lens", [
+    (1, 16, [1537]),
+    (2, 8, [1, 129]),     # one and two key steps (128 keys per step)
+    (2, 8, [128, 300]),   # exactly one, and three
+])
+def test_keylen_64key_tiles(gpu_lib, B, H, lens):
     """One workgroup per CU and at least 1536 keys: the 64-key tile geometry."""
-    case = W.encoder_custom(930, 1, 16, 2048)
-    lens = [1537]
-    _say(f"[encoder-keylen] 64-key tiles S=2048 lens={lens}")
-    _check(_run(gpu_lib, case, lens), case, lens, "64-key tiles")
+    case = W.encoder_custom(930 + B, B, H, 2048)
+    _say(f"[encoder-keylen] 64-key tiles B={B} H={H} S=2048 lens={lens}")
+    _check(_run(gpu_lib, case, lens), case, lens, f"64-key tiles lens={lens}")
 
 
 def test_keylen_fp32_inputs(gpu_lib):
