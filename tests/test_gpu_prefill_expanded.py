@@ -40,6 +40,8 @@ def _both(taa, case, want_lse=False, workspace=None):
     (6, 3, 260, 5, 64, 1),
     (4, 2, 300, 3, 64, 160),   # five tiles: one pass of the six-step loop, cut short
     (4, 2, 40, 4, 64, 193),    # seven tiles: a second pass, ragged last tile
+    (4, 2, 50, 2, 64, 64),     # exactly two tiles
+    (4, 2, 70, 3, 64, 90),     # three tiles, ragged last tile
 ])
 def test_expanded_small_full_check(gpu_lib, Hq, Hkv, Lq, nb, bs, L):
     case = W.prefill_paged(150 + Lq, Hq, Hkv, Lq, 256, nb, bs, L, n_rows=Lq)
